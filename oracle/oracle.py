@@ -1,0 +1,177 @@
+"""ctypes front end of the fp64 C oracle (oracle/flare_oracle.c).
+
+TEST INFRASTRUCTURE: imported by tests, by the smoke check and by the
+benchmark's CPU-baseline leg only.  It shares no code with the GPU library.
+
+All arrays are converted to contiguous float64; outputs are float64.
+Shapes: K, V [B,H,N,D]; Q [H,M,D] (shared over the batch) or [B,H,M,D];
+Z [B,H,M,D]; L [B,H,M]; Y [B,H,N,D].  ``scale <= 0`` selects 1/sqrt(D).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "flare_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+__all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
+           "flare_pp_forward", "materialize"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into oracle/liboracle.so."""
+    global _lib
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        L.oracle_encode.argtypes = [dp, i, dp, dp, i, i, i, i, i, ctypes.c_double, dp, dp]
+        L.oracle_decode_rows.argtypes = [dp, i, dp, dp, i, i, i, i, i, ctypes.c_double,
+                                         ctypes.POINTER(ctypes.c_long), ctypes.c_long, dp]
+        L.oracle_flare_forward.argtypes = [dp, i, dp, dp, i, i, i, i, i, ctypes.c_double, dp, dp, dp]
+        L.oracle_pp_queries.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, ctypes.c_double, dp]
+        L.oracle_flare_pp_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, ctypes.c_double,
+                                              dp, dp, dp, dp]
+        L.oracle_materialize.argtypes = [dp, dp, i, i, i, ctypes.c_double, dp, dp]
+        L.oracle_threads.argtypes = [i]
+        for fn in (L.oracle_encode, L.oracle_decode_rows, L.oracle_flare_forward, L.oracle_pp_queries,
+                   L.oracle_flare_pp_forward, L.oracle_materialize, L.oracle_threads):
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def threads(n: int = 0) -> int:
+    """Set (n > 0) and return the OpenMP thread count the oracle uses."""
+    return int(lib().oracle_threads(int(n)))
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x: Optional[np.ndarray]):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _q_batched(Q: np.ndarray, B: int) -> int:
+    if Q.ndim == 3:
+        return 0
+    if Q.ndim == 4 and Q.shape[0] == B:
+        return 1
+    raise ValueError(f"Q must be [H,M,D] or [B,H,M,D], got {Q.shape}")
+
+
+def encode(Q, K, V, scale: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Z = SDPA(Q, K, V) per (b, h) and its log-normaliser L."""
+    K, V, Q = _f64(K), _f64(V), _f64(Q)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    if V.shape != K.shape or Q.shape[-1] != D:
+        raise ValueError("shape mismatch")
+    Z = np.empty((B, H, M, D))
+    L = np.empty((B, H, M))
+    rc = lib().oracle_encode(_p(Q), _q_batched(Q, B), _p(K), _p(V), B, H, N, M, D, float(scale), _p(Z), _p(L))
+    if rc:
+        raise RuntimeError(f"oracle_encode failed ({rc})")
+    return Z, L
+
+
+def decode(Q, K, Z, scale: float = 0.0, idx=None) -> np.ndarray:
+    """Y = SDPA(K, Q, Z) per (b, h); with ``idx`` only those token rows ([B,H,len(idx),D])."""
+    K, Q, Z = _f64(K), _f64(Q), _f64(Z)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    if idx is None:
+        count, ip = N, None
+    else:
+        idx_arr = np.ascontiguousarray(np.asarray(idx, dtype=np.int64))
+        count = int(idx_arr.size)
+        ip = idx_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
+    Y = np.empty((B, H, count, D))
+    rc = lib().oracle_decode_rows(_p(Q), _q_batched(Q, B), _p(K), _p(Z), B, H, N, M, D, float(scale), ip,
+                                  count, _p(Y))
+    if rc:
+        raise RuntimeError(f"oracle_decode_rows failed ({rc})")
+    return Y
+
+
+def flare_forward(Q, K, V, scale: float = 0.0):
+    """FLARE routing forward: returns (Y, Z, L)."""
+    K, V, Q = _f64(K), _f64(V), _f64(Q)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    Y = np.empty((B, H, N, D))
+    Z = np.empty((B, H, M, D))
+    L = np.empty((B, H, M))
+    rc = lib().oracle_flare_forward(_p(Q), _q_batched(Q, B), _p(K), _p(V), B, H, N, M, D, float(scale),
+                                    _p(Y), _p(Z), _p(L))
+    if rc:
+        raise RuntimeError(f"oracle_flare_forward failed ({rc})")
+    return Y, Z, L
+
+
+def pp_queries(Qs, Ks, Vs, Qf, gate, scale: float = 0.0) -> np.ndarray:
+    """FLARE++ routing queries Q[b,h] = Qf[h] + gate[h] * SDPA(Qs[h], Ks[b,h], Vs[b,h])."""
+    Qs, Ks, Vs, Qf, gate = _f64(Qs), _f64(Ks), _f64(Vs), _f64(Qf), _f64(gate)
+    B, H, N, D = Ks.shape
+    M = Qs.shape[-2]
+    Qout = np.empty((B, H, M, D))
+    rc = lib().oracle_pp_queries(_p(Qs), _p(Ks), _p(Vs), _p(Qf), _p(gate), B, H, N, M, D, float(scale),
+                                 _p(Qout))
+    if rc:
+        raise RuntimeError(f"oracle_pp_queries failed ({rc})")
+    return Qout
+
+
+def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0):
+    """FLARE++ routing forward: returns (Y, Q, Z, L) with Q the per-batch routing queries."""
+    Qs, Ks, Vs, Qf, gate = _f64(Qs), _f64(Ks), _f64(Vs), _f64(Qf), _f64(gate)
+    K, V = _f64(K), _f64(V)
+    B, H, N, D = K.shape
+    M = Qs.shape[-2]
+    Y = np.empty((B, H, N, D))
+    Qout = np.empty((B, H, M, D))
+    Z = np.empty((B, H, M, D))
+    L = np.empty((B, H, M))
+    rc = lib().oracle_flare_pp_forward(_p(Qs), _p(Ks), _p(Vs), _p(Qf), _p(gate), _p(K), _p(V), B, H, N, M, D,
+                                       float(scale), _p(Y), _p(Qout), _p(Z), _p(L))
+    if rc:
+        raise RuntimeError(f"oracle_flare_pp_forward failed ({rc})")
+    return Y, Qout, Z, L
+
+
+def materialize(Q, K, scale: float = 0.0):
+    """One head: (Wenc [M,N], Wdec [N,M]) with Z = Wenc V and Y = Wdec Z."""
+    Q, K = _f64(Q), _f64(K)
+    M, D = Q.shape
+    N = K.shape[0]
+    Wenc = np.empty((M, N))
+    Wdec = np.empty((N, M))
+    rc = lib().oracle_materialize(_p(Q), _p(K), N, M, D, float(scale), _p(Wenc), _p(Wdec))
+    if rc:
+        raise RuntimeError(f"oracle_materialize failed ({rc})")
+    return Wenc, Wdec
