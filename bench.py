@@ -1,0 +1,170 @@
+"""Benchmark of the FLARE routing forward on one MI355X.
+
+One step = one flare_forward call (encode partials -> merge -> decode) over
+the whole million-token surface-mesh workload: B=1, H=8, N=1,048,576, M=256,
+D=32, bf16 inputs with float32 accumulation, inputs resident in HBM before
+the timed region.  FLOPs are counted as 8*B*H*N*M*D per routing pass.
+
+Prints one JSON line with the throughput, the roofline position of the
+dominant kernel (timed with HIP events on the stream the library launches
+on) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FLARE routing fwd tokens/s at N=1M,M=256 (1 GPU); % of bf16 MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The fp64 oracle on a bounded sample: one head, the first n tokens."""
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.threads()
+    h = 0
+
+    def run(n):
+        Q = w.Q[h:h + 1]
+        K = np.ascontiguousarray(w.K[:, h:h + 1, :n])
+        V = np.ascontiguousarray(w.V[:, h:h + 1, :n])
+        t0 = time.perf_counter()
+        oracle.flare_forward(Q, K, V)
+        return time.perf_counter() - t0
+
+    n = min(16384, w.N)
+    t = run(n)
+    n2 = int(min(w.N, max(n, n * target_s / max(t, 1e-3))))
+    n2 = max(1024, (n2 // 1024) * 1024)
+    t2 = run(n2) if n2 != n else t
+    n, t = (n2, t2)
+    # tokens/s of the whole routing pass: a token needs all H heads
+    value = n / t / w.H
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle FLARE forward on head 0 of {w.H}, first {n} of {w.N} tokens "
+                      f"(M={w.M}, D={w.D}), {t:.1f} s on {cores} threads ({platform.processor() or 'host cpu'}); "
+                      f"rate divided by H for whole-pass tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["c5", "c5pp"], default="c5")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU path is a design, "
+              "not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_latent_attention_amd as flare
+    from rank_latent_attention_amd.inputs import config5
+
+    pp = args.workload == "c5pp"
+    t0 = time.perf_counter()
+    w = config5(pp=pp)
+    log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    B, H, N, M, D = w.B, w.H, w.N, w.M, w.D
+    K, V = up(w.K), up(w.V)
+    Y = torch.empty_like(K)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    if pp:
+        Qs, Ks, Qf = up(w.Qs), up(w.Ks), up(w.Qf)
+        gate = torch.from_numpy(w.gate).to(dev)
+        Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+        ws = flare.workspace(flare.flare.OP_PP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
+
+        def step():
+            flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Y=Y, Q_out=Qo, Z=Z, L=L, ws=ws)
+    else:
+        Q = up(w.Q)
+        ws = flare.workspace(flare.flare.OP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
+
+        def step():
+            flare.flare_forward(Q, K, V, Y=Y, Z=Z, L=L, ws=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps: {ms:.3f} ms/step")
+
+    # Per-phase times with events between the launches: the encode entry
+    # point (encode partials + merge) and the decode entry point (decode
+    # kernel alone), run back to back exactly as one flare_forward step runs them.
+    Qr = Qo if pp else Q
+    qb = Qr.to(torch.bfloat16).contiguous() if pp else Qr
+    nrep = max(args.steps, 5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    wse = flare.workspace(flare.flare.OP_ENCODE, B, H, N, M, D, flare.flare.BF16, dev)
+    for i in range(nrep):
+        ev[3 * i].record(stream)
+        flare.flare_encode(qb, K, V, Z=Z, L=L, ws=wse)
+        ev[3 * i + 1].record(stream)
+        flare.flare_decode(qb, K, Z, Y=Y)
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    t_enc = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(nrep))[nrep // 2]
+    t_dec = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(nrep))[nrep // 2]
+    log(f"phases (median of {nrep}): encode+merge {t_enc * 1e3:.1f} us, decode {t_dec * 1e3:.1f} us")
+
+    half_flops = 4.0 * B * H * N * M * D           # one of the two SDPA passes
+    if t_dec >= t_enc:
+        kname, kt, kb = "decode_kernel", t_dec, B * H * N * D * 2 * 2   # read K, write Y
+    else:
+        kname, kt, kb = "encode_kernel+merge_kernel", t_enc, B * H * N * D * 2 * 2  # read K, V
+    achieved = half_flops / (kt * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kname,
+                "kernel_us": round(kt * 1e3, 2), "algorithmic_bytes": kb,
+                "hbm_frac_of_kernel": round(kb / (kt * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    flops = (12.0 if pp else 8.0) * B * H * N * M * D
+    tok_s = B * N / (ms * 1e-3)
+    out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": ("FLARE++" if pp else "FLARE") + " routing forward, million-point surface mesh",
+                      "B": B, "H": H, "N": N, "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "step_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "roofline": roofline}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

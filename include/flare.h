@@ -1,0 +1,128 @@
+/*
+ * flare.h -- C ABI of the MI355X (gfx950) FLARE / FLARE++ routing forward.
+ *
+ * The operations are those of the FLARE++ paper ("FLARE++: Low-rank attention
+ * with attention-synthesized routing", Puri et al.):
+ *
+ *   SDPA(Q, K, V) = softmax(s Q K^T) V, softmax taken row-wise, s = 1/sqrt(D)
+ *                                                     (Sec. 3.1, "Full self-attention")
+ *   FLARE encode  Z_h = SDPA(Q_h, K_h, V_h): M latent queries attend over the
+ *                 N tokens, softmax over N                (App. A.1; Table 2 in A.7)
+ *   FLARE decode  Y_h = SDPA(K_h, Q_h, Z_h): every token attends over the M
+ *                 latents, softmax over M                 (App. A.1; Table 2 in A.7)
+ *   Log-normaliser of the encode  L_m = log sum_n exp(s q_m . k_n), natural log
+ *                                                     (App. B.2, B.3)
+ *   FLARE++ query synthesis  Q_b,h = Qf_h + g_h SDPA(Qs_h, Ks_b,h, Vs_b,h)
+ *                                                     (Sec. 3.2; App. A.1, A.4, A.6)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers of the current HIP device,
+ *   contiguous, row-major, D innermost, 16-byte aligned.
+ *     K, V, Ks, Vs, Y : [B, H, N, D] in `dtype`
+ *     Q               : [H, M, D] (q_batched == 0, shared by the batch, the
+ *                       learned queries of Sec. 3.1) or [B, H, M, D]
+ *                       (q_batched == 1), in `dtype`
+ *     Z               : [B, H, M, D] float32;  L : [B, H, M] float32
+ *     Q_out           : [B, H, M, D] float32
+ *     gate            : [H] float32, already g_h = sigmoid(gamma_h) (App. A.4)
+ * - dtype: FLARE_F32 or FLARE_BF16.  Scores, softmax statistics and every
+ *   accumulation are float32; bf16 inputs feed bf16 matrix-core products.
+ * - scale <= 0 selects s = 1/sqrt(D); any positive value overrides it.  The
+ *   same s is used by the encode and by the decode (whose query, a token
+ *   key, also has width D).
+ * - Supported sizes: B >= 1, H >= 1, N >= 0, 1 <= M <= 256, D in {16, 32},
+ *   B*H*N < 2^31.  N == 0 is the empty-row case of App. B.3: Z = 0 and
+ *   L = -inf, and nothing is written to Y.
+ * - ws / ws_bytes: caller-owned DEVICE scratch of at least
+ *   flare_workspace_size(op, ...) bytes, 256-byte aligned.  It may be NULL
+ *   when that size is 0.  Its contents on entry do not matter.
+ * - stream: a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *   work; they never synchronise the host, allocate memory or keep state
+ *   between calls, so they are reentrant.  Results are bitwise reproducible
+ *   for a fixed (shape, dtype, device).
+ * - Ownership: the caller owns every buffer; the library never frees or
+ *   retains a pointer after the call returns.
+ * - Errors: every argument is validated before anything is enqueued; a
+ *   failed check returns a nonzero status and leaves all outputs untouched.
+ *   A launch failure returns FLARE_ERR_HIP.  NaN or Inf inputs give
+ *   undefined (but finite-time) results.
+ */
+#ifndef FLARE_H
+#define FLARE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define FLARE_F32 0
+#define FLARE_BF16 1
+
+/* status codes */
+#define FLARE_OK 0
+#define FLARE_ERR_INVALID_ARG 1 /* null pointer, negative size, misalignment, bad flag */
+#define FLARE_ERR_UNSUPPORTED 2 /* D not in {16,32}, M > 256, unknown dtype, size overflow */
+#define FLARE_ERR_WORKSPACE 3   /* ws smaller than flare_workspace_size() */
+#define FLARE_ERR_HIP 4         /* the HIP runtime rejected a query or a launch */
+
+/* operation codes for flare_workspace_size */
+#define FLARE_OP_ENCODE 0
+#define FLARE_OP_DECODE 1
+#define FLARE_OP_FORWARD 2
+#define FLARE_OP_PP_FORWARD 3
+
+/* Scratch bytes that `op` needs for this problem (0 when none); returns 0 for
+ * arguments the op would reject.  Depends only on its arguments and on the
+ * compute-unit count of the current device. */
+size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype);
+
+/* FLARE encode (App. A.1 with the log-normaliser of App. B.2):
+ *   Z[b,h,m,:] = sum_n softmax_n(s q_m . k_n) v_n ,  L[b,h,m] = log sum_n exp(s q_m . k_n).
+ * The token axis is split over workgroups; each split keeps a running
+ * (max, sum, accumulator) triple and the splits are combined with the
+ * log-sum-exp merge of Sec. 3.3 / App. B.3 in a fixed order.
+ * Q: [H,M,D] or [B,H,M,D] (q_batched); K, V: [B,H,N,D]; Z: [B,H,M,D] f32 (required);
+ * L: [B,H,M] f32 or NULL. */
+int flare_encode(const void* Q, int q_batched, const void* K, const void* V, float* Z, float* L, int B,
+                 int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* FLARE decode (App. A.1): Y[b,h,n,:] = sum_m softmax_m(s k_n . q_m) Z[b,h,m,:].
+ * Q: [H,M,D] or [B,H,M,D] (q_batched) in dtype; K: [B,H,N,D]; Z: [B,H,M,D] f32;
+ * Y: [B,H,N,D] in dtype.  Needs no workspace (ws may be NULL). */
+int flare_decode(const void* Q, int q_batched, const void* K, const float* Z, void* Y, int B, int H, int N,
+                 int M, int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* FLARE routing forward, encode then decode on one stream (App. A.1, Table 2):
+ * Y = SDPA(K, Q, SDPA(Q, K, V)).  The N x M scores are never stored; the
+ * decode recomputes them.  Z_out / L_out (may be NULL) receive the latents
+ * and log-normalisers.  Heads are processed in groups so that a head's keys
+ * are re-read by the decode while still cache resident. */
+int flare_forward(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out,
+                  float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* FLARE++ routing forward (Sec. 3.2; App. A.1, A.4, A.6):
+ *   Qd[b,h] = SDPA(Qs[h], Ks[b,h], Vs[b,h])            (synthesis encode)
+ *   Q[b,h]  = Qf[h] + gate[h] * Qd[b,h]                 (float32 blend)
+ *   Y       = SDPA(K, Q, SDPA(Q, K, V))                 (routing with the per-batch Q)
+ * Qs, Qf: [H,M,D] in dtype (already normalised by the caller); Ks, Vs:
+ * [B,H,N,D] in dtype, Vs may equal Ks (shared synthesis keys and values,
+ * App. A.6: each tile is then read once); gate: [H] f32; K, V: [B,H,N,D];
+ * Y: [B,H,N,D] in dtype.  Q_out [B,H,M,D] f32, Z_out, L_out may be NULL. */
+int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                     const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out, int B,
+                     int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* flare_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLARE_H */

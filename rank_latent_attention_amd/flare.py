@@ -1,0 +1,188 @@
+"""ctypes binding of libflare.so (include/flare.h).
+
+Argument marshalling only: every step of the routing forward runs in the HIP
+kernels of csrc/flare.hip.  PyTorch supplies device memory (outputs and the
+workspace are ``torch.empty`` tensors on the inputs' device) and the current
+stream.  There is no fallback: without the built library every call raises.
+
+Layouts (contiguous, D innermost):
+  K, V, Ks, Vs, Y : [B, H, N, D]   float32 or bfloat16
+  Q, Qs, Qf       : [H, M, D] (shared over the batch) or [B, H, M, D]
+  Z               : [B, H, M, D] float32;  L : [B, H, M] float32
+  gate            : [H] float32, g_h = sigmoid(gamma_h)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflare.so")
+
+F32, BF16 = 0, 1
+OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD = 0, 1, 2, 3
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+#: every C entry point declared in include/flare.h
+SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
+           "flare_status_string")
+
+_lib = None
+
+
+class FlareError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libflare.so and declare the C signatures; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m rank_latent_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.flare_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    L.flare_workspace_size.restype = sz
+    L.flare_encode.argtypes = [vp, i, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_decode.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_pp_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward):
+        fn.restype = i
+    L.flare_status_string.argtypes = [i]
+    L.flare_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise FlareError(fn, rc)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dims(Q: torch.Tensor, K: torch.Tensor) -> Tuple[int, int, int, int, int, int]:
+    if K.dim() != 4:
+        raise ValueError(f"K must be [B,H,N,D], got {tuple(K.shape)}")
+    B, H, N, D = K.shape
+    if Q.dim() == 3 and Q.shape[0] == H and Q.shape[2] == D:
+        return B, H, N, Q.shape[1], D, 0
+    if Q.dim() == 4 and Q.shape[0] == B and Q.shape[1] == H and Q.shape[3] == D:
+        return B, H, N, Q.shape[2], D, 1
+    raise ValueError(f"Q must be [H,M,D] or [B,H,M,D] matching K {tuple(K.shape)}, got {tuple(Q.shape)}")
+
+
+def _same(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if t.device != ref.device:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
+    return int(load().flare_workspace_size(op, B, H, N, M, D, dtype))
+
+
+def workspace(op: int, B: int, H: int, N: int, M: int, D: int, dtype: int, device) -> Optional[torch.Tensor]:
+    n = workspace_size(op, B, H, N, M, D, dtype)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def flare_encode(Q, K, V, scale: float = 0.0, Z=None, L=None, ws=None):
+    """Z = SDPA(Q, K, V) and its natural-log normaliser L; returns (Z, L)."""
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("Q, K, V must share dtype and K, V shape")
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device) if Z is None else Z
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device) if L is None else L
+    _same(K, Q, V, Z, L)
+    ws = workspace(OP_ENCODE, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_encode(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_encode", rc)
+    return Z, L
+
+
+def flare_decode(Q, K, Z, scale: float = 0.0, Y=None):
+    """Y = SDPA(K, Q, Z): every token attends over the latents."""
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or Z.dtype != torch.float32 or tuple(Z.shape) != (B, H, M, D):
+        raise ValueError("Q must match K's dtype and Z must be float32 [B,H,M,D]")
+    Y = torch.empty_like(K) if Y is None else Y
+    _same(K, Q, Z, Y)
+    rc = load().flare_decode(_ptr(Q), qb, _ptr(K), _ptr(Z), _ptr(Y), B, H, N, M, D, dt, float(scale), None, 0,
+                             _stream(K.device))
+    _check("flare_decode", rc)
+    return Y
+
+
+def flare_forward(Q, K, V, scale: float = 0.0, Y=None, Z=None, L=None, ws=None):
+    """FLARE routing forward Y = SDPA(K, Q, SDPA(Q, K, V)); returns (Y, Z, L).
+
+    Z and L are returned only when passed in (they are written into the given
+    tensors); otherwise they live in the workspace and (Y, None, None) is returned.
+    """
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("Q, K, V must share dtype and K, V shape")
+    Y = torch.empty_like(K) if Y is None else Y
+    _same(K, Q, V, Y, Z, L)
+    ws = workspace(OP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_forward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Y), _ptr(Z), _ptr(L), B, H, N, M, D, dt,
+                              float(scale), _ptr(ws), 0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_forward", rc)
+    return Y, Z, L
+
+
+def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0, Y=None, Q_out=None, Z=None, L=None, ws=None):
+    """FLARE++ routing forward; returns (Y, Q_out, Z, L) (the last three only when passed in)."""
+    if K.dim() != 4:
+        raise ValueError("K must be [B,H,N,D]")
+    B, H, N, D = K.shape
+    if Qs.dim() != 3 or Qs.shape[0] != H or Qs.shape[2] != D or Qf.shape != Qs.shape:
+        raise ValueError("Qs and Qf must be [H,M,D]")
+    M = Qs.shape[1]
+    dt = _dtype_code(K)
+    for t in (Qs, Ks, Vs, Qf, V):
+        if t.dtype != K.dtype:
+            raise ValueError("Qs, Ks, Vs, Qf, K, V must share one dtype")
+    if Ks.shape != K.shape or Vs.shape != K.shape or V.shape != K.shape:
+        raise ValueError("Ks, Vs, K, V must all be [B,H,N,D]")
+    if gate.dtype != torch.float32 or gate.numel() != H:
+        raise ValueError("gate must be float32 [H]")
+    Y = torch.empty_like(K) if Y is None else Y
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L)
+    ws = workspace(OP_PP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_pp_forward(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Y),
+                                 _ptr(Q_out), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_pp_forward", rc)
+    return Y, Q_out, Z, L

@@ -1,0 +1,77 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+that include/flare.h declares, and rejects bad arguments before touching the
+GPU (these calls return before any HIP runtime call, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flare.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rank_latent_attention_amd import flare
+    if not os.path.exists(flare.LIB_PATH):
+        from rank_latent_attention_amd import build
+        build.build()
+    return flare.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(flare_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
+                                           "flare_pp_forward", "flare_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from rank_latent_attention_amd import flare
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(flare.SYMBOLS) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")]:
+        assert word in lib.flare_status_string(code)
+    assert lib.flare_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def enc(lib, B=1, H=1, N=64, M=32, D=16, dt=1, qb=0, Q=FAKE, K=FAKE, V=FAKE, Z=FAKE):
+    return lib.flare_encode(Q, qb, K, V, Z, None, B, H, N, M, D, dt, 0.0, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=24), 2), (dict(D=64), 2), (dict(M=257), 2), (dict(dt=7), 2),
+    (dict(M=0), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(N=-5), 1), (dict(qb=2), 1),
+    (dict(Q=None), 1), (dict(Z=None), 1), (dict(K=None), 1), (dict(V=None), 1),
+    (dict(Q=MISALIGNED), 1), (dict(K=MISALIGNED), 1),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), 2),
+])
+def test_encode_rejects_bad_arguments(lib, kw, status):
+    assert enc(lib, **kw) == status
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    assert lib.flare_decode(FAKE, 0, FAKE, FAKE, FAKE, 1, 1, 8, 8, 48, 1, 0.0, None, 0, None) == 2
+    assert lib.flare_decode(None, 0, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 1, 0.0, None, 0, None) == 1
+    assert lib.flare_forward(FAKE, 0, FAKE, FAKE, None, None, None, 1, 1, 8, 8, 16, 1, 0.0, None, 0, None) == 1
+    assert lib.flare_forward(FAKE, 0, FAKE, FAKE, FAKE, None, None, 1, 1, 8, 300, 16, 1, 0.0, None, 0, None) == 2
+    assert lib.flare_pp_forward(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None,
+                                1, 1, 8, 8, 16, 1, 0.0, None, 0, None) == 1
+    assert lib.flare_pp_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                1, 1, 8, 8, 20, 1, 0.0, None, 0, None) == 2
+    assert lib.flare_workspace_size(9, 1, 1, 8, 8, 16, 1) == 0
+    assert lib.flare_workspace_size(0, 1, 1, 8, 8, 24, 1) == 0
+    assert lib.flare_workspace_size(1, 1, 1, 8, 8, 16, 1) == 0   # the decode needs no workspace

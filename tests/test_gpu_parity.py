@@ -1,0 +1,315 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs from rank_latent_attention_amd.inputs, runs the
+same arrays through both sides and compares element by element with the
+rel-L2 bars: 1e-5 for float32 inputs, 1e-2 for bf16 inputs with float32
+accumulation.  The million-token workload is launched exactly as the
+benchmark launches it and checked on whole heads of Z and on sampled token
+rows of Y, which the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from helpers import TOL, dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def flare():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_attention_amd as r
+    r.load()
+    return r
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_flare(flare, w, scale=0.0):
+    import torch
+    Q, K, V = dev(w.Q, w.dtype), dev(w.K, w.dtype), dev(w.V, w.dtype)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    Y, _, _ = flare.flare_forward(Q, K, V, scale=scale, Z=Z, L=L)
+    torch.cuda.synchronize()
+    return host(Y), host(Z), host(L)
+
+
+def run_pp(flare, w, scale=0.0, alias=True):
+    import torch
+    d = w.dtype
+    Qs, Ks, Qf, K, V = dev(w.Qs, d), dev(w.Ks, d), dev(w.Qf, d), dev(w.K, d), dev(w.V, d)
+    Vs = Ks if (alias and w.Vs is w.Ks) else dev(w.Vs, d)
+    gate = dev(w.gate, "f32")
+    B, H, N, D = K.shape
+    M = Qs.shape[1]
+    Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    Y, _, _, _ = flare.flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale=scale, Q_out=Qo, Z=Z, L=L)
+    torch.cuda.synchronize()
+    return host(Y), host(Qo), host(Z), host(L)
+
+
+def check(name, got, ref, tol):
+    e = rel_l2(got, ref)
+    say(f"  {name}: rel-L2 {e:.3e} (bar {tol:g})")
+    assert e <= tol, f"{name}: rel-L2 {e:.3e} > {tol:g}"
+
+
+# --------------------------------------------------------------------------
+# The five workloads (the million-token one is sampled, below)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", ["c1", "c2f", "c2b", "c3a", "c3b"])
+def test_config_flare(flare, orc, cfg):
+    from rank_latent_attention_amd.inputs import CONFIGS
+    w = CONFIGS[cfg]()
+    say(f"[{cfg}] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D} {w.dtype}")
+    Y, Z, L = run_flare(flare, w)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    tol = TOL[w.dtype]
+    check("Z", Z, Zr, tol)
+    check("L", L, Lr, tol)
+    check("Y", Y, Yr, tol)
+
+
+def test_config4_flare_pp(flare, orc):
+    from rank_latent_attention_amd.inputs import config4
+    w = config4()
+    say(f"[c4] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D} {w.dtype}")
+    Y, Qo, Z, L = run_pp(flare, w)
+    Yr, Qr, Zr, Lr = orc.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+    tol = TOL[w.dtype]
+    check("Q", Qo, Qr, tol)
+    check("Z", Z, Zr, tol)
+    check("L", L, Lr, tol)
+    check("Y", Y, Yr, tol)
+
+
+def _sample_tokens(N, seed, count=2048):
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([[0, 1, N // 2, N - 2, N - 1], rng.choice(N, size=count, replace=False)])
+    return np.unique(idx)
+
+
+@pytest.mark.parametrize("pp", [False, True], ids=["c5", "c5pp"])
+def test_config5_million_tokens_sampled(flare, orc, pp):
+    import torch
+    from rank_latent_attention_amd.inputs import config5
+    w = config5(pp=pp)
+    say(f"[{'c5pp' if pp else 'c5'}] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D} {w.dtype} (full launch, sampled check)")
+    if pp:
+        Y, Qo, Z, L = run_pp(flare, w)
+    else:
+        Y, Z, L = run_flare(flare, w)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Z)) and np.all(np.isfinite(L))
+    idx = _sample_tokens(w.N, 11)
+    tol = TOL[w.dtype]
+    for h in (0, 5):
+        sl = slice(h, h + 1)
+        K, V = w.K[:, sl], w.V[:, sl]
+        if pp:
+            Qb = orc.pp_queries(w.Qs[sl], w.Ks[:, sl], w.Vs[:, sl], w.Qf[sl], w.gate[sl])
+            check(f"head {h} Q", Qo[:, sl], Qb, tol)
+            Zr, Lr = orc.encode(Qb, K, V)
+            Yr = orc.decode(Qb, K, Zr, idx=idx)
+        else:
+            Zr, Lr = orc.encode(w.Q[sl], K, V)
+            Yr = orc.decode(w.Q[sl], K, Zr, idx=idx)
+        check(f"head {h} Z", Z[:, sl], Zr, tol)
+        check(f"head {h} L", L[:, sl], Lr, tol)
+        check(f"head {h} Y[{idx.size} tokens]", Y[:, sl][:, :, idx], Yr, tol)
+    del torch
+
+
+# --------------------------------------------------------------------------
+# Shapes: ragged tails, tiny and maximal latent counts, both widths and dtypes
+# --------------------------------------------------------------------------
+
+SHAPES = [  # B, H, N, M, D
+    (1, 1, 1, 1, 16), (1, 1, 5, 3, 16), (1, 2, 31, 32, 32), (2, 3, 100, 33, 32), (1, 2, 300, 65, 16),
+    (1, 1, 1000, 200, 32), (2, 2, 257, 256, 16), (1, 1, 129, 96, 32), (3, 1, 4099, 128, 16),
+    (1, 1, 20000, 256, 32), (1, 1, 640, 17, 16),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}N{}M{}D{}".format(*s))
+def test_shapes(flare, orc, shape, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    B, H, N, M, D = shape
+    w = make_gaussian(B, H, N, M, D, dtype, seed=sum(shape))
+    say(f"[shape] {shape} {dtype}")
+    Y, Z, L = run_flare(flare, w)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    tol = TOL[dtype]
+    check("Z", Z, Zr, tol)
+    check("L", L, Lr, tol)
+    check("Y", Y, Yr, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batched_queries(flare, orc, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(2, 3, 700, 48, 32, dtype, seed=5)
+    rng = np.random.default_rng(6)
+    from rank_latent_attention_amd.inputs import to_dtype
+    w.Q = to_dtype(rng.standard_normal((2, 3, 48, 32)) / math.sqrt(32), dtype)
+    Y, Z, L = run_flare(flare, w)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    check("Z", Z, Zr, TOL[dtype])
+    check("Y", Y, Yr, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pp_shapes_and_unshared_values(flare, orc, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian_pp
+    for shape, share in [((2, 2, 333, 40, 16), True), ((1, 3, 1500, 64, 32), False)]:
+        w = make_gaussian_pp(*shape, dtype=dtype, seed=7, share_vs=share)
+        say(f"[pp] {shape} {dtype} shared={share}")
+        Y, Qo, Z, L = run_pp(flare, w)
+        Yr, Qr, Zr, Lr = orc.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+        check("Q", Qo, Qr, TOL[dtype])
+        check("Z", Z, Zr, TOL[dtype])
+        check("Y", Y, Yr, TOL[dtype])
+
+
+def test_encode_and_decode_entry_points(flare, orc):
+    import torch
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(2, 2, 777, 64, 16, "f32", seed=8)
+    Q, K, V = dev(w.Q, "f32"), dev(w.K, "f32"), dev(w.V, "f32")
+    Z, L = flare.flare_encode(Q, K, V)
+    Zr, Lr = orc.encode(w.Q, w.K, w.V)
+    check("encode Z", host(Z), Zr, 1e-5)
+    check("encode L", host(L), Lr, 1e-5)
+    Zin = dev(Zr, "f32")                      # decode on the oracle's latents
+    Y = flare.flare_decode(Q, K, Zin)
+    torch.cuda.synchronize()
+    check("decode Y", host(Y), orc.decode(w.Q, w.K, Zr), 1e-5)
+
+
+# --------------------------------------------------------------------------
+# Closed forms and properties
+# --------------------------------------------------------------------------
+
+def test_hand_example_embedded(flare):
+    """Worked example (s = 1, D = 1) padded to D = 16 with zeros: exact values."""
+    import torch
+    D = 16
+    Q = np.zeros((1, 2, D), np.float32); Q[0, 1, 0] = 1.0
+    K = np.zeros((1, 1, 2, D), np.float32); K[0, 0, 1, 0] = math.log(3.0)
+    V = np.zeros((1, 1, 2, D), np.float32); V[0, 0, 0, 0] = 1.0; V[0, 0, 1, 0] = 5.0
+    Zt = torch.empty((1, 1, 2, D), dtype=torch.float32, device="cuda:0")
+    Lt = torch.empty((1, 1, 2), dtype=torch.float32, device="cuda:0")
+    Y, _, _ = flare.flare_forward(dev(Q, "f32"), dev(K, "f32"), dev(V, "f32"), scale=1.0, Z=Zt, L=Lt)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(Zt)[0, 0, :, 0], [3.0, 4.0], rtol=2e-6)
+    np.testing.assert_allclose(host(Lt)[0, 0], [math.log(2), math.log(4)], rtol=2e-6)
+    np.testing.assert_allclose(host(Y)[0, 0, :, 0], [3.5, 3.75], rtol=2e-6)
+    assert np.all(host(Zt)[..., 1:] == 0) and np.all(host(Y)[..., 1:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identical_keys_give_mean(flare, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(1, 2, 3000, 64, 32, dtype, seed=9)
+    w.K = np.ascontiguousarray(np.broadcast_to(w.K[:, :, :1], w.K.shape))
+    Y, Z, L = run_flare(flare, w)
+    mean = w.V.astype(np.float64).mean(axis=2, keepdims=True)
+    check("Z vs mean(V)", Z, np.broadcast_to(mean, Z.shape), TOL[dtype])
+    check("Y vs mean(V)", Y, np.broadcast_to(mean, Y.shape), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_permutation_equivariance(flare, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(1, 2, 2000, 64, 16, dtype, seed=10)
+    perm = np.random.default_rng(11).permutation(w.N)
+    Y, Z, L = run_flare(flare, w)
+    w.K, w.V = np.ascontiguousarray(w.K[:, :, perm]), np.ascontiguousarray(w.V[:, :, perm])
+    Yp, Zp, Lp = run_flare(flare, w)
+    tol = TOL[dtype]
+    check("Z permuted", Zp, Z, tol)
+    check("L permuted", Lp, L, tol)
+    check("Y permuted", Yp, Y[:, :, perm], tol)
+
+
+def test_bitwise_reproducible(flare):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(2, 4, 50000, 128, 32, "bf16", seed=12)
+    a = run_flare(flare, w)
+    b = run_flare(flare, w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_shared_values_path_equals_copy(flare):
+    from rank_latent_attention_amd.inputs import make_gaussian_pp
+    w = make_gaussian_pp(2, 2, 5000, 64, 32, dtype="bf16", seed=13, share_vs=True)
+    a = run_pp(flare, w, alias=True)
+    b = run_pp(flare, w, alias=False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_scores_do_not_overflow(flare, orc, dtype):
+    """Scores of order 1e2-1e3 in log2 units: the lazy shift must be raised."""
+    from rank_latent_attention_amd.inputs import make_gaussian, to_dtype
+    w = make_gaussian(1, 2, 4000, 64, 16, dtype, seed=14)
+    w.Q = to_dtype(w.Q.astype(np.float64) * 60.0, dtype)
+    Y, Z, L = run_flare(flare, w)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Z)) and np.all(np.isfinite(L))
+    # bf16 scores this large amplify the rounding of the queries into the
+    # exponent; the bar scales with the score magnitude for bf16
+    tol = TOL[dtype] if dtype == "f32" else 5e-2
+    check("Z", Z, Zr, tol)
+    check("L", L, Lr, TOL[dtype])
+    check("Y", Y, Yr, tol)
+
+
+def test_explicit_scale(flare, orc):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(1, 2, 900, 32, 16, "f32", seed=15)
+    Y, Z, L = run_flare(flare, w, scale=0.37)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V, scale=0.37)
+    check("Z", Z, Zr, 1e-5)
+    check("Y", Y, Yr, 1e-5)
+
+
+def test_empty_token_axis(flare):
+    """N = 0: every latent is an empty row, Z = 0 and L = -inf (App. B.3)."""
+    import torch
+    Q = torch.randn(2, 8, 16, device="cuda:0")
+    K = torch.empty(1, 2, 0, 16, device="cuda:0")
+    Z = torch.full((1, 2, 8, 16), 7.0, device="cuda:0")
+    L = torch.zeros((1, 2, 8), device="cuda:0")
+    flare.flare_forward(Q, K, K.clone(), Z=Z, L=L)
+    torch.cuda.synchronize()
+    assert torch.all(Z == 0) and torch.all(torch.isneginf(L))
+
+
+def test_workspace_too_small_is_rejected(flare):
+    import torch
+    from rank_latent_attention_amd.flare import FlareError, OP_FORWARD, workspace_size
+    Q = torch.randn(1, 64, 16, device="cuda:0")
+    K = torch.randn(1, 1, 4096, 16, device="cuda:0")
+    need = workspace_size(OP_FORWARD, 1, 1, 4096, 64, 16, 0)
+    assert need > 0
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(FlareError) as e:
+        flare.flare_forward(Q, K, K, ws=ws)
+    assert e.value.status == 3
