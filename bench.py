@@ -34,32 +34,28 @@ def log(*a):
 
 
 def cpu_baseline(w, target_s: float = 15.0):
-    """The fp64 oracle on a bounded sample: one head, the first n tokens."""
+    """The fp64 oracle on a bounded sample: all N tokens of the first k heads,
+    k chosen from a one-head timing so the sample takes about target_s."""
     import oracle
     oracle.build(force=False)
     cores = oracle.threads()
-    h = 0
 
-    def run(n):
-        Q = w.Q[h:h + 1]
-        K = np.ascontiguousarray(w.K[:, h:h + 1, :n])
-        V = np.ascontiguousarray(w.V[:, h:h + 1, :n])
+    def run(k):
+        Q = w.Q[:k]
+        K = np.ascontiguousarray(w.K[:, :k])
+        V = np.ascontiguousarray(w.V[:, :k])
         t0 = time.perf_counter()
         oracle.flare_forward(Q, K, V)
         return time.perf_counter() - t0
 
-    n = min(16384, w.N)
-    t = run(n)
-    n2 = int(min(w.N, max(n, n * target_s / max(t, 1e-3))))
-    n2 = max(1024, (n2 // 1024) * 1024)
-    t2 = run(n2) if n2 != n else t
-    n, t = (n2, t2)
-    # tokens/s of the whole routing pass: a token needs all H heads
-    value = n / t / w.H
+    t1 = run(1)
+    k = int(max(1, min(w.H, round(target_s / max(t1, 1e-3)))))
+    t = run(k) if k > 1 else t1
+    # a token of the whole routing pass needs all H heads
+    value = w.B * w.N * k / (t * w.H)
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle FLARE forward on head 0 of {w.H}, first {n} of {w.N} tokens "
-                      f"(M={w.M}, D={w.D}), {t:.1f} s on {cores} threads ({platform.processor() or 'host cpu'}); "
-                      f"rate divided by H for whole-pass tokens/s"}
+            "sample": f"fp64 oracle FLARE forward (encode + decode) on heads 0..{k - 1} of {w.H}, all {w.N} tokens, "
+                      f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
 
 
 def main():

@@ -26,8 +26,12 @@ def hipcc() -> str:
 
 def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # NaN inputs are undefined behaviour of the library: no NaN canonicalisation around max
+            "-fno-honor-nans",
             # hipcc must not emit packed-fp32 VALU instructions on this target
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs (no AGPR copies around the softmax)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, SRC, "-o", out]
 
 

@@ -48,7 +48,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kTile = 128;         // tokens per encode LDS tile (4 blocks of 32)
-constexpr int kDecGroup = 256;     // tokens per decode step of a workgroup (64 per wave)
+constexpr int kDecGroup = 128;     // tokens per decode step of a workgroup (32 per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTheta = 8.0f;     // lazy-rescale threshold, log2 units
@@ -176,19 +176,64 @@ __device__ inline void zero_pv(PVOp<float>& o) {
   for (int j = 0; j < 16; ++j) o.a[j] = 0.f;
 }
 
-// acc += X^T P, P being the (already exponentiated) score tile in registers.
-__device__ inline f32x16 pv_mma(const PVOp<bf16>& a, const f32x16& p, f32x16 acc) {
+// acc += X^T P, P being the (already exponentiated) score tile in registers,
+// and the softmax denominator of this lane's column.  With D = 16 the A
+// operand's row 16 is all ones (see ones_pv), so accumulator row 16 collects
+// the column sums inside the MFMA and lsum is unused.  bf16 with D = 32 sums
+// the bf16 weights that enter the MFMA with packed dot products; float32 with
+// D = 32 adds the weights.
+template <int D> __device__ inline f32x16 pv_accum(const PVOp<bf16>& a, const f32x16& p, f32x16 acc, float& lsum) {
   bf16x8 b0, b1;
 #pragma unroll
   for (int s = 0; s < 8; ++s) { b0[s] = (bf16)p[s]; b1[s] = (bf16)p[8 + s]; }
+  if constexpr (D == 32) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b0[s], b0[s + 1]}, one, l0, false);
+      l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b1[s], b1[s + 1]}, one, l1, false);
+    }
+    lsum += l0 + l1;
+  }
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a0, b0, acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a1, b1, acc, 0, 0, 0);
   return acc;
 }
-__device__ inline f32x16 pv_mma(const PVOp<float>& a, const f32x16& p, f32x16 acc) {
+template <int D> __device__ inline f32x16 pv_accum(const PVOp<float>& a, const f32x16& p, f32x16 acc, float& lsum) {
+  if constexpr (D == 32) {
+    float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) { t0 += p[j]; t1 += p[j + 1]; t2 += p[j + 2]; t3 += p[j + 3]; }
+    lsum += (t0 + t1) + (t2 + t3);
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[j], p[j], acc, 0, 0, 0);
   return acc;
+}
+
+// Softmax denominator of this lane's column, on both lanes of the pair.
+template <int D> __device__ inline float col_sum(float lsum, const f32x16& acc) {
+  if constexpr (D == 16) {  // accumulator row 16 = register 8 of the lower half
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8]), __float_as_uint(acc[8]), false, false);
+    return __uint_as_float(r[0]);
+  } else {
+    return pair_sum(lsum);
+  }
+}
+
+// PV A operand of a lane whose feature row is beyond D: zero, except row 16
+// (lanes 16 and 48), which is all ones when D = 16.
+__device__ inline void ones_pv(PVOp<bf16>& o, int li, int D) {
+  const bf16 v = (bf16)(D == 16 && li == 16 ? 1.f : 0.f);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) { o.a0[s] = v; o.a1[s] = v; }
+}
+__device__ inline void ones_pv(PVOp<float>& o, int li, int D) {
+  const float v = D == 16 && li == 16 ? 1.f : 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o.a[j] = v;
 }
 
 // One online-softmax step on a 32x32 score tile whose column (this lane's
@@ -198,10 +243,10 @@ __device__ inline f32x16 pv_mma(const PVOp<float>& a, const f32x16& p, f32x16 ac
 // raised to the tile maximum when that exceeds it by more than kTheta, or on
 // the first non-empty tile; the running sum and accumulator are rescaled then.
 __device__ inline void online_step(f32x16& s, f32x16& negshift, bool& started, float& lsum, f32x16& acc) {
-  float t = s[0];
+  float t = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) t = fmaxf(t, s[r]);
-  t = pair_max(t);
+  for (int r = 3; r < 15; r += 2) t = fmaxf(fmaxf(t, s[r]), s[r + 1]);
+  t = pair_max(fmaxf(t, s[15]));
   const bool need = (t > kTheta) || (!started && t > -INFINITY);
   if (need) {
     const float f = started ? fast_exp2(-t) : 0.f;
@@ -211,7 +256,96 @@ __device__ inline void online_step(f32x16& s, f32x16& negshift, bool& started, f
     started = true;
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { s[r] = fast_exp2(s[r]); lsum += s[r]; }
+  for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r]);
+}
+
+// ----------------------------------------------------------------------------
+// bf16 tiles in LDS, row-major with 16-byte chunks XOR-swizzled per row so that
+// 16 consecutive rows read at one chunk column, and 4 rows read across all
+// chunks, hit distinct banks.  Tiles are filled by LDS DMA (global_load_lds,
+// 16 bytes per lane, no VGPR staging); the PV operand gathers token columns
+// with the transposing read ds_read_b64_tr_b16.
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D> __device__ inline int chunk_pos(int n, int c) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int sw = CPR == 4 ? ((n >> 2) & 3) : ((n >> 3) & 1);
+  return n * CPR + (c ^ sw);
+}
+
+// Element offset of (row n, feature d) in a swizzled tile.
+template <int D> __device__ inline int tile_off(int n, int d) { return chunk_pos<D>(n, d >> 3) * 8 + (d & 7); }
+
+// Issue the DMA of rows [t0, t0 + kTile) of a [*, D] bf16 matrix into a
+// swizzled tile.  Rows at or beyond n_hi repeat row n_hi - 1 (they are masked
+// out of the softmax by the caller), so no read leaves the matrix.
+template <int D, int NW>
+__device__ inline void dma_tile(bf16* tile, const bf16* src, int t0, int n_hi, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int INSTR = kTile * CPR / 64;  // 64 chunks (1 KB) per wave instruction
+#pragma unroll
+  for (int i = wave; i < INSTR; i += NW) {
+    const int P = i * 64 + lane;
+    const int n = P / CPR;
+    const int c = (P % CPR) ^ (CPR == 4 ? ((n >> 2) & 3) : ((n >> 3) & 1));
+    int row = t0 + n;
+    row = row < n_hi ? row : n_hi - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)row * D + c * 8), (lds_void*)(tile + i * 512),
+                                     16, 0, 0);
+  }
+}
+
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-lane byte offsets into a swizzled tile for token block 0.  The XOR
+// swizzle of a row only depends on the row index modulo 32, so token block nb
+// adds nb * 64 * D bytes to every offset.
+//   kq[st]: QK operand (key row li, chunk 2 st + g)
+//   vq[k] : transposing read k of the PV operand: in a group of 16 lanes, lane
+//           i points at row 8 k + 4 g + i/4, features d0 + 4 (i % 4) .. +3, so
+//           lane j of the group receives feature d0 + j of rows 8 k + 4 g .. +3
+//           (the four runs of acc_row).  Feature groups beyond D read
+//           features 0..15 and are replaced by ones_pv afterwards.
+template <int D> struct TileOffs {
+  unsigned kq[D / 16];
+  unsigned vq[4];
+};
+template <int D> __device__ inline TileOffs<D> tile_offsets(int lane) {
+  TileOffs<D> o;
+  const int li = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) o.kq[st] = chunk_pos<D>(li, 2 * st + g) * 16;
+  const int i = lane & 15, q = lane >> 4;
+  const int d0 = 16 * (q & 1);
+  const int d = (d0 < D ? d0 : 0) + 4 * (i & 3);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.vq[k] = tile_off<D>(8 * k + 4 * g + (i >> 2), d) * 2;
+  return o;
+}
+
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <typename V> __device__ inline V lds_load(unsigned addr) {
+  return *(const __attribute__((address_space(3))) V*)(uintptr_t)addr;
+}
+
+// The transposing reads are issued as inline assembly: the compiler does not
+// know which LDS bytes the builtin touches and would otherwise wait for every
+// DMA in flight (including the one filling the other buffer) before each
+// read.  pv_wait() must run before the operand is used; it takes the operand
+// as an in/out value so no use can be scheduled ahead of it.  Only tiles whose
+// DMA completed before the last barrier are read this way.
+template <int OFF> __device__ inline bf16x4 tr_read(unsigned addr) {
+  bf16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+__device__ inline void pv_wait(PVOp<bf16>& o, int lane, int D) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o.a0), "+v"(o.a1));
+  if (16 * ((lane >> 4) & 1) >= D) ones_pv(o, lane & 31, D);  // feature rows beyond D
 }
 
 // ----------------------------------------------------------------------------
@@ -334,7 +468,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
         load_op<D>(kop, ks + (32 * nb + li) * L::KST, g);
         PVOp<T> vop;
         if (li < D) load_pv(vop, vt + li * L::VST + 32 * nb, g);
-        else zero_pv(vop);
+        else ones_pv(vop, li, D);
         const bool tail = row0 + 32 > n_hi;
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
@@ -345,7 +479,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
               if (row0 + acc_row(r, g) >= n_hi) s[r] = -INFINITY;
           }
           online_step(s, negs[mb], started[mb], lsum[mb], acc[mb]);
-          acc[mb] = pv_mma(vop, s, acc[mb]);
+          acc[mb] = pv_accum<D>(vop, s, acc[mb], lsum[mb]);
         }
       }
       if (L::DB) {
@@ -363,7 +497,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
       const int m = (mg * MBW + mb) * 32 + li;
-      const float ltot = pair_sum(lsum[mb]);
+      const float ltot = col_sum<D>(lsum[mb], acc[mb]);
       if (m < M) {
         const size_t p = (size_t)bhl * a.pmax + slot;
         float* dst = a.part_acc + (p * M + m) * D;
@@ -376,6 +510,146 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
         }
         if (g == 0) a.part_al[p * M + m] = make_float2(-negs[mb][0], ltot);
       }
+    }
+    x = hb + n_hi;
+  }
+}
+
+// Token block NB of a tile (at LDS byte addresses kb/vb + NB * 64 * D) for one
+// wave's 32 latents.  row0 is the block's first token, n_hi the end of the
+// piece.
+template <int D, int NB>
+__device__ inline void encode_block(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int row0, int n_hi,
+                                    int g, int lane, const QKOp<bf16, D>& qop, f32x16& negs, bool& started,
+                                    float& lsum, f32x16& acc) {
+  constexpr int OFF = NB * 64 * D;
+  if (row0 >= n_hi) return;
+  QKOp<bf16, D> kop;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) kop.v[st] = lds_load<bf16x8>(ka[st] + OFF);
+  PVOp<bf16> vop;
+  {
+    const bf16x4 r0 = tr_read<OFF>(va[0]), r1 = tr_read<OFF>(va[1]);
+    const bf16x4 r2 = tr_read<OFF>(va[2]), r3 = tr_read<OFF>(va[3]);
+    vop.a0 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    vop.a1 = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  f32x16 sc = qk_mma<D>(kop, qop, negs);
+  if (row0 + 32 > n_hi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (row0 + acc_row(r, g) >= n_hi) sc[r] = -INFINITY;
+  }
+  online_step(sc, negs, started, lsum, acc);
+  pv_wait(vop, lane, D);
+  acc = pv_accum<D>(vop, sc, acc, lsum);
+}
+
+// The 128-token tile at t0 for one wave: token blocks ng, ng + WN, ...
+// (the per-wave offset ng * 64 * D is already folded into ka / va).
+template <int D, int WN>
+__device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
+                                   int lane, const QKOp<bf16, D>& qop, f32x16& negs, bool& started, float& lsum,
+                                   f32x16& acc) {
+  encode_block<D, 0>(ka, va, t0, n_hi, g, lane, qop, negs, started, lsum, acc);
+  if constexpr (WN <= 2) encode_block<D, WN>(ka, va, t0 + 32 * WN, n_hi, g, lane, qop, negs, started, lsum, acc);
+  if constexpr (WN == 1) {
+    encode_block<D, 2>(ka, va, t0 + 64, n_hi, g, lane, qop, negs, started, lsum, acc);
+    encode_block<D, 3>(ka, va, t0 + 96, n_hi, g, lane, qop, negs, started, lsum, acc);
+  }
+}
+
+// bf16 encode: NW waves in WN token lanes of G = NW / WN latent groups; wave w
+// owns latent block w % G (32 latents) and token blocks w / G + k WN of every
+// 128-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
+// DMA of the next tile is in flight while the current one is consumed.
+template <typename QT, int D, int NW, int WN>
+__global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
+  constexpr int TE = kTile * D;  // elements per tile
+  constexpr int G = NW / WN;
+  __shared__ __align__(16) bf16 k0[TE], v0[TE], k1[TE], v1[TE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, g = lane >> 5;
+  const int mg = wave % G, ng = wave / G;
+  const int N = a.N, M = a.M;
+  const bool alias = a.v_alias;
+
+  // LDS byte addresses of this lane's operands in both buffers
+  const TileOffs<D> to = tile_offsets<D>(lane);
+  const unsigned wofs = ng * 64 * D;
+  unsigned ka0[D / 16], ka1[D / 16], va0[4], va1[4];
+  {
+    const unsigned bk0 = lds_addr(k0) + wofs, bk1 = lds_addr(k1) + wofs;
+    const unsigned bv0 = lds_addr(alias ? k0 : v0) + wofs, bv1 = lds_addr(alias ? k1 : v1) + wofs;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) { ka0[st] = bk0 + to.kq[st]; ka1[st] = bk1 + to.kq[st]; }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { va0[k] = bv0 + to.vq[k]; va1[k] = bv1 + to.vq[k]; }
+  }
+
+  long long x = piece_start(blockIdx.x, a.total, a.nwg);
+  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  while (x < xe) {
+    const int bhl = (int)(x / N);
+    const long long hb = (long long)bhl * N;
+    const int n_lo = (int)(x - hb);
+    const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
+    const int bh = a.bh0 + bhl;
+    const int h = bh % a.H;
+    const int slot = (blockIdx.x - piece_of(hb, a.total, a.nwg)) * WN + ng;
+
+    const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
+    const int m = mg * 32 + li;
+    QKOp<bf16, D> qop;
+    if (m < M) load_op_scaled<D>(qop, Qh + (size_t)m * D, g, a.qscale);
+    else zero_op<D>(qop);
+    f32x16 negs, acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
+    float lsum = 0.f;
+    bool started = false;
+
+    const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
+    const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + (size_t)bh * N * D;
+    __syncthreads();  // the previous piece is done with the tiles
+    dma_tile<D, NW>(k0, Kh, n_lo, n_hi, wave, lane);
+    if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
+    wait_dma();
+    __syncthreads();
+    for (int t0 = n_lo; t0 < n_hi; t0 += 2 * kTile) {
+      // tile t0 from buffer 0 while tile t0 + kTile streams into buffer 1
+      const int tn = t0 + kTile;
+      if (tn < n_hi) {
+        dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
+        if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
+      }
+      encode_tile<D, WN>(ka0, va0, t0 + 32 * ng, n_hi, g, lane, qop, negs, started, lsum, acc);
+      wait_dma();
+      __syncthreads();
+      if (tn >= n_hi) break;
+      // tile tn from buffer 1 while tn + kTile streams into buffer 0
+      const int tn2 = tn + kTile;
+      if (tn2 < n_hi) {
+        dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
+        if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
+      }
+      encode_tile<D, WN>(ka1, va1, tn + 32 * ng, n_hi, g, lane, qop, negs, started, lsum, acc);
+      wait_dma();
+      __syncthreads();
+    }
+
+    const float ltot = col_sum<D>(lsum, acc);
+    if (m < M) {
+      const size_t p = (size_t)bhl * a.pmax + slot;
+      float* dst = a.part_acc + (p * M + m) * D;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (8 * c + 4 * g < D) {
+          f32x4 v = {acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+          *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g) = v;
+        }
+      }
+      if (g == 0) a.part_al[p * M + m] = make_float2(-negs[0], ltot);
     }
     x = hb + n_hi;
   }
@@ -400,45 +674,64 @@ struct MergeArgs {
   int N, M, D, H, WN, nwg, pmax, bh0, nbh;
 };
 
+// One workgroup per (head, latent); thread (pg, d) folds the splits
+// p = pg, pg + PG, ... into a local (A, den, num) with the same rule, and the
+// PG partial results are then combined in ascending pg order.
 template <typename QT>
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
-  const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (long long)a.nbh * a.M * a.D) return;
-  const int d = (int)(idx % a.D);
-  const long long t = idx / a.D;
-  const int m = (int)(t % a.M);
-  const int bhl = (int)(t / a.M);
+  __shared__ float sA[kThreads], sDen[kThreads], sNum[kThreads];
+  const int D = a.D, PG = kThreads / D;
+  const int pg = threadIdx.x / D, d = threadIdx.x % D;
+  const int m = blockIdx.x % a.M;
+  const int bhl = blockIdx.x / a.M;
   const int bh = a.bh0 + bhl;
-  float z = 0.f, lse = -INFINITY;
+  float A = -INFINITY, den = 0.f, num = 0.f;
   if (a.N > 0) {
     const long long hb = (long long)bhl * a.N;
-    const int w0 = piece_of(hb, a.total, a.nwg);
-    const int w1 = piece_of(hb + a.N - 1, a.total, a.nwg);
-    const int cnt = (w1 - w0 + 1) * a.WN;
+    const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
-    float A = -INFINITY;
-    for (int p = 0; p < cnt; ++p) {
+#pragma unroll 4
+    for (int p = pg; p < cnt; p += PG) {
       const float2 v = a.part_al[(base + p) * a.M + m];
-      if (v.y > 0.f) A = fmaxf(A, v.x);
-    }
-    if (A > -INFINITY) {
-      float den = 0.f, num = 0.f;
-      for (int p = 0; p < cnt; ++p) {
-        const float2 v = a.part_al[(base + p) * a.M + m];
-        if (v.y > 0.f) {
-          const float w = fast_exp2(v.x - A);
-          den += w * v.y;
-          num += w * a.part_acc[((base + p) * a.M + m) * a.D + d];
+      const float u = a.part_acc[((base + p) * a.M + m) * D + d];
+      if (v.y > 0.f) {
+        if (v.x > A) {
+          const float f = fast_exp2(A - v.x);  // 0 while A = -inf
+          den *= f;
+          num *= f;
+          A = v.x;
         }
+        const float w = fast_exp2(v.x - A);
+        den += w * v.y;
+        num += w * u;
       }
-      z = num / den;
-      lse = kLn2 * (A + __builtin_amdgcn_logf(den));
     }
   }
-  const size_t o = ((size_t)bh * a.M + m) * a.D + d;
+  sA[threadIdx.x] = A;
+  sDen[threadIdx.x] = den;
+  sNum[threadIdx.x] = num;
+  __syncthreads();
+  if (pg != 0) return;
+  float At = -INFINITY;
+  for (int t = 0; t < PG; ++t) At = fmaxf(At, sA[t * D + d]);
+  float z = 0.f, lse = -INFINITY;
+  if (At > -INFINITY) {
+    float dt = 0.f, nt = 0.f;
+    for (int t = 0; t < PG; ++t) {
+      const float At_t = sA[t * D + d];
+      if (At_t > -INFINITY) {
+        const float w = fast_exp2(At_t - At);
+        dt += w * sDen[t * D + d];
+        nt += w * sNum[t * D + d];
+      }
+    }
+    z = nt / dt;
+    lse = kLn2 * (At + __builtin_amdgcn_logf(dt));
+  }
+  const size_t o = ((size_t)bh * a.M + m) * D + d;
   if (a.Qout) {
     const int h = bh % a.H;
-    const float qf = to_f(reinterpret_cast<const QT*>(a.Qf)[((size_t)h * a.M + m) * a.D + d]);
+    const float qf = to_f(reinterpret_cast<const QT*>(a.Qf)[((size_t)h * a.M + m) * D + d]);
     a.Qout[o] = qf + a.gate[h] * z;
   } else {
     a.Z[o] = z;
@@ -502,64 +795,59 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs a) {
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
-    for (int t0 = n_lo + 64 * wave; t0 < n_hi; t0 += kDecGroup) {
-      QKOp<T, D> kop[2];
-      f32x16 negs[2], acc[2];
-      float lsum[2];
-      bool started[2];
+    // wave w takes tokens t0 + [0, 32) for t0 = n_lo + 32 w, + kDecGroup, ...;
+    // the next block's key rows are fetched while the current one is decoded
+    int t0 = n_lo + 32 * wave;
+    QKOp<T, D> kop;
+    if (t0 + li < n_hi) load_op<D>(kop, Kh + (size_t)(t0 + li) * D, g);
+    else zero_op<D>(kop);
+    for (; t0 < n_hi; t0 += kDecGroup) {
+      QKOp<T, D> knext;
+      const int tn = t0 + kDecGroup + li;
+      if (tn < n_hi) load_op<D>(knext, Kh + (size_t)tn * D, g);
+      else zero_op<D>(knext);
+      f32x16 negs, acc;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = t0 + 32 * j + li;
-        if (n < n_hi) load_op<D>(kop[j], Kh + (size_t)n * D, g);
-        else zero_op<D>(kop[j]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { negs[j][r] = 0.f; acc[j][r] = 0.f; }
-        lsum[j] = 0.f;
-        started[j] = false;
-      }
+      for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
+      float lsum = 0.f;
+      bool started = false;
       for (int mb = 0; mb < MB; ++mb) {
         QKOp<T, D> qop;
         load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
         PVOp<T> zop;
         if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
-        else zero_pv(zop);
-        const bool tail = mask_tail && mb == MB - 1;
+        else ones_pv(zop, li, D);
+        f32x16 sc = qk_mma<D>(qop, kop, negs);
+        if (mask_tail && mb == MB - 1) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          f32x16 s = qk_mma<D>(qop, kop[j], negs[j]);
-          if (tail) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (mb * 32 + acc_row(r, g) >= M) s[r] = -INFINITY;
-          }
-          online_step(s, negs[j], started[j], lsum[j], acc[j]);
-          acc[j] = pv_mma(zop, s, acc[j]);
+          for (int r = 0; r < 16; ++r)
+            if (mb * 32 + acc_row(r, g) >= M) sc[r] = -INFINITY;
         }
+        online_step(sc, negs, started, lsum, acc);
+        acc = pv_accum<D>(zop, sc, acc, lsum);
       }
+      const int n = t0 + li;
+      const float inv = 1.f / col_sum<D>(lsum, acc);
+      if (n < n_hi) {
+        T* dst = Yh + (size_t)n * D;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = t0 + 32 * j + li;
-        const float inv = 1.f / pair_sum(lsum[j]);
-        if (n < n_hi) {
-          T* dst = Yh + (size_t)n * D;
+        for (int c = 0; c < 4; ++c) {
+          if (8 * c + 4 * g < D) {
+            if constexpr (sizeof(T) == 2) {
+              bf16x4 v;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (8 * c + 4 * g < D) {
-              if constexpr (sizeof(T) == 2) {
-                bf16x4 v;
+              for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[4 * c + i] * inv);
+              *reinterpret_cast<bf16x4*>(dst + 8 * c + 4 * g) = v;
+            } else {
+              f32x4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[j][4 * c + i] * inv);
-                *reinterpret_cast<bf16x4*>(dst + 8 * c + 4 * g) = v;
-              } else {
-                f32x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = acc[j][4 * c + i] * inv;
-                *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g) = v;
-              }
+              for (int i = 0; i < 4; ++i) v[i] = acc[4 * c + i] * inv;
+              *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g) = v;
             }
           }
         }
       }
+      kop = knext;
     }
     x = hb + n_hi;
   }
@@ -596,23 +884,32 @@ inline int latent_blocks(int M) {
 }
 
 struct EncPlan {
-  int G, MBW, WN, nwg, pmax;
+  int G, MBW, WN, NW, nwg, pmax;
   long long total;
 };
 
-// Workgroups per encode launch: enough to fill the chip twice over, but at
-// least 128 tokens each.
-constexpr int kEncWgPerCu = 2;
+// Resident waves per compute unit the encode grid is sized for, and the
+// decode's workgroups per compute unit.
+constexpr int kEncWavesPerCu = 16;
 constexpr int kDecWgPerCu = 4;
 
-EncPlan plan_encode(const Dev& dev, int nbh, int N, int M) {
+// bf16: one 32-latent block per wave, max(4, blocks) waves per workgroup.
+// f32: up to two latent blocks per wave, 4 waves per workgroup.
+EncPlan plan_encode(const Dev& dev, int nbh, int N, int M, int dtype) {
   EncPlan p{};
   const int mbp = latent_blocks(M);
-  p.MBW = mbp >= 2 ? 2 : 1;
-  p.G = mbp / p.MBW;  // 1, 2 or 4 waves across the latents
-  p.WN = 4 / p.G;
+  if (dtype == FLARE_BF16) {
+    p.MBW = 1;
+    p.G = mbp;
+    p.NW = mbp > 4 ? mbp : 4;
+  } else {
+    p.MBW = mbp >= 2 ? 2 : 1;
+    p.G = mbp / p.MBW;
+    p.NW = 4;
+  }
+  p.WN = p.NW / p.G;
   p.total = (long long)nbh * N;
-  long long want = (long long)dev.cus * kEncWgPerCu;
+  long long want = (long long)dev.cus * kEncWavesPerCu / p.NW;
   long long maxw = cdiv(p.total, kTile);
   p.nwg = (int)(want < maxw ? want : maxw);
   if (p.nwg < 1) p.nwg = 1;
@@ -656,24 +953,36 @@ int check_common(int B, int H, int N, int M, int D, int dtype, int q_batched) {
   return FLARE_OK;
 }
 
-template <typename T, typename QT, int D, int MBW>
-int launch_encode_t(const EncArgs& a, hipStream_t st) {
-  const size_t lds = EncLds<T, D>::bytes;
-  hipLaunchKernelGGL((encode_kernel<T, QT, D, MBW>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+template <typename QT, int D, int NW, int WN>
+int launch_encode_dma(const EncArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((encode_dma_kernel<QT, D, NW, WN>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename T, typename QT>
-int launch_encode_d(const EncArgs& a, int D, int MBW, hipStream_t st) {
-  if (D == 16) return MBW == 2 ? launch_encode_t<T, QT, 16, 2>(a, st) : launch_encode_t<T, QT, 16, 1>(a, st);
-  return MBW == 2 ? launch_encode_t<T, QT, 32, 2>(a, st) : launch_encode_t<T, QT, 32, 1>(a, st);
+template <typename QT, int D>
+int launch_encode_bf16_d(const EncArgs& a, int NW, int WN, hipStream_t st) {
+  if (NW == 8) return launch_encode_dma<QT, D, 8, 1>(a, st);
+  if (WN == 4) return launch_encode_dma<QT, D, 4, 4>(a, st);
+  if (WN == 2) return launch_encode_dma<QT, D, 4, 2>(a, st);
+  return launch_encode_dma<QT, D, 4, 1>(a, st);
+}
+
+template <typename QT>
+int launch_encode_bf16(const EncArgs& a, int D, int NW, int WN, hipStream_t st) {
+  return D == 16 ? launch_encode_bf16_d<QT, 16>(a, NW, WN, st) : launch_encode_bf16_d<QT, 32>(a, NW, WN, st);
+}
+
+template <int D, int MBW>
+int launch_encode_f32(const EncArgs& a, hipStream_t st) {
+  const size_t lds = EncLds<float, D>::bytes;
+  hipLaunchKernelGGL((encode_kernel<float, float, D, MBW>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
 // qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
-int launch_encode(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0,
-                  int nbh, int H, int N, int M, int D, int dtype, float qscale, float* part_acc, float2* part_al,
-                  const EncPlan& p, hipStream_t st) {
-  (void)dev;
+int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0, int H, int N,
+                  int M, int D, int dtype, float qscale, float* part_acc, float2* part_al, const EncPlan& p,
+                  hipStream_t st) {
   EncArgs a;
   a.Q = Q; a.K = K; a.V = V;
   a.part_acc = part_acc; a.part_al = part_al;
@@ -682,11 +991,12 @@ int launch_encode(const Dev& dev, const void* Q, int qtype, int q_batched, const
   a.G = p.G; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0;
   a.qscale = qscale;
   if (dtype == FLARE_BF16) {
-    if (qtype == FLARE_BF16) return launch_encode_d<bf16, bf16>(a, D, p.MBW, st);
-    return launch_encode_d<bf16, float>(a, D, p.MBW, st);
+    if (qtype == FLARE_BF16) return launch_encode_bf16<bf16>(a, D, p.NW, p.WN, st);
+    return launch_encode_bf16<float>(a, D, p.NW, p.WN, st);
   }
   if (qtype != FLARE_F32) return FLARE_ERR_UNSUPPORTED;
-  return launch_encode_d<float, float>(a, D, p.MBW, st);
+  if (D == 16) return p.MBW == 2 ? launch_encode_f32<16, 2>(a, st) : launch_encode_f32<16, 1>(a, st);
+  return p.MBW == 2 ? launch_encode_f32<32, 2>(a, st) : launch_encode_f32<32, 1>(a, st);
 }
 
 int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H, int N,
@@ -697,8 +1007,7 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   a.Z = Z; a.L = L; a.Qf = Qf; a.gate = gate; a.Qout = Qout;
   a.total = p.total;
   a.N = N; a.M = M; a.D = D; a.H = H; a.WN = p.WN; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0; a.nbh = nbh;
-  const long long n = (long long)nbh * M * D;
-  const dim3 grid((unsigned)cdiv(n, kThreads));
+  const dim3 grid((unsigned)((long long)nbh * M));
   if (qftype == FLARE_BF16) hipLaunchKernelGGL((merge_kernel<bf16>), grid, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((merge_kernel<float>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
@@ -730,7 +1039,7 @@ int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const
   a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = bh0;
   a.qscale = qscale;
   long long want = (long long)dev.cus * kDecWgPerCu;
-  long long maxw = cdiv(a.total, 64);
+  long long maxw = cdiv(a.total, 32);
   a.nwg = (int)(want < maxw ? want : maxw);
   const size_t lds = decode_lds(dtype, D, M);
   if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
@@ -762,7 +1071,7 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
     const int groups[3] = {grp, BH % grp ? BH % grp : grp, op == FLARE_OP_PP_FORWARD ? BH : grp};
     size_t max_acc = 0, max_al = 0;
     for (int gi = 0; gi < 3; ++gi) {
-      const EncPlan p = plan_encode(dev, groups[gi], N, M);
+      const EncPlan p = plan_encode(dev, groups[gi], N, M, dtype);
       const size_t acc = align256((size_t)groups[gi] * p.pmax * M * D * sizeof(float));
       const size_t al = align256((size_t)groups[gi] * p.pmax * M * sizeof(float2));
       if (acc > max_acc) max_acc = acc;
@@ -820,11 +1129,11 @@ int flare_encode(const void* Q, int q_batched, const void* K, const void* V, flo
   hipStream_t st = (hipStream_t)stream;
   const float qs = pick_scale(scale, D) * kLog2e;
   const int BH = B * H;
-  const EncPlan p = plan_encode(dev, BH, N, M);
+  const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   float* pacc = (float*)((char*)ws + w.part_acc);
   float2* pal = (float2*)((char*)ws + w.part_al);
   if (N > 0) {
-    rc = launch_encode(dev, Q, dtype, q_batched, K, V, 0, BH, H, N, M, D, dtype, qs, pacc, pal, p, st);
+    rc = launch_encode(Q, dtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, st);
     if (rc) return rc;
   }
   return launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, st);
@@ -856,9 +1165,9 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
   int rc;
   for (int bh0 = 0; bh0 < BH; bh0 += grp) {
     const int nbh = BH - bh0 < grp ? BH - bh0 : grp;
-    const EncPlan p = plan_encode(dev, nbh, N, M);
+    const EncPlan p = plan_encode(dev, nbh, N, M, dtype);
     if (N > 0) {
-      rc = launch_encode(dev, Q, qtype, q_batched, K, V, bh0, nbh, H, N, M, D, dtype, qs, pacc, pal, p, st);
+      rc = launch_encode(Q, qtype, q_batched, K, V, bh0, H, N, M, D, dtype, qs, pacc, pal, p, st);
       if (rc) return rc;
     }
     rc = launch_merge(p, pacc, pal, bh0, nbh, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, st);
@@ -912,11 +1221,11 @@ int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void*
   const float qs = pick_scale(scale, D) * kLog2e;
   const int BH = B * H;
   // Synthesis encode over all heads, merged straight into the blended queries.
-  const EncPlan p = plan_encode(dev, BH, N, M);
+  const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   float* pacc = (float*)(wsc + w.part_acc);
   float2* pal = (float2*)(wsc + w.part_al);
   if (N > 0) {
-    rc = launch_encode(dev, Qs, dtype, 0, Ks, Vs, 0, BH, H, N, M, D, dtype, qs, pacc, pal, p, st);
+    rc = launch_encode(Qs, dtype, 0, Ks, Vs, 0, H, N, M, D, dtype, qs, pacc, pal, p, st);
     if (rc) return rc;
   }
   rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, nullptr, nullptr, Qf, dtype, gate, Qb, st);
