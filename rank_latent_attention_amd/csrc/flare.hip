@@ -176,31 +176,10 @@ __device__ inline void zero_pv(PVOp<float>& o) {
   for (int j = 0; j < 16; ++j) o.a[j] = 0.f;
 }
 
-// acc += X^T P, P being the (already exponentiated) score tile in registers,
-// and the softmax denominator of this lane's column.  With D = 16 the A
-// operand's row 16 is all ones (see ones_pv), so accumulator row 16 collects
-// the column sums inside the MFMA and lsum is unused.  bf16 with D = 32 sums
-// the bf16 weights that enter the MFMA with packed dot products; float32 with
-// D = 32 adds the weights.
-template <int D> __device__ inline f32x16 pv_accum(const PVOp<bf16>& a, const f32x16& p, f32x16 acc, float& lsum) {
-  bf16x8 b0, b1;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) { b0[s] = (bf16)p[s]; b1[s] = (bf16)p[8 + s]; }
-  if constexpr (D == 32) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-    float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b0[s], b0[s + 1]}, one, l0, false);
-      l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b1[s], b1[s + 1]}, one, l1, false);
-    }
-    lsum += l0 + l1;
-  }
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a0, b0, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a1, b1, acc, 0, 0, 0);
-  return acc;
-}
+// acc += X^T P for float32 tiles, P being the exponentiated score tile in
+// registers, plus the softmax denominator of this lane's column.  With D = 16
+// the A operand's row 16 is all ones (see ones_pv), so accumulator row 16
+// collects the column sums inside the MFMA; with D = 32 the weights are added.
 template <int D> __device__ inline f32x16 pv_accum(const PVOp<float>& a, const f32x16& p, f32x16 acc, float& lsum) {
   if constexpr (D == 32) {
     float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
@@ -213,9 +192,17 @@ template <int D> __device__ inline f32x16 pv_accum(const PVOp<float>& a, const f
   return acc;
 }
 
+// acc += X^T P for bf16 tiles from the packed weights (rows acc_row(0..7) in
+// b0, acc_row(8..15) in b1).
+__device__ inline f32x16 pv_mma(const PVOp<bf16>& a, const bf16x8& b0, const bf16x8& b1, f32x16 acc) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a0, b0, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a1, b1, acc, 0, 0, 0);
+  return acc;
+}
+
 // Softmax denominator of this lane's column, on both lanes of the pair.
-template <int D> __device__ inline float col_sum(float lsum, const f32x16& acc) {
-  if constexpr (D == 16) {  // accumulator row 16 = register 8 of the lower half
+template <typename T, int D> __device__ inline float col_sum(float lsum, const f32x16& acc) {
+  if constexpr (sizeof(T) == 4 && D == 16) {  // accumulator row 16 = register 8 of the lower half
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[8]), __float_as_uint(acc[8]), false, false);
     return __uint_as_float(r[0]);
   } else {
@@ -226,7 +213,8 @@ template <int D> __device__ inline float col_sum(float lsum, const f32x16& acc) 
 // PV A operand of a lane whose feature row is beyond D: zero, except row 16
 // (lanes 16 and 48), which is all ones when D = 16.
 __device__ inline void ones_pv(PVOp<bf16>& o, int li, int D) {
-  const bf16 v = (bf16)(D == 16 && li == 16 ? 1.f : 0.f);
+  (void)li; (void)D;  // bf16 tiles sum their weights with dot products instead
+  const bf16 v = (bf16)0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) { o.a0[s] = v; o.a1[s] = v; }
 }
@@ -236,27 +224,84 @@ __device__ inline void ones_pv(PVOp<float>& o, int li, int D) {
   for (int j = 0; j < 16; ++j) o.a[j] = v;
 }
 
-// One online-softmax step on a 32x32 score tile whose column (this lane's
-// latent in the encode, token in the decode) is the softmax row.  On entry
-// s = raw score - shift (the shift entered as -shift through the MFMA
-// accumulator `negshift`); on exit s holds the weights exp2(s).  The shift is
-// raised to the tile maximum when that exceeds it by more than kTheta, or on
-// the first non-empty tile; the running sum and accumulator are rescaled then.
-__device__ inline void online_step(f32x16& s, f32x16& negshift, bool& started, float& lsum, f32x16& acc) {
+// Maximum of the tile column held by this lane pair.
+__device__ inline float col_max(const f32x16& s) {
   float t = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
   for (int r = 3; r < 15; r += 2) t = fmaxf(fmaxf(t, s[r]), s[r + 1]);
-  t = pair_max(fmaxf(t, s[15]));
-  const bool need = (t > kTheta) || (!started && t > -INFINITY);
-  if (need) {
-    const float f = started ? fast_exp2(-t) : 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] -= t; negshift[r] -= t; acc[r] *= f; }
-    lsum *= f;
-    started = true;
-  }
+  return pair_max(fmaxf(t, s[15]));
+}
+
+// Raise the running shift of this lane's column by t: s, the shift (entered
+// through the MFMA accumulator as -shift), the accumulator and the running
+// sum follow.  The first non-empty tile sets the shift (nothing to rescale).
+__device__ inline void raise_shift(float t, f32x16& s, f32x16& negshift, bool& started, float& lsum, f32x16& acc) {
+  const float f = started ? fast_exp2(-t) : 0.f;
+  s = s - t;
+  negshift = negshift - t;
+  acc = acc * f;
+  lsum *= f;
+  started = true;
+}
+
+// float32 tiles: one online-softmax step with the exact tile maximum.  On
+// entry s = raw score - shift; on exit s holds the weights exp2(s).  The shift
+// is raised to the tile maximum when that exceeds it by more than kTheta, or
+// on the first non-empty tile.
+__device__ inline void online_step(f32x16& s, f32x16& negshift, bool& started, float& lsum, f32x16& acc) {
+  const float t = col_max(s);
+  if ((t > kTheta) || (!started && t > -INFINITY)) raise_shift(t, s, negshift, started, lsum, acc);
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r]);
+}
+
+// Weights already exponentiated, packed to bf16 (rows acc_row(0..7) in b0,
+// acc_row(8..15) in b1).  Returns this lane's partial sum of the float32
+// weights (plain adds: unlike packed dot products they issue alongside the
+// MFMAs of other waves).
+__device__ inline float pack_exps(const f32x16& p, bf16x8& b0, bf16x8& b1) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) { b0[r] = (bf16)p[r]; b1[r] = (bf16)p[8 + r]; }
+  float t[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) t[r] = p[2 * r] + p[2 * r + 1];
+  return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+}
+
+// Scores minus the running shift -> packed weights and their lane sum.
+__device__ inline float pack_weights(const f32x16& s, bf16x8& b0, bf16x8& b1) {
+  f32x16 p;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r]);
+  return pack_exps(p, b0, b1);
+}
+
+// Set rows at or beyond `from` (tile row index, acc_row order) to -inf.
+__device__ inline void mask_rows(f32x16& s, int from, int g) {
+  const int lim = from - 4 * g;  // acc_row(r, g) >= from  <=>  acc_row(r, 0) >= lim
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+}
+
+// bf16 fast path.  The running shift of a column is fixed before the loop
+// (the exact maximum of the first tile the wave sees) and never raised inside
+// it: every tile is exponentiated with it and accumulated unconditionally.
+// That is exact softmax arithmetic for any shift as long as nothing
+// overflows; weights far above 1 only appear when later scores exceed the
+// first tile's maximum by a lot, and a weight, running sum or accumulator
+// that overflows becomes Inf or NaN and stays non-finite.  So a non-finite
+// sum or accumulator at the end tells exactly when the fast result is
+// unusable; the caller then recomputes that wave's work with the exact
+// maximum of every tile.  The test works on the exponent bits, so it does not
+// depend on the compiler's NaN assumptions.
+__device__ inline bool nonfinite(float x) { return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u; }
+
+__device__ inline bool fast_failed(float lsum, const f32x16& acc) {
+  bool bad = nonfinite(lsum);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bad = bad || nonfinite(acc[r]);
+  return __builtin_amdgcn_ballot_w64(bad) != 0;
 }
 
 // ----------------------------------------------------------------------------
@@ -497,7 +542,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
       const int m = (mg * MBW + mb) * 32 + li;
-      const float ltot = col_sum<D>(lsum[mb], acc[mb]);
+      const float ltot = col_sum<float, D>(lsum[mb], acc[mb]);
       if (m < M) {
         const size_t p = (size_t)bhl * a.pmax + slot;
         float* dst = a.part_acc + (p * M + m) * D;
@@ -515,14 +560,14 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
   }
 }
 
-// Token block NB of a tile (at LDS byte addresses kb/vb + NB * 64 * D) for one
-// wave's 32 latents.  row0 is the block's first token, n_hi the end of the
+// Token block NB of a tile in buffer BO (LDS byte addresses ka / va +
+// BO + NB * 64 * D) for one wave's 32 latents.  row0 is the block's first token, n_hi the end of the
 // piece.
-template <int D, int NB>
+template <int D, int NB, int BO>
 __device__ inline void encode_block(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int row0, int n_hi,
-                                    int g, int lane, const QKOp<bf16, D>& qop, f32x16& negs, bool& started,
-                                    float& lsum, f32x16& acc) {
-  constexpr int OFF = NB * 64 * D;
+                                    int g, int lane, const QKOp<bf16, D>& qop, const f32x16& negs, float& lsum,
+                                    f32x16& acc) {
+  constexpr int OFF = BO + NB * 64 * D;
   if (row0 >= n_hi) return;
   QKOp<bf16, D> kop;
 #pragma unroll
@@ -535,27 +580,61 @@ __device__ inline void encode_block(const unsigned (&ka)[D / 16], const unsigned
     vop.a1 = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   f32x16 sc = qk_mma<D>(kop, qop, negs);
-  if (row0 + 32 > n_hi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (row0 + acc_row(r, g) >= n_hi) sc[r] = -INFINITY;
-  }
-  online_step(sc, negs, started, lsum, acc);
+  if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
+  bf16x8 b0, b1;
+  lsum += pack_weights(sc, b0, b1);
   pv_wait(vop, lane, D);
-  acc = pv_accum<D>(vop, sc, acc, lsum);
+  acc = pv_mma(vop, b0, b1, acc);
 }
 
 // The 128-token tile at t0 for one wave: token blocks ng, ng + WN, ...
 // (the per-wave offset ng * 64 * D is already folded into ka / va).
-template <int D, int WN>
+template <int D, int WN, int BO>
 __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
-                                   int lane, const QKOp<bf16, D>& qop, f32x16& negs, bool& started, float& lsum,
-                                   f32x16& acc) {
-  encode_block<D, 0>(ka, va, t0, n_hi, g, lane, qop, negs, started, lsum, acc);
-  if constexpr (WN <= 2) encode_block<D, WN>(ka, va, t0 + 32 * WN, n_hi, g, lane, qop, negs, started, lsum, acc);
+                                   int lane, const QKOp<bf16, D>& qop, const f32x16& negs, float& lsum, f32x16& acc) {
+  encode_block<D, 0, BO>(ka, va, t0, n_hi, g, lane, qop, negs, lsum, acc);
+  if constexpr (WN <= 2) encode_block<D, WN, BO>(ka, va, t0 + 32 * WN, n_hi, g, lane, qop, negs, lsum, acc);
   if constexpr (WN == 1) {
-    encode_block<D, 2>(ka, va, t0 + 64, n_hi, g, lane, qop, negs, started, lsum, acc);
-    encode_block<D, 3>(ka, va, t0 + 96, n_hi, g, lane, qop, negs, started, lsum, acc);
+    encode_block<D, 2, BO>(ka, va, t0 + 64, n_hi, g, lane, qop, negs, lsum, acc);
+    encode_block<D, 3, BO>(ka, va, t0 + 96, n_hi, g, lane, qop, negs, lsum, acc);
+  }
+}
+
+// Careful recomputation of one wave's share of a piece (the token blocks
+// t0 + 32 (ng + k WN) of every 128-token tile), straight from global memory
+// with the exact maximum of every block (online softmax with a shift raised
+// whenever the block maximum exceeds it by more than kTheta).  Used only when
+// the fast loop reported weights too large to accumulate safely.
+template <int D>
+__device__ inline void encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int lane,
+                                      const QKOp<bf16, D>& qop, f32x16& negs, float& lsum, f32x16& acc) {
+  const int li = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
+  lsum = 0.f;
+  bool started = false;
+  for (int t0 = n_lo; t0 < n_hi; t0 += kTile) {
+    for (int nb = ng; nb < kTile / 32; nb += WN) {
+      const int row0 = t0 + 32 * nb;
+      if (row0 >= n_hi) break;
+      QKOp<bf16, D> kop;
+      if (row0 + li < n_hi) load_op<D>(kop, Kh + (size_t)(row0 + li) * D, g);
+      else zero_op<D>(kop);
+      PVOp<bf16> vop;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int n = row0 + acc_row(j, g);
+        const bf16 v = (li < D && n < n_hi) ? Vh[(size_t)n * D + li] : (bf16)0.f;
+        if (j < 8) vop.a0[j] = v;
+        else vop.a1[j - 8] = v;
+      }
+      f32x16 sc = qk_mma<D>(kop, qop, negs);
+      if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
+      online_step(sc, negs, started, lsum, acc);
+      bf16x8 b0, b1;
+      lsum += pack_exps(sc, b0, b1);
+      acc = pv_mma(vop, b0, b1, acc);
+    }
   }
 }
 
@@ -564,27 +643,31 @@ __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned 
 // 128-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
 // DMA of the next tile is in flight while the current one is consumed.
 template <typename QT, int D, int NW, int WN>
-__global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
   constexpr int TE = kTile * D;  // elements per tile
   constexpr int G = NW / WN;
-  __shared__ __align__(16) bf16 k0[TE], v0[TE], k1[TE], v1[TE];
+  __shared__ __align__(16) bf16 tiles[4 * TE];  // [buffer][K, V][TE]
+  bf16* const k0 = tiles;
+  bf16* const v0 = tiles + TE;
+  bf16* const k1 = tiles + 2 * TE;
+  bf16* const v1 = tiles + 3 * TE;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, g = lane >> 5;
   const int mg = wave % G, ng = wave / G;
   const int N = a.N, M = a.M;
   const bool alias = a.v_alias;
 
-  // LDS byte addresses of this lane's operands in both buffers
+  // LDS byte addresses of this lane's operands in buffer 0; buffer 1 is a
+  // fixed distance further (folded into the read offsets)
   const TileOffs<D> to = tile_offsets<D>(lane);
   const unsigned wofs = ng * 64 * D;
-  unsigned ka0[D / 16], ka1[D / 16], va0[4], va1[4];
+  unsigned ka[D / 16], va[4];
   {
-    const unsigned bk0 = lds_addr(k0) + wofs, bk1 = lds_addr(k1) + wofs;
-    const unsigned bv0 = lds_addr(alias ? k0 : v0) + wofs, bv1 = lds_addr(alias ? k1 : v1) + wofs;
+    const unsigned bk = lds_addr(k0) + wofs, bv = lds_addr(alias ? k0 : v0) + wofs;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) { ka0[st] = bk0 + to.kq[st]; ka1[st] = bk1 + to.kq[st]; }
+    for (int st = 0; st < D / 16; ++st) ka[st] = bk + to.kq[st];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { va0[k] = bv0 + to.vq[k]; va1[k] = bv1 + to.vq[k]; }
+    for (int k = 0; k < 4; ++k) va[k] = bv + to.vq[k];
   }
 
   long long x = piece_start(blockIdx.x, a.total, a.nwg);
@@ -607,7 +690,6 @@ __global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
     float lsum = 0.f;
-    bool started = false;
 
     const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
     const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + (size_t)bh * N * D;
@@ -616,6 +698,18 @@ __global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
     if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
     wait_dma();
     __syncthreads();
+    // running shift of each latent: the exact maximum over the wave's first block
+    const int first = n_lo + 32 * ng;
+    if (first < n_hi) {
+      QKOp<bf16, D> kop;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) kop.v[st] = lds_load<bf16x8>(ka[st]);
+      f32x16 sc = qk_mma<D>(kop, qop, negs);
+      if (first + 32 > n_hi) mask_rows(sc, n_hi - first, g);
+      const float t = col_max(sc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negs[r] = -t;
+    }
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * kTile) {
       // tile t0 from buffer 0 while tile t0 + kTile streams into buffer 1
       const int tn = t0 + kTile;
@@ -623,7 +717,7 @@ __global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
         dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, WN>(ka0, va0, t0 + 32 * ng, n_hi, g, lane, qop, negs, started, lsum, acc);
+      encode_tile<D, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, negs, lsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
@@ -633,12 +727,13 @@ __global__ void __launch_bounds__(NW * 64) encode_dma_kernel(EncArgs a) {
         dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, WN>(ka1, va1, tn + 32 * ng, n_hi, g, lane, qop, negs, started, lsum, acc);
+      encode_tile<D, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, negs, lsum, acc);
       wait_dma();
       __syncthreads();
     }
+    if (fast_failed(lsum, acc)) encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, lane, qop, negs, lsum, acc);
 
-    const float ltot = col_sum<D>(lsum, acc);
+    const float ltot = col_sum<bf16, D>(lsum, acc);
     if (m < M) {
       const size_t p = (size_t)bhl * a.pmax + slot;
       float* dst = a.part_acc + (p * M + m) * D;
@@ -755,17 +850,20 @@ struct DecArgs {
 template <typename T, int D> struct DecLds {
   static constexpr int E = 16 / sizeof(T);
   static constexpr int QST = D + E;
-  __host__ __device__ static size_t zst(int MB) { return (size_t)MB * 32 + (sizeof(T) == 2 ? 8 : 4); }
+  // row stride of the transposed latents: 2 mod 4 dwords for bf16, so the 32
+  // feature rows read by a wave's 8-byte PV operand loads hit distinct banks
+  __host__ __device__ static size_t zst(int MB) { return (size_t)MB * 32 + 4; }
   static size_t bytes(int MB) { return ((size_t)MB * 32 * QST + (size_t)D * zst(MB)) * sizeof(T); }
 };
 
 template <typename T, typename QT, int D>
-__global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
   T* zt = qs + (size_t)Mp * L::QST;
+  __shared__ float zred[kThreads / 64];
   const int zst = (int)L::zst(MB);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, g = lane >> 5;
@@ -785,50 +883,119 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs a) {
     __syncthreads();
     const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
     const float* Zh = a.Z + (size_t)bh * M * D;
+    float zmax = 0.f;
     for (int i = threadIdx.x; i < Mp * D; i += kThreads) {
       const int m = i / D, d = i % D;
       const bool ok = m < M;
+      const float z = ok ? Zh[i] : 0.f;
       qs[m * L::QST + d] = from_f<T>(ok ? to_f(Qh[i]) * a.qscale : 0.f);
-      zt[d * zst + m] = from_f<T>(ok ? Zh[i] : 0.f);
+      zt[d * zst + m] = from_f<T>(z);
+      zmax = fmaxf(zmax, fabsf(z));
     }
+    // |Y accumulator| <= (sum of weights) * max |z|: a token block whose
+    // weight sum stays below zlim cannot have overflowed (see fast_failed)
+    for (int o = 32; o > 0; o >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
+    if (lane == 0) zred[wave] = zmax;
     __syncthreads();
+    zmax = fmaxf(fmaxf(zred[0], zred[1]), fmaxf(zred[2], zred[3]));
+    const float zlim = 1.329228e36f / fmaxf(zmax * 1.01f, 1.f);  // 2^120 / max|z|
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
     // wave w takes tokens t0 + [0, 32) for t0 = n_lo + 32 w, + kDecGroup, ...;
-    // the next block's key rows are fetched while the current one is decoded
+    // the next block's key rows are fetched while the current one is decoded.
+    // Lanes past the piece read its last row instead: their outputs are not
+    // stored and their scores only reach their own column.
     int t0 = n_lo + 32 * wave;
     QKOp<T, D> kop;
-    if (t0 + li < n_hi) load_op<D>(kop, Kh + (size_t)(t0 + li) * D, g);
-    else zero_op<D>(kop);
+    load_op<D>(kop, Kh + (size_t)(t0 + li < n_hi ? t0 + li : n_hi - 1) * D, g);
+    // Settle these keys before the loop: inside it the compiler would place
+    // the wait for them after the prefetch and so also wait for the prefetch.
+#pragma unroll
+    for (int st = 0; st < (int)(sizeof(kop.v) / sizeof(kop.v[0])); ++st) asm volatile("" : "+v"(kop.v[st]));
+    const f32x16 zero16 = {};
     for (; t0 < n_hi; t0 += kDecGroup) {
       QKOp<T, D> knext;
-      const int tn = t0 + kDecGroup + li;
-      if (tn < n_hi) load_op<D>(knext, Kh + (size_t)tn * D, g);
-      else zero_op<D>(knext);
+      {
+        const int tn = t0 + kDecGroup + li;
+        load_op<D>(knext, Kh + (size_t)(tn < n_hi ? tn : n_hi - 1) * D, g);
+      }
       f32x16 negs, acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
       float lsum = 0.f;
       bool started = false;
-      for (int mb = 0; mb < MB; ++mb) {
-        QKOp<T, D> qop;
-        load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
-        PVOp<T> zop;
-        if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
-        else ones_pv(zop, li, D);
-        f32x16 sc = qk_mma<D>(qop, kop, negs);
-        if (mask_tail && mb == MB - 1) {
+      if constexpr (sizeof(T) == 2) {
+        // latent block 0: the running shift of each token is its exact
+        // maximum there; the block's weights then start the accumulator
+        {
+          QKOp<T, D> qop;
+          load_op<D>(qop, qs + li * L::QST, g);
+          PVOp<T> zop;
+          if (li < D) load_pv(zop, zt + li * zst, g);
+          else ones_pv(zop, li, D);
+          f32x16 sc = qk_mma<D>(qop, kop, zero16);
+          if (mask_tail && MB == 1) mask_rows(sc, M, g);
+          const float t = col_max(sc);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (mb * 32 + acc_row(r, g) >= M) sc[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) negs[r] = -t;
+          sc = qk_mma<D>(qop, kop, negs);
+          if (mask_tail && MB == 1) mask_rows(sc, M, g);
+          bf16x8 b0, b1;
+          lsum = pack_weights(sc, b0, b1);
+          acc = pv_mma(zop, b0, b1, zero16);
         }
-        online_step(sc, negs, started, lsum, acc);
-        acc = pv_accum<D>(zop, sc, acc, lsum);
+        for (int mb = 1; mb < MB; ++mb) {
+          QKOp<T, D> qop;
+          load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+          PVOp<T> zop;
+          if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
+          else ones_pv(zop, li, D);
+          f32x16 sc = qk_mma<D>(qop, kop, negs);
+          if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
+          bf16x8 b0, b1;
+          lsum += pack_weights(sc, b0, b1);
+          acc = pv_mma(zop, b0, b1, acc);
+        }
+        if (__builtin_amdgcn_ballot_w64(lsum > zlim) != 0) {  // careful redo of this token block: exact maximum of every latent block
+          negs = zero16;
+          acc = zero16;
+          lsum = 0.f;
+          for (int mb = 0; mb < MB; ++mb) {
+            QKOp<T, D> qop;
+            load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+            PVOp<T> zop;
+            if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
+            else ones_pv(zop, li, D);
+            f32x16 sc = qk_mma<D>(qop, kop, negs);
+            if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
+            online_step(sc, negs, started, lsum, acc);
+            bf16x8 b0, b1;
+            lsum += pack_exps(sc, b0, b1);
+            acc = pv_mma(zop, b0, b1, acc);
+          }
+        }
+      } else {
+        negs = zero16;
+        acc = zero16;
+        for (int mb = 0; mb < MB; ++mb) {
+          QKOp<T, D> qop;
+          load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+          PVOp<T> zop;
+          if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
+          else ones_pv(zop, li, D);
+          f32x16 sc = qk_mma<D>(qop, kop, negs);
+          if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
+          online_step(sc, negs, started, lsum, acc);
+          acc = pv_accum<D>(zop, sc, acc, lsum);
+        }
       }
-      const int n = t0 + li;
-      const float inv = 1.f / col_sum<D>(lsum, acc);
-      if (n < n_hi) {
+      // Lanes past the piece decoded the piece's last key row, so their
+      // output is bitwise that of token n_hi - 1: they store it there too.
+      // The stores are unconditional on purpose: inside a divergent branch
+      // the compiler's wait for the prefetched keys below would also wait
+      // for them to reach memory.
+      const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
+      const float inv = __builtin_amdgcn_rcpf(col_sum<T, D>(lsum, acc));
+      {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -890,8 +1057,14 @@ struct EncPlan {
 
 // Resident waves per compute unit the encode grid is sized for, and the
 // decode's workgroups per compute unit.
-constexpr int kEncWavesPerCu = 16;
-constexpr int kDecWgPerCu = 4;
+#ifndef FLARE_ENC_WAVES_PER_CU
+#define FLARE_ENC_WAVES_PER_CU 16
+#endif
+#ifndef FLARE_DEC_WG_PER_CU
+#define FLARE_DEC_WG_PER_CU 4
+#endif
+constexpr int kEncWavesPerCu = FLARE_ENC_WAVES_PER_CU;
+constexpr int kDecWgPerCu = FLARE_DEC_WG_PER_CU;
 
 // bf16: one 32-latent block per wave, max(4, blocks) waves per workgroup.
 // f32: up to two latent blocks per wave, 4 waves per workgroup.
