@@ -52,6 +52,7 @@ constexpr int kDecGroup = 128;     // tokens per decode step of a workgroup (32 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTheta = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr float kMinSum = 0x1p-64f;  // smallest weight sum the unshifted bf16 path accepts
 
 // ----------------------------------------------------------------------------
 // Small device helpers
@@ -284,21 +285,29 @@ __device__ inline void mask_rows(f32x16& s, int from, int g) {
     if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
 }
 
-// bf16 fast path.  The running shift of a column is fixed before the loop
-// (the exact maximum of the first tile the wave sees) and never raised inside
-// it: every tile is exponentiated with it and accumulated unconditionally.
-// That is exact softmax arithmetic for any shift as long as nothing
-// overflows; weights far above 1 only appear when later scores exceed the
-// first tile's maximum by a lot, and a weight, running sum or accumulator
-// that overflows becomes Inf or NaN and stays non-finite.  So a non-finite
-// sum or accumulator at the end tells exactly when the fast result is
-// unusable; the caller then recomputes that wave's work with the exact
-// maximum of every tile.  The test works on the exponent bits, so it does not
-// depend on the compiler's NaN assumptions.
+// bf16 fast path.  Softmax is invariant to the shift, and floating point is
+// scale-invariant inside its exponent range, so the weights are taken as
+// exp2(score) with no shift at all: the score MFMA starts from an inline
+// zero, no maximum is tracked and every block is accumulated
+// unconditionally.  The result equals the shifted computation up to rounding
+// order as long as nothing leaves the range: a weight, running sum or
+// accumulator that overflows becomes Inf and stays non-finite, and a column
+// whose scores all lie far below zero shows a vanishing sum.  A sum of n
+// weights that reaches kMinSum has a largest weight of at least kMinSum / n,
+// so the weights lost to underflow (below 2^-126) are under 2^-62 n of it,
+// far below bf16 resolution for any n < 2^40.  A column sum below kMinSum or
+// a non-finite sum or accumulator sends that wave's work to a careful
+// recomputation with the exact maximum of every block.  The tests work on the exponent bits and on ordered
+// comparisons, so they do not depend on the compiler's NaN assumptions.
 __device__ inline bool nonfinite(float x) { return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u; }
 
-__device__ inline bool fast_failed(float lsum, const f32x16& acc) {
-  bool bad = nonfinite(lsum);
+// Column sum usable: finite and not vanishing.
+__device__ inline bool fast_ok(float den) { return !nonfinite(den) && den >= kMinSum; }
+
+// Encode partial usable: the column has no tokens (an empty split) or its sum
+// passes fast_ok, and the accumulator is finite.
+__device__ inline bool fast_failed(float den, bool has_tokens, const f32x16& acc) {
+  bool bad = nonfinite(den) || (has_tokens && den < kMinSum);
 #pragma unroll
   for (int r = 0; r < 16; ++r) bad = bad || nonfinite(acc[r]);
   return __builtin_amdgcn_ballot_w64(bad) != 0;
@@ -458,7 +467,9 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
   using L = EncLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, block guards derived
+  // from it become scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int G = a.G, WN = 4 / G;
   const int mg = wave % G, ng = wave / G;
@@ -560,18 +571,24 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
   }
 }
 
-// Token block NB of a tile in buffer BO (LDS byte addresses ka / va +
-// BO + NB * 64 * D) for one wave's 32 latents.  row0 is the block's first token, n_hi the end of the
-// piece.
+// Scores S^T = K Q^T of token block NB of the tile in buffer BO (LDS byte
+// addresses ka + BO + NB * 64 * D) against one wave's 32 latents, unshifted.
 template <int D, int NB, int BO>
-__device__ inline void encode_block(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int row0, int n_hi,
-                                    int g, int lane, const QKOp<bf16, D>& qop, const f32x16& negs, float& lsum,
-                                    f32x16& acc) {
+__device__ inline f32x16 enc_scores(const unsigned (&ka)[D / 16], const QKOp<bf16, D>& qop) {
   constexpr int OFF = BO + NB * 64 * D;
-  if (row0 >= n_hi) return;
   QKOp<bf16, D> kop;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) kop.v[st] = lds_load<bf16x8>(ka[st] + OFF);
+  return qk_mma<D>(kop, qop, f32x16{});
+}
+
+// Weights of those scores into the running sum and Z^T += V^T P^T.  row0 is
+// the block's first token, n_hi the end of the piece: rows at or past n_hi
+// (all of them for a block past the end) get no weight.
+template <int D, int NB, int BO>
+__device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0, int n_hi, int g, int lane,
+                                   float& lsum, f32x16& acc) {
+  constexpr int OFF = BO + NB * 64 * D;
   PVOp<bf16> vop;
   {
     const bf16x4 r0 = tr_read<OFF>(va[0]), r1 = tr_read<OFF>(va[1]);
@@ -579,24 +596,38 @@ __device__ inline void encode_block(const unsigned (&ka)[D / 16], const unsigned
     vop.a0 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     vop.a1 = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  f32x16 sc = qk_mma<D>(kop, qop, negs);
   if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
   bf16x8 b0, b1;
   lsum += pack_weights(sc, b0, b1);
+  // keep the block's sum here: sunk to the end of the tile, the adds would
+  // hold every block's weights in registers until then
+  asm volatile("" : "+v"(lsum));
   pv_wait(vop, lane, D);
   acc = pv_mma(vop, b0, b1, acc);
 }
 
 // The 128-token tile at t0 for one wave: token blocks ng, ng + WN, ...
-// (the per-wave offset ng * 64 * D is already folded into ka / va).
+// (the per-wave offset ng * 64 * D is already folded into ka / va).  The
+// scores of the next block are issued before the current block's weights
+// are exponentiated, so the MFMAs run under the exponentials.
 template <int D, int WN, int BO>
 __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
-                                   int lane, const QKOp<bf16, D>& qop, const f32x16& negs, float& lsum, f32x16& acc) {
-  encode_block<D, 0, BO>(ka, va, t0, n_hi, g, lane, qop, negs, lsum, acc);
-  if constexpr (WN <= 2) encode_block<D, WN, BO>(ka, va, t0 + 32 * WN, n_hi, g, lane, qop, negs, lsum, acc);
-  if constexpr (WN == 1) {
-    encode_block<D, 2, BO>(ka, va, t0 + 64, n_hi, g, lane, qop, negs, lsum, acc);
-    encode_block<D, 3, BO>(ka, va, t0 + 96, n_hi, g, lane, qop, negs, lsum, acc);
+                                   int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
+  f32x16 s0 = enc_scores<D, 0, BO>(ka, qop);
+  if constexpr (WN == 4) {
+    enc_consume<D, 0, BO>(va, s0, t0, n_hi, g, lane, lsum, acc);
+  } else {
+    f32x16 s1 = enc_scores<D, WN, BO>(ka, qop);
+    enc_consume<D, 0, BO>(va, s0, t0, n_hi, g, lane, lsum, acc);
+    if constexpr (WN == 2) {
+      enc_consume<D, 2, BO>(va, s1, t0 + 64, n_hi, g, lane, lsum, acc);
+    } else {
+      s0 = enc_scores<D, 2, BO>(ka, qop);
+      enc_consume<D, 1, BO>(va, s1, t0 + 32, n_hi, g, lane, lsum, acc);
+      s1 = enc_scores<D, 3, BO>(ka, qop);
+      enc_consume<D, 2, BO>(va, s0, t0 + 64, n_hi, g, lane, lsum, acc);
+      enc_consume<D, 3, BO>(va, s1, t0 + 96, n_hi, g, lane, lsum, acc);
+    }
   }
 }
 
@@ -605,10 +636,12 @@ __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned 
 // with the exact maximum of every block (online softmax with a shift raised
 // whenever the block maximum exceeds it by more than kTheta).  Used only when
 // the fast loop reported weights too large to accumulate safely.
+// Returns the final shift of this lane's latent.
 template <int D>
-__device__ inline void encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int lane,
-                                      const QKOp<bf16, D>& qop, f32x16& negs, float& lsum, f32x16& acc) {
+__device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int lane,
+                                       const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
   const int li = lane & 31, g = lane >> 5;
+  f32x16 negs;
 #pragma unroll
   for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
   lsum = 0.f;
@@ -636,6 +669,7 @@ __device__ inline void encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, 
       acc = pv_mma(vop, b0, b1, acc);
     }
   }
+  return -negs[0];
 }
 
 // bf16 encode: NW waves in WN token lanes of G = NW / WN latent groups; wave w
@@ -651,7 +685,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
   bf16* const v0 = tiles + TE;
   bf16* const k1 = tiles + 2 * TE;
   bf16* const v1 = tiles + 3 * TE;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, block guards derived
+  // from it become scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int mg = wave % G, ng = wave / G;
   const int N = a.N, M = a.M;
@@ -686,9 +722,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     QKOp<bf16, D> qop;
     if (m < M) load_op_scaled<D>(qop, Qh + (size_t)m * D, g, a.qscale);
     else zero_op<D>(qop);
-    f32x16 negs, acc;
+    f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     float lsum = 0.f;
 
     const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
@@ -698,18 +734,6 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
     wait_dma();
     __syncthreads();
-    // running shift of each latent: the exact maximum over the wave's first block
-    const int first = n_lo + 32 * ng;
-    if (first < n_hi) {
-      QKOp<bf16, D> kop;
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) kop.v[st] = lds_load<bf16x8>(ka[st]);
-      f32x16 sc = qk_mma<D>(kop, qop, negs);
-      if (first + 32 > n_hi) mask_rows(sc, n_hi - first, g);
-      const float t = col_max(sc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) negs[r] = -t;
-    }
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * kTile) {
       // tile t0 from buffer 0 while tile t0 + kTile streams into buffer 1
       const int tn = t0 + kTile;
@@ -717,7 +741,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, negs, lsum, acc);
+      encode_tile<D, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, lsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
@@ -727,13 +751,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, negs, lsum, acc);
+      encode_tile<D, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, lsum, acc);
       wait_dma();
       __syncthreads();
     }
-    if (fast_failed(lsum, acc)) encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, lane, qop, negs, lsum, acc);
-
-    const float ltot = col_sum<bf16, D>(lsum, acc);
+    // unshifted partial (see fast_ok), or the careful recomputation's
+    float ltot = pair_sum(lsum), shift = 0.f;
+    if (fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
+      shift = encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, lane, qop, lsum, acc);
+      ltot = pair_sum(lsum);
+    }
     if (m < M) {
       const size_t p = (size_t)bhl * a.pmax + slot;
       float* dst = a.part_acc + (p * M + m) * D;
@@ -744,7 +771,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
           *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g) = v;
         }
       }
-      if (g == 0) a.part_al[p * M + m] = make_float2(-negs[0], ltot);
+      if (g == 0) a.part_al[p * M + m] = make_float2(shift, ltot);
     }
     x = hb + n_hi;
   }
@@ -856,7 +883,9 @@ template <typename T, int D> struct DecLds {
   static size_t bytes(int MB) { return ((size_t)MB * 32 * QST + (size_t)D * zst(MB)) * sizeof(T); }
 };
 
-template <typename T, typename QT, int D>
+// TAIL: M is not a multiple of 32, so the last latent block has rows past M
+// that must not receive weight (compiled out for whole blocks).
+template <typename T, typename QT, int D, bool TAIL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -865,9 +894,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   T* zt = qs + (size_t)Mp * L::QST;
   __shared__ float zred[kThreads / 64];
   const int zst = (int)L::zst(MB);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, block guards derived
+  // from it become scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
-  const bool mask_tail = (M & 31) != 0;
+  constexpr bool mask_tail = TAIL;
+  __builtin_assume(MB >= 1);
 
   long long x = piece_start(blockIdx.x, a.total, a.nwg);
   const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
@@ -920,61 +952,71 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         const int tn = t0 + kDecGroup + li;
         load_op<D>(knext, Kh + (size_t)(tn < n_hi ? tn : n_hi - 1) * D, g);
       }
-      f32x16 negs, acc;
-      float lsum = 0.f;
-      bool started = false;
+      f32x16 acc;
+      float lsum = 0.f, den;
       if constexpr (sizeof(T) == 2) {
-        // latent block 0: the running shift of each token is its exact
-        // maximum there; the block's weights then start the accumulator
-        {
-          QKOp<T, D> qop;
-          load_op<D>(qop, qs + li * L::QST, g);
-          PVOp<T> zop;
-          if (li < D) load_pv(zop, zt + li * zst, g);
-          else ones_pv(zop, li, D);
-          f32x16 sc = qk_mma<D>(qop, kop, zero16);
-          if (mask_tail && MB == 1) mask_rows(sc, M, g);
-          const float t = col_max(sc);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) negs[r] = -t;
-          sc = qk_mma<D>(qop, kop, negs);
-          if (mask_tail && MB == 1) mask_rows(sc, M, g);
-          bf16x8 b0, b1;
-          lsum = pack_weights(sc, b0, b1);
-          acc = pv_mma(zop, b0, b1, zero16);
-        }
-        for (int mb = 1; mb < MB; ++mb) {
+        // Fast path: unshifted weights exp2(score) (see fast_ok).  The
+        // scores of latent block mb + 1 go to the MFMA unit before the
+        // weights of block mb are exponentiated, so within the wave the
+        // matrix products run under the exponentials.
+        auto scores = [&](int mb) {
           QKOp<T, D> qop;
           load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+          return qk_mma<D>(qop, kop, zero16);
+        };
+        auto consume = [&](f32x16 sc, int mb, const f32x16& from) {
           PVOp<T> zop;
           if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
           else ones_pv(zop, li, D);
-          f32x16 sc = qk_mma<D>(qop, kop, negs);
           if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
           bf16x8 b0, b1;
           lsum += pack_weights(sc, b0, b1);
-          acc = pv_mma(zop, b0, b1, acc);
+          acc = pv_mma(zop, b0, b1, from);
+        };
+        f32x16 sa = scores(0), sb;
+        if (MB > 1) sb = scores(1);
+        consume(sa, 0, zero16);
+        int mb = 1;
+        for (; mb + 2 < MB; mb += 2) {  // block mb is in sb
+          sa = scores(mb + 1);
+          consume(sb, mb, acc);
+          sb = scores(mb + 2);
+          consume(sa, mb + 1, acc);
         }
-        if (__builtin_amdgcn_ballot_w64(lsum > zlim) != 0) {  // careful redo of this token block: exact maximum of every latent block
-          negs = zero16;
+        if (mb + 1 < MB) {
+          sa = scores(mb + 1);
+          consume(sb, mb, acc);
+          consume(sa, mb + 1, acc);
+        } else if (mb < MB) {
+          consume(sb, mb, acc);
+        }
+        den = pair_sum(lsum);
+        // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim
+        if (__builtin_amdgcn_ballot_w64(!fast_ok(den) || den > zlim) != 0) {
+          // careful redo of this token block: exact maximum of every latent block
+          f32x16 negs = zero16;
+          bool started = false;
           acc = zero16;
           lsum = 0.f;
-          for (int mb = 0; mb < MB; ++mb) {
+          int mc = 0;
+          do {
             QKOp<T, D> qop;
-            load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+            load_op<D>(qop, qs + (mc * 32 + li) * L::QST, g);
             PVOp<T> zop;
-            if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
+            if (li < D) load_pv(zop, zt + li * zst + mc * 32, g);
             else ones_pv(zop, li, D);
             f32x16 sc = qk_mma<D>(qop, kop, negs);
-            if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
+            if (mask_tail && mc == MB - 1) mask_rows(sc, M - mc * 32, g);
             online_step(sc, negs, started, lsum, acc);
             bf16x8 b0, b1;
             lsum += pack_exps(sc, b0, b1);
             acc = pv_mma(zop, b0, b1, acc);
-          }
+          } while (++mc < MB);
+          den = pair_sum(lsum);
         }
       } else {
-        negs = zero16;
+        f32x16 negs = zero16;
+        bool started = false;
         acc = zero16;
         for (int mb = 0; mb < MB; ++mb) {
           QKOp<T, D> qop;
@@ -987,6 +1029,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           online_step(sc, negs, started, lsum, acc);
           acc = pv_accum<D>(zop, sc, acc, lsum);
         }
+        den = col_sum<T, D>(lsum, acc);
       }
       // Lanes past the piece decoded the piece's last key row, so their
       // output is bitwise that of token n_hi - 1: they store it there too.
@@ -994,7 +1037,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       // the compiler's wait for the prefetched keys below would also wait
       // for them to reach memory.
       const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
-      const float inv = __builtin_amdgcn_rcpf(col_sum<T, D>(lsum, acc));
+      const float inv = __builtin_amdgcn_rcpf(den);
       {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
@@ -1186,15 +1229,20 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename T, typename QT, int D>
-int launch_decode_t(const DecArgs& a, size_t lds, hipStream_t st) {
+template <typename T, typename QT, int D, bool TAIL>
+int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
   if (lds > 65536) {
-    if (hipFuncSetAttribute((const void*)decode_kernel<T, QT, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)decode_kernel<T, QT, D, TAIL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((decode_kernel<T, QT, D>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL>), dim3(a.nwg), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+template <typename T, typename QT, int D>
+int launch_decode_t(const DecArgs& a, size_t lds, hipStream_t st) {
+  return (a.M & 31) ? launch_decode_k<T, QT, D, true>(a, lds, st) : launch_decode_k<T, QT, D, false>(a, lds, st);
 }
 
 size_t decode_lds(int dtype, int D, int M) {
