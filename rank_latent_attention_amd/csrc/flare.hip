@@ -796,59 +796,74 @@ struct MergeArgs {
   int N, M, D, H, WN, nwg, pmax, bh0, nbh;
 };
 
-// One workgroup per (head, latent); thread (pg, d) folds the splits
-// p = pg, pg + PG, ... into a local (A, den, num) with the same rule, and the
-// PG partial results are then combined in ascending pg order.
+// Running (A, den, num) of a set of splits: max shift, and sum of l_p and of
+// U_p scaled to 2^A.  Empty sets have A = -inf, den = num = 0.
+struct MergeState {
+  float A, den, num;
+};
+
+__device__ inline MergeState merge_fold(MergeState s, float a, float l, float u) {
+  if (l > 0.f) {
+    if (a > s.A) {
+      const float f = fast_exp2(s.A - a);  // 0 while A = -inf
+      s.den *= f;
+      s.num *= f;
+      s.A = a;
+    }
+    const float w = fast_exp2(a - s.A);
+    s.den += w * l;
+    s.num += w * u;
+  }
+  return s;
+}
+
+// Symmetric in its arguments (max and + commute exactly), so both lanes of a
+// butterfly pair obtain bitwise the same state.
+__device__ inline MergeState merge_pair(MergeState x, MergeState y) {
+  const float A = fmaxf(x.A, y.A);
+  if (!(A > -INFINITY)) return x;
+  const float fx = x.A > -INFINITY ? fast_exp2(x.A - A) : 0.f;
+  const float fy = y.A > -INFINITY ? fast_exp2(y.A - A) : 0.f;
+  return MergeState{A, x.den * fx + y.den * fy, x.num * fx + y.num * fy};
+}
+
+// One wave per (head, latent): lane (pg, d) folds the splits p = pg, pg + PGW,
+// ... (PGW = 64 / D lane groups) in ascending order, and the PGW group states
+// are combined by a fixed xor butterfly over the group bits of the lane.
 template <typename QT>
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
-  __shared__ float sA[kThreads], sDen[kThreads], sNum[kThreads];
-  const int D = a.D, PG = kThreads / D;
-  const int pg = threadIdx.x / D, d = threadIdx.x % D;
-  const int m = blockIdx.x % a.M;
-  const int bhl = blockIdx.x / a.M;
+  const int lane = threadIdx.x & 63;
+  const long long pair = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (pair >= (long long)a.nbh * a.M) return;  // the whole wave
+  const int D = a.D, PGW = 64 / D;
+  const int pg = lane / D, d = lane % D;
+  const int m = (int)(pair % a.M);
+  const int bhl = (int)(pair / a.M);
   const int bh = a.bh0 + bhl;
-  float A = -INFINITY, den = 0.f, num = 0.f;
+  MergeState st{-INFINITY, 0.f, 0.f};
   if (a.N > 0) {
     const long long hb = (long long)bhl * a.N;
     const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
 #pragma unroll 4
-    for (int p = pg; p < cnt; p += PG) {
+    for (int p = pg; p < cnt; p += PGW) {
       const float2 v = a.part_al[(base + p) * a.M + m];
       const float u = a.part_acc[((base + p) * a.M + m) * D + d];
-      if (v.y > 0.f) {
-        if (v.x > A) {
-          const float f = fast_exp2(A - v.x);  // 0 while A = -inf
-          den *= f;
-          num *= f;
-          A = v.x;
-        }
-        const float w = fast_exp2(v.x - A);
-        den += w * v.y;
-        num += w * u;
-      }
+      st = merge_fold(st, v.x, v.y, u);
     }
   }
-  sA[threadIdx.x] = A;
-  sDen[threadIdx.x] = den;
-  sNum[threadIdx.x] = num;
-  __syncthreads();
+  for (int o = D; o < 64; o <<= 1) {
+    MergeState t;
+    t.A = __shfl_xor(st.A, o);
+    t.den = __shfl_xor(st.den, o);
+    t.num = __shfl_xor(st.num, o);
+    st = merge_pair(st, t);
+  }
   if (pg != 0) return;
-  float At = -INFINITY;
-  for (int t = 0; t < PG; ++t) At = fmaxf(At, sA[t * D + d]);
   float z = 0.f, lse = -INFINITY;
-  if (At > -INFINITY) {
-    float dt = 0.f, nt = 0.f;
-    for (int t = 0; t < PG; ++t) {
-      const float At_t = sA[t * D + d];
-      if (At_t > -INFINITY) {
-        const float w = fast_exp2(At_t - At);
-        dt += w * sDen[t * D + d];
-        nt += w * sNum[t * D + d];
-      }
-    }
-    z = nt / dt;
-    lse = kLn2 * (At + __builtin_amdgcn_logf(dt));
+  if (st.A > -INFINITY) {
+    z = st.num / st.den;
+    lse = kLn2 * (st.A + __builtin_amdgcn_logf(st.den));
   }
   const size_t o = ((size_t)bh * a.M + m) * D + d;
   if (a.Qout) {
@@ -1223,7 +1238,7 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   a.Z = Z; a.L = L; a.Qf = Qf; a.gate = gate; a.Qout = Qout;
   a.total = p.total;
   a.N = N; a.M = M; a.D = D; a.H = H; a.WN = p.WN; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0; a.nbh = nbh;
-  const dim3 grid((unsigned)((long long)nbh * M));
+  const dim3 grid((unsigned)cdiv((long long)nbh * M, kThreads / 64));
   if (qftype == FLARE_BF16) hipLaunchKernelGGL((merge_kernel<bf16>), grid, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((merge_kernel<float>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
