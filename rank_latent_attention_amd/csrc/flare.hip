@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include "flare.h"
+#include "pieces.h"
 
 namespace {
 
@@ -75,19 +76,6 @@ __device__ inline float pair_sum(float x) {
 // Row of the 32x32 MFMA accumulator held by register r of a lane in half g
 // (the column is lane % 32): rows come in chunks of 4 consecutive rows.
 __device__ inline int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
-
-// Flattened (head, token) range of workgroup i when `total` tokens are cut
-// into `nwg` contiguous pieces.
-__host__ __device__ inline long long piece_start(long long i, long long total, int nwg) {
-  return i * total / nwg;
-}
-__host__ __device__ inline int piece_of(long long x, long long total, int nwg) {
-  long long i = x * nwg / total;
-  if (i >= nwg) i = nwg - 1;
-  while (i + 1 < nwg && piece_start(i + 1, total, nwg) <= x) ++i;
-  while (i > 0 && piece_start(i, total, nwg) > x) --i;
-  return (int)i;
-}
 
 // ----------------------------------------------------------------------------
 // MFMA operands.  A 32x32 product contracts over the feature axis d (QK) or
@@ -833,12 +821,13 @@ __device__ inline MergeState merge_pair(MergeState x, MergeState y) {
 template <typename QT>
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
-  const long long pair = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (pair >= (long long)a.nbh * a.M) return;  // the whole wave
+  // B H M < 2^31 (checked on the host): 32-bit index arithmetic
+  const unsigned pair = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (pair >= (unsigned)a.nbh * (unsigned)a.M) return;  // the whole wave
   const int D = a.D, PGW = 64 / D;
   const int pg = lane / D, d = lane % D;
-  const int m = (int)(pair % a.M);
-  const int bhl = (int)(pair / a.M);
+  const int m = (int)(pair % (unsigned)a.M);
+  const int bhl = (int)(pair / (unsigned)a.M);
   const int bh = a.bh0 + bhl;
   MergeState st{-INFINITY, 0.f, 0.f};
   if (a.N > 0) {
