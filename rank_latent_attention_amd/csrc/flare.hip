@@ -834,11 +834,22 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
     const long long hb = (long long)bhl * a.N;
     const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
-#pragma unroll 4
-    for (int p = pg; p < cnt; p += PGW) {
-      const float2 v = a.part_al[(base + p) * a.M + m];
-      const float u = a.part_acc[((base + p) * a.M + m) * D + d];
-      st = merge_fold(st, v.x, v.y, u);
+    // batches of four splits: all loads are issued before any is folded
+    // (slots past cnt re-read split pg and count as empty), so a batch costs
+    // one memory round trip instead of two dependent ones per split
+    for (int p0 = pg; p0 < cnt; p0 += 4 * PGW) {
+      float2 v[4];
+      float u[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = p0 + j * PGW;
+        const size_t i = (base + (p < cnt ? p : pg)) * a.M + m;
+        v[j] = a.part_al[i];
+        u[j] = a.part_acc[i * D + d];
+      }
+      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st = merge_fold(st, v[j].x, p0 + j * PGW < cnt ? v[j].y : 0.f, u[j]);
     }
   }
   for (int o = D; o < 64; o <<= 1) {
