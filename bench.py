@@ -57,18 +57,23 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(w, target_s: float = 15.0):
-    """The fp64 oracle on a bounded sample: all N tokens of the first k heads,
+    """The fp64 oracle of the same routing forward (FLARE, or FLARE++ with its
+    synthesis step) on a bounded sample: all N tokens of the first k heads,
     k chosen from a one-head timing so the sample takes about target_s."""
     import oracle
     oracle.build(force=False)
     cores = oracle.threads()
 
+    def heads(x, k):
+        return np.ascontiguousarray(x[:, :k])
+
     def run(k):
-        Q = w.Q[:k]
-        K = np.ascontiguousarray(w.K[:, :k])
-        V = np.ascontiguousarray(w.V[:, :k])
         t0 = time.perf_counter()
-        oracle.flare_forward(Q, K, V)
+        if w.pp:
+            oracle.flare_pp_forward(w.Qs[:k], heads(w.Ks, k), heads(w.Vs, k), w.Qf[:k], w.gate[:k],
+                                    heads(w.K, k), heads(w.V, k))
+        else:
+            oracle.flare_forward(w.Q[:k], heads(w.K, k), heads(w.V, k))
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -76,8 +81,9 @@ def cpu_baseline(w, target_s: float = 15.0):
     t = run(k) if k > 1 else t1
     # a token of the whole routing pass needs all H heads
     value = w.B * w.N * k / (t * w.H)
+    what = "FLARE++ forward (synthesis encode, blend, encode + decode)" if w.pp else "FLARE forward (encode + decode)"
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle FLARE forward (encode + decode) on heads 0..{k - 1} of {w.H}, all {w.N} tokens, "
+            "sample": f"fp64 oracle {what} on heads 0..{k - 1} of {w.H}, all {w.N} tokens, "
                       f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
 
 
