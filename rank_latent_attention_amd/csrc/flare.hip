@@ -48,7 +48,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;      // 4 waves per workgroup
-constexpr int kTile = 128;         // tokens per encode LDS tile (4 blocks of 32)
+constexpr int kTile = 128;         // tokens per float32 encode LDS tile (4 blocks of 32)
+#ifndef FLARE_DMA_TILE
+#define FLARE_DMA_TILE 128
+#endif
+// Tokens per bf16 encode LDS tile (DMA-filled, double-buffered) for a
+// workgroup of NW waves: 32 per wave up to FLARE_DMA_TILE, so two tiles of K
+// and V stay within 64 KB and four waves per SIMD still fit.
+template <int NW> constexpr int dma_rows() { return FLARE_DMA_TILE < 32 * NW ? FLARE_DMA_TILE : 32 * NW; }
 constexpr int kDecGroup = 128;     // tokens per decode step of a workgroup (32 per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -320,13 +327,13 @@ template <int D> __device__ inline int chunk_pos(int n, int c) {
 // Element offset of (row n, feature d) in a swizzled tile.
 template <int D> __device__ inline int tile_off(int n, int d) { return chunk_pos<D>(n, d >> 3) * 8 + (d & 7); }
 
-// Issue the DMA of rows [t0, t0 + kTile) of a [*, D] bf16 matrix into a
+// Issue the DMA of rows [t0, t0 + dma_rows<NW>()) of a [*, D] bf16 matrix into a
 // swizzled tile.  Rows at or beyond n_hi repeat row n_hi - 1 (they are masked
 // out of the softmax by the caller), so no read leaves the matrix.
 template <int D, int NW>
 __device__ inline void dma_tile(bf16* tile, const bf16* src, int t0, int n_hi, int wave, int lane) {
   constexpr int CPR = D / 8;
-  constexpr int INSTR = kTile * CPR / 64;  // 64 chunks (1 KB) per wave instruction
+  constexpr int INSTR = dma_rows<NW>() * CPR / 64;  // 64 chunks (1 KB) per wave instruction
 #pragma unroll
   for (int i = wave; i < INSTR; i += NW) {
     const int P = i * 64 + lane;
@@ -594,48 +601,52 @@ __device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0,
   acc = pv_mma(vop, b0, b1, acc);
 }
 
-// The 128-token tile at t0 for one wave: token blocks ng, ng + WN, ...
-// (the per-wave offset ng * 64 * D is already folded into ka / va).  The
-// scores of the next block are issued before the current block's weights
-// are exponentiated, so the MFMAs run under the exponentials.
-template <int D, int WN, int BO>
-__device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
-                                   int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
-  f32x16 s0 = enc_scores<D, 0, BO>(ka, qop);
-  if constexpr (WN == 4) {
-    enc_consume<D, 0, BO>(va, s0, t0, n_hi, g, lane, lsum, acc);
+// Blocks J, J + 1, ... of one wave's share of a tile (block J is token block
+// J WN of the tile, its scores already issued in `cur`).  The scores of the
+// next block are issued before the current block's weights are
+// exponentiated, so the MFMAs run under the exponentials.  Blocks past the
+// end of the piece are computed and masked to zero weight (their rows repeat
+// the piece's last row): a branch per block costs more than the rare waste.
+template <int D, int WN, int BO, int J, int NBLK>
+__device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
+                                    int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc, const f32x16& cur) {
+  if constexpr (J + 1 < NBLK) {
+    const f32x16 nxt = enc_scores<D, (J + 1) * WN, BO>(ka, qop);
+    enc_consume<D, J * WN, BO>(va, cur, t0 + 32 * J * WN, n_hi, g, lane, lsum, acc);
+    encode_chain<D, WN, BO, J + 1, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, nxt);
   } else {
-    f32x16 s1 = enc_scores<D, WN, BO>(ka, qop);
-    enc_consume<D, 0, BO>(va, s0, t0, n_hi, g, lane, lsum, acc);
-    if constexpr (WN == 2) {
-      enc_consume<D, 2, BO>(va, s1, t0 + 64, n_hi, g, lane, lsum, acc);
-    } else {
-      s0 = enc_scores<D, 2, BO>(ka, qop);
-      enc_consume<D, 1, BO>(va, s1, t0 + 32, n_hi, g, lane, lsum, acc);
-      s1 = enc_scores<D, 3, BO>(ka, qop);
-      enc_consume<D, 2, BO>(va, s0, t0 + 64, n_hi, g, lane, lsum, acc);
-      enc_consume<D, 3, BO>(va, s1, t0 + 96, n_hi, g, lane, lsum, acc);
-    }
+    enc_consume<D, J * WN, BO>(va, cur, t0 + 32 * J * WN, n_hi, g, lane, lsum, acc);
   }
 }
 
+// The dma_rows<NW>()-token tile at t0 for one wave: token blocks ng, ng + WN,
+// ... (the per-wave offset ng * 64 * D is already folded into ka / va, and t0
+// here is the wave's first row).
+template <int D, int NW, int WN, int BO>
+__device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
+                                   int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
+  if (t0 >= n_hi) return;
+  constexpr int NBLK = dma_rows<NW>() / 32 / WN;
+  encode_chain<D, WN, BO, 0, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, enc_scores<D, 0, BO>(ka, qop));
+}
+
 // Careful recomputation of one wave's share of a piece (the token blocks
-// t0 + 32 (ng + k WN) of every 128-token tile), straight from global memory
+// t0 + 32 (ng + k WN) of every `rows`-token tile), straight from global memory
 // with the exact maximum of every block (online softmax with a shift raised
 // whenever the block maximum exceeds it by more than kTheta).  Used only when
 // the fast loop reported weights too large to accumulate safely.
 // Returns the final shift of this lane's latent.
 template <int D>
-__device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int lane,
-                                       const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
+__device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int rows,
+                                       int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
   const int li = lane & 31, g = lane >> 5;
   f32x16 negs;
 #pragma unroll
   for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
   lsum = 0.f;
   bool started = false;
-  for (int t0 = n_lo; t0 < n_hi; t0 += kTile) {
-    for (int nb = ng; nb < kTile / 32; nb += WN) {
+  for (int t0 = n_lo; t0 < n_hi; t0 += rows) {
+    for (int nb = ng; nb < rows / 32; nb += WN) {
       const int row0 = t0 + 32 * nb;
       if (row0 >= n_hi) break;
       QKOp<bf16, D> kop;
@@ -662,11 +673,12 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo,
 
 // bf16 encode: NW waves in WN token lanes of G = NW / WN latent groups; wave w
 // owns latent block w % G (32 latents) and token blocks w / G + k WN of every
-// 128-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
+// ROWS-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
 // DMA of the next tile is in flight while the current one is consumed.
 template <typename QT, int D, int NW, int WN>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
-  constexpr int TE = kTile * D;  // elements per tile
+  constexpr int ROWS = dma_rows<NW>();
+  constexpr int TE = ROWS * D;  // elements per tile
   constexpr int G = NW / WN;
   __shared__ __align__(16) bf16 tiles[4 * TE];  // [buffer][K, V][TE]
   bf16* const k0 = tiles;
@@ -722,31 +734,31 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
     wait_dma();
     __syncthreads();
-    for (int t0 = n_lo; t0 < n_hi; t0 += 2 * kTile) {
-      // tile t0 from buffer 0 while tile t0 + kTile streams into buffer 1
-      const int tn = t0 + kTile;
+    for (int t0 = n_lo; t0 < n_hi; t0 += 2 * ROWS) {
+      // tile t0 from buffer 0 while tile t0 + ROWS streams into buffer 1
+      const int tn = t0 + ROWS;
       if (tn < n_hi) {
         dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, lsum, acc);
+      encode_tile<D, NW, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, lsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
-      // tile tn from buffer 1 while tn + kTile streams into buffer 0
-      const int tn2 = tn + kTile;
+      // tile tn from buffer 1 while tn + ROWS streams into buffer 0
+      const int tn2 = tn + ROWS;
       if (tn2 < n_hi) {
         dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, lsum, acc);
+      encode_tile<D, NW, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, lsum, acc);
       wait_dma();
       __syncthreads();
     }
     // unshifted partial (see fast_ok), or the careful recomputation's
     float ltot = pair_sum(lsum), shift = 0.f;
     if (fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
-      shift = encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, lane, qop, lsum, acc);
+      shift = encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, ROWS, lane, qop, lsum, acc);
       ltot = pair_sum(lsum);
     }
     if (m < M) {
