@@ -827,6 +827,11 @@ __device__ inline MergeState merge_pair(MergeState x, MergeState y) {
   return MergeState{A, x.den * fx + y.den * fy, x.num * fx + y.num * fy};
 }
 
+#ifndef FLARE_MERGE_BATCH
+#define FLARE_MERGE_BATCH 8
+#endif
+constexpr int kMergeBatch = FLARE_MERGE_BATCH;
+
 // One wave per (head, latent): lane (pg, d) folds the splits p = pg, pg + PGW,
 // ... (PGW = 64 / D lane groups) in ascending order, and the PGW group states
 // are combined by a fixed xor butterfly over the group bits of the lane.
@@ -846,22 +851,23 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
     const long long hb = (long long)bhl * a.N;
     const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
-    // batches of four splits: all loads are issued before any is folded
-    // (slots past cnt re-read split pg and count as empty), so a batch costs
-    // one memory round trip instead of two dependent ones per split
-    for (int p0 = pg; p0 < cnt; p0 += 4 * PGW) {
-      float2 v[4];
-      float u[4];
+    // batches of kMergeBatch splits: all loads are issued before any is
+    // folded (slots past cnt re-read split pg and count as empty), so a batch
+    // costs one memory round trip instead of two dependent ones per split
+    for (int p0 = pg; p0 < cnt; p0 += kMergeBatch * PGW) {
+      float2 v[kMergeBatch];
+      float u[kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kMergeBatch; ++j) {
         const int p = p0 + j * PGW;
         const size_t i = (base + (p < cnt ? p : pg)) * a.M + m;
         v[j] = a.part_al[i];
         u[j] = a.part_acc[i * D + d];
       }
-      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st = merge_fold(st, v[j].x, p0 + j * PGW < cnt ? v[j].y : 0.f, u[j]);
+      for (int j = 0; j < kMergeBatch; ++j) asm volatile("" ::"v"(v[j]), "v"(u[j]));
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) st = merge_fold(st, v[j].x, p0 + j * PGW < cnt ? v[j].y : 0.f, u[j]);
     }
   }
   for (int o = D; o < 64; o <<= 1) {
@@ -938,18 +944,59 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int bh = a.bh0 + bhl;
     const int h = bh % a.H;
 
-    // Stage this head's scaled queries (rows = latents) and transposed latents.
+    // Stage this head's scaled queries (rows = latents) and transposed
+    // latents.  Every 16-byte chunk of the head is loaded before the first
+    // one is used, so staging costs one memory round trip rather than one per
+    // element; rows M .. Mp-1 are zero.
     __syncthreads();
     const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
     const float* Zh = a.Z + (size_t)bh * M * D;
     float zmax = 0.f;
-    for (int i = threadIdx.x; i < Mp * D; i += kThreads) {
-      const int m = i / D, d = i % D;
-      const bool ok = m < M;
-      const float z = ok ? Zh[i] : 0.f;
-      qs[m * L::QST + d] = from_f<T>(ok ? to_f(Qh[i]) * a.qscale : 0.f);
-      zt[d * zst + m] = from_f<T>(z);
-      zmax = fmaxf(zmax, fabsf(z));
+    {
+      constexpr int QE = 16 / sizeof(QT);          // elements per 16-byte chunk
+      constexpr int QJ = 256 * D / QE / kThreads;  // chunks per thread at M = 256
+      constexpr int ZJ = 256 * D / 4 / kThreads;
+      const int nq = M * D / QE, nz = M * D / 4;   // chunks of real rows
+      const int pq = Mp * D / QE, pz = Mp * D / 4; // chunks including the zero rows
+      // chunk offsets from an index opaque to the compiler, so they are
+      // recomputed here rather than hoisted out of the head loop and spilled
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      uint4 qv[QJ], zv[ZJ];
+#pragma unroll
+      for (int j = 0; j < QJ; ++j) {
+        const int c = tid + j * kThreads;
+        qv[j] = reinterpret_cast<const uint4*>(Qh)[c < nq ? c : 0];
+      }
+#pragma unroll
+      for (int j = 0; j < ZJ; ++j) {
+        const int c = tid + j * kThreads;
+        zv[j] = reinterpret_cast<const uint4*>(Zh)[c < nz ? c : 0];
+      }
+#pragma unroll
+      for (int j = 0; j < QJ; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < pq) {
+          const int m = c * QE / D, d0 = c * QE % D;
+          const QT* src = reinterpret_cast<const QT*>(&qv[j]);
+#pragma unroll
+          for (int i = 0; i < QE; ++i) qs[m * L::QST + d0 + i] = from_f<T>(c < nq ? to_f(src[i]) * a.qscale : 0.f);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < ZJ; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < pz) {
+          const int m = c * 4 / D, d0 = c * 4 % D;
+          const float* src = reinterpret_cast<const float*>(&zv[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float z = c < nz ? src[i] : 0.f;
+            zt[(d0 + i) * zst + m] = from_f<T>(z);
+            zmax = fmaxf(zmax, fabsf(z));
+          }
+        }
+      }
     }
     // |Y accumulator| <= (sum of weights) * max |z|: a token block whose
     // weight sum stays below zlim cannot have overflowed (see fast_failed)
