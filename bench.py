@@ -87,6 +87,66 @@ def cpu_baseline(w, target_s: float = 15.0):
                       f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
 
 
+def time_configs(names: str) -> None:
+    """Per-workload forward timing (inputs resident, events on the library's
+    stream): one JSON line per workload, not the bench line."""
+    import torch
+    import rank_latent_attention_amd as flare
+    from rank_latent_attention_amd.inputs import CONFIGS
+    F = flare.flare
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    todo = list(CONFIGS) if names == "all" else names.split(",")
+    for name in todo:
+        w = CONFIGS[name]()
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        code = F.BF16 if w.dtype == "bf16" else F.F32
+
+        def up(x):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+
+        B, H, N, M, D = w.B, w.H, w.N, w.M, w.D
+        K, V = up(w.K), up(w.V)
+        Y = torch.empty_like(K)
+        Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+        L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+        if w.pp:
+            Qs, Ks, Qf = up(w.Qs), up(w.Ks), up(w.Qf)
+            Vs = Ks if w.shared_vs else up(w.Vs)
+            gate = torch.from_numpy(w.gate).to(dev)
+            Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+            ws = flare.workspace(F.OP_PP_FORWARD, B, H, N, M, D, code, dev)
+
+            def step():
+                F.flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, Y=Y, Q_out=Qo, Z=Z, L=L, ws=ws)
+            flops = 12.0 * B * H * N * M * D
+        else:
+            Q = up(w.Q)
+            ws = flare.workspace(F.OP_FORWARD, B, H, N, M, D, code, dev)
+
+            def step():
+                F.flare_forward(Q, K, V, Y=Y, Z=Z, L=L, ws=ws)
+            flops = 8.0 * B * H * N * M * D
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n = 50
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            ev[2 * i].record(stream)
+            step()
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))
+        med = t[n // 2]
+        print(json.dumps({"workload": w.name, "B": B, "H": H, "N": N, "M": M, "D": D, "dtype": w.dtype,
+                          "flare_pp": bool(w.pp), "us_median": round(med, 1), "us_min": round(t[0], 1),
+                          "us_max": round(t[-1], 1), "tokens_per_s": B * N / (med * 1e-6),
+                          "tflops": round(flops / (med * 1e-6) / 1e12, 1)}), flush=True)
+        del K, V, Y, Z, L, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +157,10 @@ def main():
     ap.add_argument("--workload", choices=["flare", "flare_pp"], default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--configs", default="",
+                    help="instead of the bench line, time the forward of these workloads (comma-separated names "
+                         "from rank_latent_attention_amd.inputs.CONFIGS, or 'all'): 10 warmup and 50 timed calls "
+                         "each, one JSON line per workload with the median, min and max")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB float32 scale kernel (read 256 MiB, write 256 MiB) before the steps, as a "
                          "known-size reference for HBM byte counters")
@@ -109,6 +173,10 @@ def main():
     import torch
     import rank_latent_attention_amd as flare
     from rank_latent_attention_amd.inputs import config5
+
+    if args.configs:
+        time_configs(args.configs)
+        return
 
     pp = args.workload == "flare_pp"
     t0 = time.perf_counter()
