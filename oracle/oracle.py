@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
-           "flare_pp_forward", "materialize"]
+           "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed"]
 
 
 def build(force: bool = True) -> str:
@@ -162,6 +162,49 @@ def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0):
     if rc:
         raise RuntimeError(f"oracle_flare_pp_forward failed ({rc})")
     return Y, Qout, Z, L
+
+
+def rms_norm(x, alpha=None, eps: float = 1e-6) -> np.ndarray:
+    """Per-head RMS normalisation over the head dimension D (the last axis).
+
+    FLARE++ paper, App. A.3 and A.4 and Table 2 in A.7: N_0 divides each row
+    by its root mean square, and N_a additionally multiplies by a learned
+    per-channel scale.  Written out in fp64:
+        y[..., h, r, d] = x[..., h, r, d] / sqrt(mean_d x[..., h, r, :]^2 + eps) * alpha[h, d]
+    ``x`` has the head axis third from last ([H, rows, D] or [B, H, rows, D]);
+    ``alpha`` is [H, D], or None for N_0.  The pages do not state eps; the
+    default 1e-6 is this build's reading.
+    """
+    x = _f64(x)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    if alpha is not None:
+        a = _f64(alpha)
+        if a.shape != (x.shape[-3], x.shape[-1]):
+            raise ValueError(f"alpha must be [H, D] = {(x.shape[-3], x.shape[-1])}, got {a.shape}")
+        y = y * a[:, None, :]
+    return y
+
+
+def flare_pp_forward_normed(Qs, Ks, Vs, Qf, gate, K, V, *, norm_qs=False, norm_ks=False, norm_qf=False,
+                            norm_k=False, alpha_qs=None, alpha_ks=None, alpha_k=None, eps: float = 1e-6,
+                            scale: float = 0.0):
+    """FLARE++ routing forward with its per-head input normalisations applied
+    first, in the order of Table 2 (FLARE++ paper, App. A.7):
+      seeds Q~ -> N(Q~; alpha_qs)     (FLARE++ and the simplified variant: N_a)
+      keys  K~ -> N(K~; alpha_ks)     (FLARE++: N_0; simplified: N_a)
+      V~ is the normalised K~ when it is the same array as K~ (App. A.6),
+      otherwise it is used as given (simplified variant: no norm)
+      Q^f   -> N_0(Q^f)               (FLARE++, App. A.4)
+      K     -> N(K; alpha_k)          (FLARE++: N_a)
+    then the plain FLARE++ forward.  Returns (Y, Q, Z, L).
+    """
+    shared = Vs is Ks
+    Qs_n = rms_norm(Qs, alpha_qs, eps) if norm_qs else Qs
+    Ks_n = rms_norm(Ks, alpha_ks, eps) if norm_ks else Ks
+    Vs_n = Ks_n if shared else Vs
+    Qf_n = rms_norm(Qf, None, eps) if norm_qf else Qf
+    K_n = rms_norm(K, alpha_k, eps) if norm_k else K
+    return flare_pp_forward(Qs_n, Ks_n, Vs_n, Qf_n, gate, K_n, V, scale)
 
 
 def materialize(Q, K, scale: float = 0.0):
