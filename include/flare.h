@@ -118,6 +118,38 @@ int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void*
                      int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Per-head input normalisations of FLARE++ (App. A.3, A.4, A.6 and Table 2 in
+ * App. A.7), fused into flare_pp_forward_norm.  Each is an RMS norm over the
+ * head dimension D of every row: N(x) = x / sqrt(mean_d x_d^2 + eps), then,
+ * for N_a, times a per-channel scale alpha[h, :] (N_0 when alpha is NULL). */
+#define FLARE_NORM_QS 1  /* synthesis seeds Qs, scale alpha_qs (FLARE++ and simplified: N_a) */
+#define FLARE_NORM_KS 2  /* synthesis keys Ks, scale alpha_ks (FLARE++: N_0; simplified: N_a); when
+                            Vs == Ks the values are the normalised keys (App. A.6) */
+#define FLARE_NORM_QF 4  /* fixed queries Qf, N_0 (FLARE++, App. A.4) */
+#define FLARE_NORM_K 8   /* routing keys K, scale alpha_k (FLARE++: N_a); V is never normalised */
+#define FLARE_NORM_ALL 15
+
+/* FLARE++ routing forward with its input normalisations applied inside the
+ * kernels, as they load each tensor (no normalised copy is written):
+ *   FLARE++            norm_flags = QS | KS | QF | K, alpha_qs, alpha_k given,
+ *                      alpha_ks NULL, Vs == Ks;
+ *   simplified FLARE++ norm_flags = QS | KS, alpha_qs, alpha_ks given, separate
+ *                      Vs, Qf all zeros and gate all ones (Q = Qd, no blend).
+ * Arguments as flare_pp_forward, plus:
+ *   norm_flags  OR of FLARE_NORM_*; 0 makes this call flare_pp_forward;
+ *   alpha_qs, alpha_ks, alpha_k  [H, D] float32 device arrays (16-byte aligned)
+ *               or NULL; each is read only when its flag is set;
+ *   eps         > 0 when any flag is set (the pages do not fix it; 1e-6 is
+ *               the value this library's tests use).
+ * Normalisation needs dtype FLARE_BF16 (else FLARE_ERR_UNSUPPORTED); a bad
+ * flag or eps gives FLARE_ERR_INVALID_ARG.  The normalised keys are rounded
+ * to bf16 before the matrix products, like the inputs themselves. */
+int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                          const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out,
+                          int B, int H, int N, int M, int D, int dtype, float scale, int norm_flags,
+                          const float* alpha_qs, const float* alpha_ks, const float* alpha_k, float eps,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* flare_status_string(int status);
 

@@ -4,4 +4,4 @@ The compute path is the HIP library built from csrc/flare.hip (C ABI in
 include/flare.h); ``rank_latent_attention_amd.flare`` is its Python binding.
 """
 from .flare import (FlareError, flare_decode, flare_encode, flare_forward, flare_pp_forward,  # noqa: F401
-                    load, workspace, workspace_size)
+                    flare_pp_forward_norm, load, workspace, workspace_size)

@@ -136,6 +136,64 @@ template <int D, typename QT> __device__ inline void load_op_scaled(QKOp<float, 
   for (int j = 0; j < D / 2; ++j) o.v[j] = to_f(row[g * (D / 2) + j]) * scale;
 }
 
+// ----------------------------------------------------------------------------
+// Per-head RMS normalisation over the head dimension (FLARE++ paper, App. A.3
+// and A.4, Table 2): N_0(x) = x / sqrt(mean_d x_d^2 + eps).  N_a adds a
+// per-channel scale; the kernels move that scale onto the operand it
+// multiplies (the queries, or the merged latents) and only ever apply N_0.
+// ----------------------------------------------------------------------------
+__device__ inline float norm_factor(float sumsq, int D, float eps) { return rsqrtf(sumsq / (float)D + eps); }
+
+// QK operand (bf16) from a query row of type QT: optionally N_0 over the
+// whole row (its other half is held by lane +-32, so all 64 lanes must call
+// this), then multiplied channel by channel by the [D] rows mul0 and mul1
+// (either may be null) and by `scale`, and rounded.
+template <int D, typename QT>
+__device__ inline void load_q_row(QKOp<bf16, D>& o, const QT* row, int g, float scale, bool norm, float eps,
+                                  const float* mul0, const float* mul1) {
+  float x[D / 2];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[8 * st + s] = to_f(row[16 * st + 8 * g + s]);
+  float f = scale;
+  if (norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) ss += x[j] * x[j];
+    f *= norm_factor(pair_sum(ss), D, eps);
+  }
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int d = 16 * st + 8 * g + s;
+      float v = x[8 * st + s] * f;
+      if (mul0) v *= mul0[d];
+      if (mul1) v *= mul1[d];
+      o.v[st][s] = (bf16)v;
+    }
+}
+
+// N_0 of a bf16 QK operand in registers (a key row, half in this lane and
+// half in lane +-32; all 64 lanes must call this).  Returns the row's factor.
+template <int D> __device__ inline float norm_op(QKOp<bf16, D>& o, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float v = (float)o.v[st][s];
+      ss += v * v;
+    }
+  const float r = norm_factor(pair_sum(ss), D, eps);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o.v[st][s] = (bf16)((float)o.v[st][s] * r);
+  return r;
+}
+
 template <int D> __device__ inline f32x16 qk_mma(const QKOp<bf16, D>& a, const QKOp<bf16, D>& b, f32x16 c) {
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[st], b.v[st], c, 0, 0, 0);
@@ -348,6 +406,33 @@ __device__ inline void dma_tile(bf16* tile, const bf16* src, int t0, int n_hi, i
 
 __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// N_0 of every row of a swizzled bf16 tile in LDS, in place, once the tile's
+// DMA is complete and visible to the workgroup.  Each thread takes one
+// 16-byte chunk per pass; the D / 8 chunks of a row sit in consecutive lanes
+// and add their partial sums with xor shuffles.  Rows past the piece repeat a
+// valid row, so every row holds finite values.
+template <int D, int NW> __device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
+  constexpr int CPR = D / 8;
+  constexpr int CH = dma_rows<NW>() * CPR;
+#pragma unroll
+  for (int P0 = 0; P0 < CH; P0 += NW * 64) {
+    const int P = P0 + wave * 64 + lane;
+    if (P0 + wave * 64 < CH) {  // whole waves; CH is a multiple of 64
+      bf16x8* ptr = reinterpret_cast<bf16x8*>(tile) + chunk_pos<D>(P / CPR, P % CPR);
+      bf16x8 v = *ptr;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += (float)v[i] * (float)v[i];
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+      const float r = norm_factor(ss, D, eps);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)v[i] * r);
+      *ptr = v;
+    }
+  }
+}
+
 // Per-lane byte offsets into a swizzled tile for token block 0.  The XOR
 // swizzle of a row only depends on the row index modulo 32, so token block nb
 // adds nb * 64 * D bytes to every offset.
@@ -409,6 +494,12 @@ struct EncArgs {
   long long total;    // nbh * N
   int q_batched, v_alias, H, N, M, G, nwg, pmax, bh0;
   float qscale;       // s * log2(e)
+  // query rows: N_0 when norm_q, then channel scales qmul0 / qmul1 ([H, D] or
+  // null); keys N_0 per row when the kernel's NK flag is set (bf16 only)
+  int norm_q;
+  const float* qmul0;
+  const float* qmul1;
+  float eps;
 };
 
 template <typename T, int D> struct EncLds {
@@ -635,10 +726,13 @@ __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned 
 // with the exact maximum of every block (online softmax with a shift raised
 // whenever the block maximum exceeds it by more than kTheta).  Used only when
 // the fast loop reported weights too large to accumulate safely.
-// Returns the final shift of this lane's latent.
-template <int D>
-__device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo, int n_hi, int ng, int WN, int rows,
-                                       int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
+// With NK the key rows are N_0-normalised as they are loaded, and so are the
+// values when they alias the keys.  Returns the final shift of this lane's
+// latent.
+template <int D, bool NK>
+__device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alias, float eps, int n_lo, int n_hi,
+                                       int ng, int WN, int rows, int lane, const QKOp<bf16, D>& qop, float& lsum,
+                                       f32x16& acc) {
   const int li = lane & 31, g = lane >> 5;
   f32x16 negs;
 #pragma unroll
@@ -650,15 +744,21 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo,
       const int row0 = t0 + 32 * nb;
       if (row0 >= n_hi) break;
       QKOp<bf16, D> kop;
-      if (row0 + li < n_hi) load_op<D>(kop, Kh + (size_t)(row0 + li) * D, g);
-      else zero_op<D>(kop);
+      load_op<D>(kop, Kh + (size_t)(row0 + li < n_hi ? row0 + li : n_hi - 1) * D, g);
+      float r = 1.f;  // N_0 factor of key row row0 + li
+      if constexpr (NK) r = norm_op<D>(kop, eps);
+      if (row0 + li >= n_hi) zero_op<D>(kop);
       PVOp<bf16> vop;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int n = row0 + acc_row(j, g);
-        const bf16 v = (li < D && n < n_hi) ? Vh[(size_t)n * D + li] : (bf16)0.f;
-        if (j < 8) vop.a0[j] = v;
-        else vop.a1[j - 8] = v;
+        float v = (li < D && n < n_hi) ? (float)Vh[(size_t)n * D + li] : 0.f;
+        if constexpr (NK) {
+          const float rn = __shfl(r, acc_row(j, g));  // factor of row n, held by lane n - row0
+          if (alias) v = (float)(bf16)(v * rn);       // the same rounding as the normalised tile
+        }
+        if (j < 8) vop.a0[j] = (bf16)v;
+        else vop.a1[j - 8] = (bf16)v;
       }
       f32x16 sc = qk_mma<D>(kop, qop, negs);
       if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
@@ -675,7 +775,7 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, int n_lo,
 // owns latent block w % G (32 latents) and token blocks w / G + k WN of every
 // ROWS-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
 // DMA of the next tile is in flight while the current one is consumed.
-template <typename QT, int D, int NW, int WN>
+template <typename QT, int D, int NW, int WN, bool NK>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
   constexpr int ROWS = dma_rows<NW>();
   constexpr int TE = ROWS * D;  // elements per tile
@@ -720,8 +820,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
     const int m = mg * 32 + li;
     QKOp<bf16, D> qop;
-    if (m < M) load_op_scaled<D>(qop, Qh + (size_t)m * D, g, a.qscale);
-    else zero_op<D>(qop);
+    load_q_row<D>(qop, Qh + (size_t)(m < M ? m : M - 1) * D, g, a.qscale, a.norm_q != 0, a.eps,
+                  a.qmul0 ? a.qmul0 + (size_t)h * D : nullptr, a.qmul1 ? a.qmul1 + (size_t)h * D : nullptr);
+    if (m >= M) zero_op<D>(qop);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -734,6 +835,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
     wait_dma();
     __syncthreads();
+    if constexpr (NK) {  // key rows N_0 in place (and the values with them when they alias)
+      norm_tile<D, NW>(k0, wave, lane, a.eps);
+      __syncthreads();
+    }
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * ROWS) {
       // tile t0 from buffer 0 while tile t0 + ROWS streams into buffer 1
       const int tn = t0 + ROWS;
@@ -745,6 +850,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
+      if constexpr (NK) {
+        norm_tile<D, NW>(k1, wave, lane, a.eps);
+        __syncthreads();
+      }
       // tile tn from buffer 1 while tn + ROWS streams into buffer 0
       const int tn2 = tn + ROWS;
       if (tn2 < n_hi) {
@@ -754,11 +863,18 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       encode_tile<D, NW, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, lsum, acc);
       wait_dma();
       __syncthreads();
+      if constexpr (NK) {
+        if (tn2 < n_hi) {
+          norm_tile<D, NW>(k0, wave, lane, a.eps);
+          __syncthreads();
+        }
+      }
     }
     // unshifted partial (see fast_ok), or the careful recomputation's
     float ltot = pair_sum(lsum), shift = 0.f;
     if (fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
-      shift = encode_careful<D>(Kh, alias ? Kh : Vh, n_lo, n_hi, ng, WN, ROWS, lane, qop, lsum, acc);
+      shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane, qop, lsum,
+                                    acc);
       ltot = pair_sum(lsum);
     }
     if (m < M) {
@@ -794,6 +910,9 @@ struct MergeArgs {
   float* Qout;        // [B,H,M,D], blend mode only
   long long total;
   int N, M, D, H, WN, nwg, pmax, bh0, nbh;
+  int norm_qf;        // blend with N_0(Qf) instead of Qf
+  const float* zmul;  // [H, D] channel scale of Z (the values' N_a scale), or null
+  float eps;
 };
 
 // Running (A, den, num) of a set of splits: max shift, and sum of l_p and of
@@ -877,16 +996,25 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
     t.num = __shfl_xor(st.num, o);
     st = merge_pair(st, t);
   }
+  const int h = bh % a.H;
+  float qf = 0.f;
+  if (a.Qout) {  // blend mode: the fixed query, N_0 over its D lanes while every lane group is active
+    qf = to_f(reinterpret_cast<const QT*>(a.Qf)[((size_t)h * a.M + m) * D + d]);
+    if (a.norm_qf) {
+      float ss = qf * qf;
+      for (int o = 1; o < D; o <<= 1) ss += __shfl_xor(ss, o);
+      qf *= norm_factor(ss, D, a.eps);
+    }
+  }
   if (pg != 0) return;
   float z = 0.f, lse = -INFINITY;
   if (st.A > -INFINITY) {
     z = st.num / st.den;
     lse = kLn2 * (st.A + __builtin_amdgcn_logf(st.den));
   }
+  if (a.zmul) z *= a.zmul[(size_t)h * D + d];
   const size_t o = ((size_t)bh * a.M + m) * D + d;
   if (a.Qout) {
-    const int h = bh % a.H;
-    const float qf = to_f(reinterpret_cast<const QT*>(a.Qf)[((size_t)h * a.M + m) * D + d]);
     a.Qout[o] = qf + a.gate[h] * z;
   } else {
     a.Z[o] = z;
@@ -905,6 +1033,8 @@ struct DecArgs {
   long long total; // nbh * N
   int q_batched, H, N, M, MB, nwg, bh0;
   float qscale;
+  const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
+  float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
 };
 
 template <typename T, int D> struct DecLds {
@@ -917,8 +1047,9 @@ template <typename T, int D> struct DecLds {
 };
 
 // TAIL: M is not a multiple of 32, so the last latent block has rows past M
-// that must not receive weight (compiled out for whole blocks).
-template <typename T, typename QT, int D, bool TAIL>
+// that must not receive weight (compiled out for whole blocks).  NK: each
+// token's key row is N_0-normalised in registers once per step (bf16).
+template <typename T, typename QT, int D, bool TAIL, bool NK>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -979,8 +1110,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         if (c < pq) {
           const int m = c * QE / D, d0 = c * QE % D;
           const QT* src = reinterpret_cast<const QT*>(&qv[j]);
+          const float* qm = a.qmul ? a.qmul + (size_t)h * D + d0 : nullptr;
 #pragma unroll
-          for (int i = 0; i < QE; ++i) qs[m * L::QST + d0 + i] = from_f<T>(c < nq ? to_f(src[i]) * a.qscale : 0.f);
+          for (int i = 0; i < QE; ++i) {
+            float q = c < nq ? to_f(src[i]) * a.qscale : 0.f;
+            if (qm) q *= qm[i];
+            qs[m * L::QST + d0 + i] = from_f<T>(q);
+          }
         }
       }
 #pragma unroll
@@ -1021,6 +1157,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     for (int st = 0; st < (int)(sizeof(kop.v) / sizeof(kop.v[0])); ++st) asm volatile("" : "+v"(kop.v[st]));
     const f32x16 zero16 = {};
     for (; t0 < n_hi; t0 += kDecGroup) {
+      if constexpr (NK) norm_op<D>(kop, a.eps);
       QKOp<T, D> knext;
       {
         const int tn = t0 + kDecGroup + li;
@@ -1243,24 +1380,39 @@ int check_common(int B, int H, int N, int M, int D, int dtype, int q_batched) {
   return FLARE_OK;
 }
 
-template <typename QT, int D, int NW, int WN>
+template <typename QT, int D, int NW, int WN, bool NK>
 int launch_encode_dma(const EncArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((encode_dma_kernel<QT, D, NW, WN>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((encode_dma_kernel<QT, D, NW, WN, NK>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename QT, int D>
-int launch_encode_bf16_d(const EncArgs& a, int NW, int WN, hipStream_t st) {
-  if (NW == 8) return launch_encode_dma<QT, D, 8, 1>(a, st);
-  if (WN == 4) return launch_encode_dma<QT, D, 4, 4>(a, st);
-  if (WN == 2) return launch_encode_dma<QT, D, 4, 2>(a, st);
-  return launch_encode_dma<QT, D, 4, 1>(a, st);
+template <typename QT, int D, bool NK>
+int launch_encode_bf16_dk(const EncArgs& a, int NW, int WN, hipStream_t st) {
+  if (NW == 8) return launch_encode_dma<QT, D, 8, 1, NK>(a, st);
+  if (WN == 4) return launch_encode_dma<QT, D, 4, 4, NK>(a, st);
+  if (WN == 2) return launch_encode_dma<QT, D, 4, 2, NK>(a, st);
+  return launch_encode_dma<QT, D, 4, 1, NK>(a, st);
 }
 
 template <typename QT>
-int launch_encode_bf16(const EncArgs& a, int D, int NW, int WN, hipStream_t st) {
-  return D == 16 ? launch_encode_bf16_d<QT, 16>(a, NW, WN, st) : launch_encode_bf16_d<QT, 32>(a, NW, WN, st);
+int launch_encode_bf16(const EncArgs& a, int D, int NW, int WN, bool nk, hipStream_t st) {
+  if (nk)
+    return D == 16 ? launch_encode_bf16_dk<QT, 16, true>(a, NW, WN, st)
+                   : launch_encode_bf16_dk<QT, 32, true>(a, NW, WN, st);
+  return D == 16 ? launch_encode_bf16_dk<QT, 16, false>(a, NW, WN, st)
+                 : launch_encode_bf16_dk<QT, 32, false>(a, NW, WN, st);
 }
+
+// Input normalisations of one launch sequence (FLARE++ paper, Table 2):
+// query rows N_0 (norm_q) and channel scales qmul0, qmul1 ([H, D] or null),
+// key rows N_0 (norm_k), epsilon.  Supported with bf16 keys and values.
+struct Norms {
+  int norm_q = 0;
+  const float* qmul0 = nullptr;
+  const float* qmul1 = nullptr;
+  bool norm_k = false;
+  float eps = 0.f;
+};
 
 template <int D, int MBW>
 int launch_encode_f32(const EncArgs& a, hipStream_t st) {
@@ -1272,7 +1424,7 @@ int launch_encode_f32(const EncArgs& a, hipStream_t st) {
 // qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
 int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0, int H, int N,
                   int M, int D, int dtype, float qscale, float* part_acc, float2* part_al, const EncPlan& p,
-                  hipStream_t st) {
+                  const Norms& nm, hipStream_t st) {
   EncArgs a;
   a.Q = Q; a.K = K; a.V = V;
   a.part_acc = part_acc; a.part_al = part_al;
@@ -1280,10 +1432,12 @@ int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const 
   a.q_batched = q_batched; a.v_alias = (K == V); a.H = H; a.N = N; a.M = M;
   a.G = p.G; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0;
   a.qscale = qscale;
+  a.norm_q = nm.norm_q; a.qmul0 = nm.qmul0; a.qmul1 = nm.qmul1; a.eps = nm.eps;
   if (dtype == FLARE_BF16) {
-    if (qtype == FLARE_BF16) return launch_encode_bf16<bf16>(a, D, p.NW, p.WN, st);
-    return launch_encode_bf16<float>(a, D, p.NW, p.WN, st);
+    if (qtype == FLARE_BF16) return launch_encode_bf16<bf16>(a, D, p.NW, p.WN, nm.norm_k, st);
+    return launch_encode_bf16<float>(a, D, p.NW, p.WN, nm.norm_k, st);
   }
+  if (nm.norm_q || nm.qmul0 || nm.qmul1 || nm.norm_k) return FLARE_ERR_UNSUPPORTED;
   if (qtype != FLARE_F32) return FLARE_ERR_UNSUPPORTED;
   if (D == 16) return p.MBW == 2 ? launch_encode_f32<16, 2>(a, st) : launch_encode_f32<16, 1>(a, st);
   return p.MBW == 2 ? launch_encode_f32<32, 2>(a, st) : launch_encode_f32<32, 1>(a, st);
@@ -1291,10 +1445,11 @@ int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const 
 
 int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H, int N,
                  int M, int D, float* Z, float* L, const void* Qf, int qftype, const float* gate, float* Qout,
-                 hipStream_t st) {
+                 int norm_qf, const float* zmul, float eps, hipStream_t st) {
   MergeArgs a;
   a.part_acc = part_acc; a.part_al = part_al;
   a.Z = Z; a.L = L; a.Qf = Qf; a.gate = gate; a.Qout = Qout;
+  a.norm_qf = norm_qf; a.zmul = zmul; a.eps = eps;
   a.total = p.total;
   a.N = N; a.M = M; a.D = D; a.H = H; a.WN = p.WN; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0; a.nbh = nbh;
   const dim3 grid((unsigned)cdiv((long long)nbh * M, kThreads / 64));
@@ -1303,20 +1458,28 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename T, typename QT, int D, bool TAIL>
+template <typename T, typename QT, int D, bool TAIL, bool NK>
 int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
+  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK>;
   if (lds > 65536) {
-    if (hipFuncSetAttribute((const void*)decode_kernel<T, QT, D, TAIL>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK>), dim3(a.nwg), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
 template <typename T, typename QT, int D>
-int launch_decode_t(const DecArgs& a, size_t lds, hipStream_t st) {
-  return (a.M & 31) ? launch_decode_k<T, QT, D, true>(a, lds, st) : launch_decode_k<T, QT, D, false>(a, lds, st);
+int launch_decode_t(const DecArgs& a, size_t lds, bool nk, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (nk)
+      return (a.M & 31) ? launch_decode_k<T, QT, D, true, true>(a, lds, st)
+                        : launch_decode_k<T, QT, D, false, true>(a, lds, st);
+  } else {
+    if (nk) return FLARE_ERR_UNSUPPORTED;
+  }
+  return (a.M & 31) ? launch_decode_k<T, QT, D, true, false>(a, lds, st)
+                    : launch_decode_k<T, QT, D, false, false>(a, lds, st);
 }
 
 size_t decode_lds(int dtype, int D, int M) {
@@ -1325,14 +1488,18 @@ size_t decode_lds(int dtype, int D, int M) {
   return D == 16 ? DecLds<float, 16>::bytes(MB) : DecLds<float, 32>::bytes(MB);
 }
 
+// nm.norm_k: N_0 of the key rows; nm.qmul1: channel scale of the queries.
 int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const float* Z, void* Y,
-                  int bh0, int nbh, int H, int N, int M, int D, int dtype, float qscale, hipStream_t st) {
+                  int bh0, int nbh, int H, int N, int M, int D, int dtype, float qscale, const Norms& nm,
+                  hipStream_t st) {
   if (N == 0) return FLARE_OK;
   DecArgs a;
   a.Q = Q; a.K = K; a.Z = Z; a.Y = Y;
   a.total = (long long)nbh * N;
   a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = bh0;
   a.qscale = qscale;
+  a.qmul = nm.qmul1; a.eps = nm.eps;
+  const bool nk = nm.norm_k;
   long long want = (long long)dev.cus * kDecWgPerCu;
   long long maxw = cdiv(a.total, 32);
   a.nwg = (int)(want < maxw ? want : maxw);
@@ -1340,11 +1507,11 @@ int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const
   if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   if (dtype == FLARE_BF16) {
     if (qtype == FLARE_BF16)
-      return D == 16 ? launch_decode_t<bf16, bf16, 16>(a, lds, st) : launch_decode_t<bf16, bf16, 32>(a, lds, st);
-    return D == 16 ? launch_decode_t<bf16, float, 16>(a, lds, st) : launch_decode_t<bf16, float, 32>(a, lds, st);
+      return D == 16 ? launch_decode_t<bf16, bf16, 16>(a, lds, nk, st) : launch_decode_t<bf16, bf16, 32>(a, lds, nk, st);
+    return D == 16 ? launch_decode_t<bf16, float, 16>(a, lds, nk, st) : launch_decode_t<bf16, float, 32>(a, lds, nk, st);
   }
-  if (qtype != FLARE_F32) return FLARE_ERR_UNSUPPORTED;
-  return D == 16 ? launch_decode_t<float, float, 16>(a, lds, st) : launch_decode_t<float, float, 32>(a, lds, st);
+  if (qtype != FLARE_F32 || nm.qmul1) return FLARE_ERR_UNSUPPORTED;
+  return D == 16 ? launch_decode_t<float, float, 16>(a, lds, nk, st) : launch_decode_t<float, float, 32>(a, lds, nk, st);
 }
 
 float pick_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
@@ -1428,10 +1595,11 @@ int flare_encode(const void* Q, int q_batched, const void* K, const void* V, flo
   float* pacc = (float*)((char*)ws + w.part_acc);
   float2* pal = (float2*)((char*)ws + w.part_al);
   if (N > 0) {
-    rc = launch_encode(Q, dtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, st);
+    rc = launch_encode(Q, dtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, Norms{}, st);
     if (rc) return rc;
   }
-  return launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, st);
+  return launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f,
+                      st);
 }
 
 int flare_decode(const void* Q, int q_batched, const void* K, const float* Z, void* Y, int B, int H, int N, int M,
@@ -1445,14 +1613,16 @@ int flare_decode(const void* Q, int q_batched, const void* K, const float* Z, vo
   if ((rc = query_dev(dev))) return rc;
   if (decode_lds(dtype, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const float qs = pick_scale(scale, D) * kLog2e;
-  return launch_decode(dev, Q, dtype, q_batched, K, Z, Y, 0, B * H, H, N, M, D, dtype, qs, (hipStream_t)stream);
+  return launch_decode(dev, Q, dtype, q_batched, K, Z, Y, 0, B * H, H, N, M, D, dtype, qs, Norms{},
+                       (hipStream_t)stream);
 }
 
 // Shared by flare_forward and the routing half of flare_pp_forward: encode ->
-// merge -> decode per head group.  Q has element type qtype.
+// merge -> decode per head group.  Q has element type qtype; nm carries the
+// routing keys' normalisation (N_0 rows, and their scale moved onto Q).
 static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const void* V, void* Y,
                    float* Z, float* L, int B, int H, int N, int M, int D, int dtype, float qs, char* ws,
-                   const WsLayout& w, hipStream_t st) {
+                   const WsLayout& w, const Norms& nm, hipStream_t st) {
   const int BH = B * H;
   const int grp = heads_per_group(BH, N, D, dtype);
   float* pacc = (float*)(ws + w.part_acc);
@@ -1462,12 +1632,13 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
     const int nbh = BH - bh0 < grp ? BH - bh0 : grp;
     const EncPlan p = plan_encode(dev, nbh, N, M, dtype);
     if (N > 0) {
-      rc = launch_encode(Q, qtype, q_batched, K, V, bh0, H, N, M, D, dtype, qs, pacc, pal, p, st);
+      rc = launch_encode(Q, qtype, q_batched, K, V, bh0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st);
       if (rc) return rc;
     }
-    rc = launch_merge(p, pacc, pal, bh0, nbh, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, st);
+    rc = launch_merge(p, pacc, pal, bh0, nbh, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr,
+                      0.f, st);
     if (rc) return rc;
-    rc = launch_decode(dev, Q, qtype, q_batched, K, Z, Y, bh0, nbh, H, N, M, D, dtype, qs, st);
+    rc = launch_decode(dev, Q, qtype, q_batched, K, Z, Y, bh0, nbh, H, N, M, D, dtype, qs, nm, st);
     if (rc) return rc;
   }
   return FLARE_OK;
@@ -1491,18 +1662,24 @@ int flare_forward(const void* Q, int q_batched, const void* K, const void* V, vo
   float* Z = Z_out ? Z_out : (float*)(wsc + w.z);
   float* L = L_out ? L_out : (float*)(wsc + w.l);
   const float qs = pick_scale(scale, D) * kLog2e;
-  return routing(dev, Q, dtype, q_batched, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, (hipStream_t)stream);
+  return routing(dev, Q, dtype, q_batched, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, Norms{},
+                 (hipStream_t)stream);
 }
 
-int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
-                     const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out, int B, int H,
-                     int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
+int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                          const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out, int B,
+                          int H, int N, int M, int D, int dtype, float scale, int norm_flags, const float* alpha_qs,
+                          const float* alpha_ks, const float* alpha_k, float eps, void* ws, size_t ws_bytes,
+                          void* stream) {
   int rc = check_common(B, H, N, M, D, dtype, 0);
   if (rc) return rc;
   if (!Qs || !Qf || !gate || (N > 0 && (!Ks || !Vs || !K || !V || !Y))) return FLARE_ERR_INVALID_ARG;
-  const void* ptrs[] = {Qs, Ks, Vs, Qf, gate, K, V, Y, Q_out, Z_out, L_out, ws};
+  const void* ptrs[] = {Qs, Ks, Vs, Qf, gate, K, V, Y, Q_out, Z_out, L_out, ws, alpha_qs, alpha_ks, alpha_k};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags & ~FLARE_NORM_ALL) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags && !(eps > 0.f)) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags && dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
   Dev dev;
   if ((rc = query_dev(dev))) return rc;
   if (decode_lds(dtype, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
@@ -1515,18 +1692,42 @@ int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void*
   float* L = L_out ? L_out : (float*)(wsc + w.l);
   const float qs = pick_scale(scale, D) * kLog2e;
   const int BH = B * H;
+  // Synthesis: seeds N_a (N_0 rows, then alpha_qs), keys N_0 rows with their
+  // scale alpha_ks moved onto the seeds, and, when the values are the keys,
+  // onto the merged latents too (they are linear in the values).
+  const bool nks = norm_flags & FLARE_NORM_KS;
+  Norms syn;
+  syn.norm_q = (norm_flags & FLARE_NORM_QS) ? 1 : 0;
+  syn.qmul0 = syn.norm_q ? alpha_qs : nullptr;
+  syn.qmul1 = nks ? alpha_ks : nullptr;
+  syn.norm_k = nks;
+  syn.eps = eps;
+  const float* zmul = (nks && Ks == Vs) ? alpha_ks : nullptr;
+  // Routing: keys N_0 rows with their scale alpha_k moved onto the queries.
+  Norms rt;
+  rt.norm_k = norm_flags & FLARE_NORM_K;
+  rt.qmul1 = rt.norm_k ? alpha_k : nullptr;
+  rt.eps = eps;
   // Synthesis encode over all heads, merged straight into the blended queries.
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   float* pacc = (float*)(wsc + w.part_acc);
   float2* pal = (float2*)(wsc + w.part_al);
   if (N > 0) {
-    rc = launch_encode(Qs, dtype, 0, Ks, Vs, 0, H, N, M, D, dtype, qs, pacc, pal, p, st);
+    rc = launch_encode(Qs, dtype, 0, Ks, Vs, 0, H, N, M, D, dtype, qs, pacc, pal, p, syn, st);
     if (rc) return rc;
   }
-  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, nullptr, nullptr, Qf, dtype, gate, Qb, st);
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, nullptr, nullptr, Qf, dtype, gate, Qb,
+                    (norm_flags & FLARE_NORM_QF) ? 1 : 0, zmul, eps, st);
   if (rc) return rc;
   // Routing with the per-batch float32 queries.
-  return routing(dev, Qb, FLARE_F32, 1, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, st);
+  return routing(dev, Qb, FLARE_F32, 1, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, rt, st);
+}
+
+int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                     const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out, int B, int H,
+                     int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
+  return flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, Y, Q_out, Z_out, L_out, B, H, N, M, D, dtype, scale, 0,
+                               nullptr, nullptr, nullptr, 0.f, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -24,11 +24,15 @@ LIB_PATH = os.path.join(_PKG, "libflare.so")
 
 F32, BF16 = 0, 1
 OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD = 0, 1, 2, 3
+#: input normalisation flags of flare_pp_forward_norm (include/flare.h)
+NORM_QS, NORM_KS, NORM_QF, NORM_K = 1, 2, 4, 8
+NORM_FLAREPP = NORM_QS | NORM_KS | NORM_QF | NORM_K  # FLARE++ (Table 2)
+NORM_SIMPLIFIED = NORM_QS | NORM_KS                  # simplified FLARE++ (Table 2)
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
-           "flare_status_string")
+           "flare_pp_forward_norm", "flare_status_string")
 
 _lib = None
 
@@ -54,7 +58,9 @@ def load(path: str = LIB_PATH):
     L.flare_decode.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward):
+    L.flare_pp_forward_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, vp, f,
+                                        vp, sz, vp]
+    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -185,4 +191,37 @@ def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0, Y=None, Q_o
                                  _ptr(Q_out), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(K.device))
     _check("flare_pp_forward", rc)
+    return Y, Q_out, Z, L
+
+
+def flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, norm_flags: int, alpha_qs=None, alpha_ks=None, alpha_k=None,
+                          eps: float = 1e-6, scale: float = 0.0, Y=None, Q_out=None, Z=None, L=None, ws=None):
+    """FLARE++ routing forward with the per-head RMS norms of the flags fused
+    into the kernels (flare_pp_forward_norm in include/flare.h); alpha_* are
+    float32 [H, D] or None.  Returns (Y, Q_out, Z, L)."""
+    if K.dim() != 4:
+        raise ValueError("K must be [B,H,N,D]")
+    B, H, N, D = K.shape
+    if Qs.dim() != 3 or Qs.shape[0] != H or Qs.shape[2] != D or Qf.shape != Qs.shape:
+        raise ValueError("Qs and Qf must be [H,M,D]")
+    M = Qs.shape[1]
+    dt = _dtype_code(K)
+    for t in (Qs, Ks, Vs, Qf, V):
+        if t.dtype != K.dtype:
+            raise ValueError("Qs, Ks, Vs, Qf, K, V must share one dtype")
+    if Ks.shape != K.shape or Vs.shape != K.shape or V.shape != K.shape:
+        raise ValueError("Ks, Vs, K, V must all be [B,H,N,D]")
+    if gate.dtype != torch.float32 or gate.numel() != H:
+        raise ValueError("gate must be float32 [H]")
+    for a in (alpha_qs, alpha_ks, alpha_k):
+        if a is not None and (a.dtype != torch.float32 or tuple(a.shape) != (H, D)):
+            raise ValueError("alpha arrays must be float32 [H, D]")
+    Y = torch.empty_like(K) if Y is None else Y
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L, alpha_qs, alpha_ks, alpha_k)
+    ws = workspace(OP_PP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_pp_forward_norm(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Y),
+                                      _ptr(Q_out), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale), int(norm_flags),
+                                      _ptr(alpha_qs), _ptr(alpha_ks), _ptr(alpha_k), float(eps), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_pp_forward_norm", rc)
     return Y, Q_out, Z, L

@@ -39,7 +39,8 @@ GATE_LOGIT = 0.25  # paper App. A.4 / Table 2: gate logits start at 0.25
 _TAGS = {
     "q": 1, "k": 2, "v": 3, "x": 4, "wk": 5, "wv": 6, "noise": 7, "lift": 8,
     "pts": 9, "omega": 10, "ids": 11, "emb": 12, "qs": 13, "qf": 14, "wks": 15,
-    "vs": 16, "wvs": 17,
+    "vs": 16, "wvs": 17, "ks": 18, "qs_mag": 19, "ks_mag": 20, "k_mag": 21, "qf_mag": 22,
+    "alpha_qs": 23, "alpha_ks": 24, "alpha_k": 25,
 }
 
 
@@ -83,6 +84,10 @@ class Workload:
     FLARE++: additionally Qs (synthesis seeds) [H,M,D], Ks [B,H,N,D],
              Vs [B,H,N,D] (``Vs is Ks`` when the block shares them),
              Qf (fixed queries) [H,M,D] and gate [H] (= sigmoid(gamma)).
+    Raw FLARE++ (norm_flags != 0): the inputs are not normalised; the
+             forward applies the per-head RMS norms of the flags (values as
+             the library's FLARE_NORM_* bits) with the learned channel
+             scales alpha_qs, alpha_ks, alpha_k [H,D] (None = no scale).
     """
 
     name: str
@@ -103,6 +108,10 @@ class Workload:
     gate: Optional[np.ndarray] = None
     scale: float = 0.0  # <= 0 means 1/sqrt(D)
     recipe: str = ""
+    norm_flags: int = 0
+    alpha_qs: Optional[np.ndarray] = None
+    alpha_ks: Optional[np.ndarray] = None
+    alpha_k: Optional[np.ndarray] = None
 
     @property
     def shared_vs(self) -> bool:
@@ -154,6 +163,46 @@ def make_gaussian_pp(B, H, N, M, D, dtype="bf16", seed=0, share_vs=True, gate=No
         else np.asarray(gate, dtype=np.float32).reshape(H)
     return dataclasses.replace(base, K=K, pp=True, Qs=Qs, Ks=Ks, Vs=Vs, Qf=Qf, gate=g,
                                recipe=base.recipe + "; FLARE++: Ks=N0(N(0,1)), Qs,Qf=N0(N(0,1/D)), K=N0(K)")
+
+
+def channel_scales(seed, tag, H, D, std=0.1) -> np.ndarray:
+    """Per-head learned channel scales of an RMS norm: 1 + N(0, std^2), float32 [H, D]."""
+    return (1.0 + _gauss(seed, tag, (H, D), std)).astype(np.float32)
+
+
+def make_gaussian_pp_raw(B, H, N, M, D, dtype="bf16", seed=0, variant="flarepp", name="gaussian_pp_raw"):
+    """Un-normalised FLARE++ inputs for the fused-norm forward.
+
+    variant "flarepp": Vs is Ks; norms on Qs (N_a), Ks (N_0), Qf (N_0) and
+    K (N_a), flags 15.  variant "simplified": a separate Vs; norms on Qs and
+    Ks (both N_a), flags 3; Qf = 0 and gate = 1 so the routing query is the
+    synthesised one.  Row magnitudes are spread (log-normal, sigma 0.5, per
+    row) so the norms change every row, while the raw scores stay moderate;
+    the learned channel scales are 1 + N(0, 0.1^2).
+    """
+    def rows(tag, shape, std):  # Gaussian rows with a per-row log-normal magnitude
+        x = _gauss(seed, tag, shape, std)
+        return x * np.exp(_gauss(seed, tag + "_mag", shape[:-1] + (1,), 0.5))
+    Qs = to_dtype(rows("qs", (H, M, D), 0.6), dtype)
+    Ks = to_dtype(rows("ks", (B, H, N, D), 0.7), dtype)
+    K = to_dtype(rows("k", (B, H, N, D), 0.7), dtype)
+    V = to_dtype(_gauss(seed, "v", (B, H, N, D)), dtype)
+    if variant == "flarepp":
+        Vs = Ks
+        Qf = to_dtype(rows("qf", (H, M, D), 0.5), dtype)
+        g = np.full((H,), 1.0 / (1.0 + math.exp(-GATE_LOGIT)), dtype=np.float32)
+        flags, aks, ak = 15, None, channel_scales(seed, "alpha_k", H, D)
+    elif variant == "simplified":
+        Vs = to_dtype(_gauss(seed, "vs", (B, H, N, D), 1.3), dtype)
+        Qf = to_dtype(np.zeros((H, M, D)), dtype)
+        g = np.ones((H,), dtype=np.float32)
+        flags, aks, ak = 3, channel_scales(seed, "alpha_ks", H, D), None
+    else:
+        raise ValueError(f"unknown variant {variant!r}")
+    return Workload(name, B, H, N, M, D, dtype, Q=Qf, K=K, V=V, pp=True, Qs=Qs, Ks=Ks, Vs=Vs, Qf=Qf, gate=g,
+                    norm_flags=flags, alpha_qs=channel_scales(seed, "alpha_qs", H, D), alpha_ks=aks, alpha_k=ak,
+                    recipe=f"raw FLARE++ ({variant}): rows N(0, s^2) x lognormal(0, 0.5) magnitude, "
+                           f"alpha = 1 + N(0, 0.01); seed {seed}")
 
 
 # ---------------------------------------------------------------------------
@@ -239,6 +288,28 @@ def config4(seed=4, B=32, N=4096):
 def sphere_points(seed: int, B: int, N: int) -> np.ndarray:
     g = _rng(seed, "pts").standard_normal(size=(B, N, 3))
     return g / np.linalg.norm(g, axis=-1, keepdims=True)
+
+
+def config5_raw(seed=5, N=1 << 20, H=8):
+    """The million-point FLARE++ workload before its per-head norms: Ks, K, Qs
+    and Qf as in config5(pp=True) but not normalised, and the learned channel
+    scales of Qs and K drawn as 1 + N(0, 0.01); the forward normalises them
+    (flags 15, the FLARE++ column of Table 2)."""
+    B, D, M, C = 1, 32, 256, 128
+    pts = sphere_points(seed, B, N).astype(np.float32)
+    omega = _gauss(seed, "omega", (C // 2, 3), 4.0).astype(np.float32)
+    X = _rff(pts, omega).astype(np.float32)
+    K = _heads(X, _gauss(seed, "wk", (C, H * D)).astype(np.float32), H, D)
+    V = _heads(X, _gauss(seed, "wv", (C, H * D)).astype(np.float32), H, D)
+    Ks = to_dtype(_heads(X, _gauss(seed, "wks", (C, H * D)).astype(np.float32), H, D), "bf16")
+    Qs = _gauss(seed, "qs", (H, M, D), 1.0 / math.sqrt(D))
+    Qf = _gauss(seed, "qf", (H, M, D), 1.0 / math.sqrt(D))
+    g = np.full((H,), 1.0 / (1.0 + math.exp(-GATE_LOGIT)), dtype=np.float32)
+    return Workload("c5_surface_mesh_pp_raw_bf16", B, H, N, M, D, "bf16", Q=to_dtype(Qf, "bf16"),
+                    K=to_dtype(K, "bf16"), V=to_dtype(V, "bf16"), pp=True, Qs=to_dtype(Qs, "bf16"), Ks=Ks, Vs=Ks,
+                    Qf=to_dtype(Qf, "bf16"), gate=g, norm_flags=15,
+                    alpha_qs=channel_scales(seed, "alpha_qs", H, D), alpha_k=channel_scales(seed, "alpha_k", H, D),
+                    recipe="as c5pp before the norms: Ks=RFF Wks/sqrt 128 (=Vs), K, Qs, Qf raw; alpha=1+N(0,0.01)")
 
 
 def config5(pp=False, seed=5, N=1 << 20, H=8):

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
-                                           "flare_pp_forward", "flare_status_string"])
+                                           "flare_pp_forward", "flare_pp_forward_norm", "flare_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -75,3 +75,19 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.flare_workspace_size(9, 1, 1, 8, 8, 16, 1) == 0
     assert lib.flare_workspace_size(0, 1, 1, 8, 8, 24, 1) == 0
     assert lib.flare_workspace_size(1, 1, 1, 8, 8, 16, 1) == 0   # the decode needs no workspace
+
+
+def ppn(lib, flags=15, eps=1e-6, dt=1, D=16, aqs=None, aks=None, ak=None):
+    return lib.flare_pp_forward_norm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                     1, 1, 8, 8, D, dt, 0.0, flags, aqs, aks, ak, eps, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=16), 1), (dict(flags=-1), 1),                       # unknown flag bits
+    (dict(eps=0.0), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
+    (dict(dt=0), 2),                                                 # float32 inputs cannot be normalised
+    (dict(aqs=MISALIGNED), 1), (dict(ak=MISALIGNED), 1),
+    (dict(D=20), 2),
+])
+def test_pp_forward_norm_rejects_bad_arguments(lib, kw, status):
+    assert ppn(lib, **kw) == status
