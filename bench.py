@@ -69,7 +69,16 @@ def cpu_baseline(w, target_s: float = 15.0):
 
     def run(k):
         t0 = time.perf_counter()
-        if w.pp:
+        if w.pp and w.norm_flags:
+            f = w.norm_flags
+            Ks = heads(w.Ks, k)
+            oracle.flare_pp_forward_normed(
+                w.Qs[:k], Ks, Ks if w.Vs is w.Ks else heads(w.Vs, k), w.Qf[:k], w.gate[:k], heads(w.K, k),
+                heads(w.V, k), norm_qs=bool(f & 1), norm_ks=bool(f & 2), norm_qf=bool(f & 4), norm_k=bool(f & 8),
+                alpha_qs=None if w.alpha_qs is None else w.alpha_qs[:k],
+                alpha_ks=None if w.alpha_ks is None else w.alpha_ks[:k],
+                alpha_k=None if w.alpha_k is None else w.alpha_k[:k])
+        elif w.pp:
             oracle.flare_pp_forward(w.Qs[:k], heads(w.Ks, k), heads(w.Vs, k), w.Qf[:k], w.gate[:k],
                                     heads(w.K, k), heads(w.V, k))
         else:
@@ -82,6 +91,8 @@ def cpu_baseline(w, target_s: float = 15.0):
     # a token of the whole routing pass needs all H heads
     value = w.B * w.N * k / (t * w.H)
     what = "FLARE++ forward (synthesis encode, blend, encode + decode)" if w.pp else "FLARE forward (encode + decode)"
+    if w.norm_flags:
+        what = "FLARE++ forward with its per-head RMS norms (norms, synthesis encode, blend, encode + decode)"
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle {what} on heads 0..{k - 1} of {w.H}, all {w.N} tokens, "
                       f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
@@ -154,8 +165,9 @@ def main():
     # MFMA + transcendental load; 30 warmup steps (about 90 launches) reach it
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["flare", "flare_pp"], default="flare",
-                    help="FLARE or FLARE++ routing forward on the million-point surface mesh")
+    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm"], default="flare",
+                    help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
+                         "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--configs", default="",
                     help="instead of the bench line, time the forward of these workloads (comma-separated names "
@@ -172,15 +184,16 @@ def main():
 
     import torch
     import rank_latent_attention_amd as flare
-    from rank_latent_attention_amd.inputs import config5
+    from rank_latent_attention_amd.inputs import config5, config5_raw
 
     if args.configs:
         time_configs(args.configs)
         return
 
-    pp = args.workload == "flare_pp"
+    pp = args.workload in ("flare_pp", "flare_pp_norm")
+    norm = args.workload == "flare_pp_norm"
     t0 = time.perf_counter()
-    w = config5(pp=pp)
+    w = config5_raw() if norm else config5(pp=pp)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
 
@@ -198,8 +211,15 @@ def main():
         Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
         ws = flare.workspace(flare.flare.OP_PP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
 
-        def step():
-            flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Y=Y, Q_out=Qo, Z=Z, L=L, ws=ws)
+        if norm:
+            aqs, ak = (torch.from_numpy(w.alpha_qs).to(dev), torch.from_numpy(w.alpha_k).to(dev))
+
+            def step():
+                flare.flare_pp_forward_norm(Qs, Ks, Ks, Qf, gate, K, V, w.norm_flags, aqs, None, ak, Y=Y, Q_out=Qo,
+                                            Z=Z, L=L, ws=ws)
+        else:
+            def step():
+                flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Y=Y, Q_out=Qo, Z=Z, L=L, ws=ws)
     else:
         Q = up(w.Q)
         ws = flare.workspace(flare.flare.OP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
@@ -225,50 +245,62 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} steps: {ms:.3f} ms/step")
 
-    # Per-phase times with events between the launches: the encode entry
-    # point (encode partials + merge) and the decode entry point (decode
-    # kernel alone), run back to back exactly as one flare_forward step runs them.
-    Qr = Qo if pp else Q
-    qb = Qr.to(torch.bfloat16).contiguous() if pp else Qr
-    nrep = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
-    wse = flare.workspace(flare.flare.OP_ENCODE, B, H, N, M, D, flare.flare.BF16, dev)
-    for i in range(nrep):
-        ev[3 * i].record(stream)
-        flare.flare_encode(qb, K, V, Z=Z, L=L, ws=wse)
-        ev[3 * i + 1].record(stream)
-        flare.flare_decode(qb, K, Z, Y=Y)
-        ev[3 * i + 2].record(stream)
-    torch.cuda.synchronize()
-    t_enc = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(nrep))[nrep // 2]
-    t_dec = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(nrep))[nrep // 2]
-    log(f"phases (median of {nrep}): encode+merge {t_enc * 1e3:.1f} us, decode {t_dec * 1e3:.1f} us")
+    if not norm:
+        # Per-phase times with events between the launches: the encode entry
+        # point (encode partials + merge) and the decode entry point (decode
+        # kernel alone), run back to back exactly as one flare_forward step runs them.
+        Qr = Qo if pp else Q
+        qb = Qr.to(torch.bfloat16).contiguous() if pp else Qr
+        nrep = max(args.steps, 5)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+        wse = flare.workspace(flare.flare.OP_ENCODE, B, H, N, M, D, flare.flare.BF16, dev)
+        for i in range(nrep):
+            ev[3 * i].record(stream)
+            flare.flare_encode(qb, K, V, Z=Z, L=L, ws=wse)
+            ev[3 * i + 1].record(stream)
+            flare.flare_decode(qb, K, Z, Y=Y)
+            ev[3 * i + 2].record(stream)
+        torch.cuda.synchronize()
+        t_enc = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(nrep))[nrep // 2]
+        t_dec = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(nrep))[nrep // 2]
+        log(f"phases (median of {nrep}): encode+merge {t_enc * 1e3:.1f} us, decode {t_dec * 1e3:.1f} us")
 
-    # Roofline of the dominant kernel, the decode: it is the longest single
-    # kernel of the step in the committed kernel traces, and the decode entry
-    # point launches it alone, so events around that call time exactly it.
-    # The encode entry point launches the encode and the split merge; its
-    # phase time is reported beside it.
-    half_flops = 4.0 * B * H * N * M * D           # one of the two SDPA passes
-    kname, kt = "decode_kernel", t_dec
-    kb = B * H * N * D * 2 * 2                     # algorithmic: read K, write Y (bf16)
-    achieved = half_flops / (kt * 1e-3) / 1e12
-    exps = B * H * N * M                           # one exponential per score of the pass
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(kname, args.workload),
-                "kernel": kname, "kernel_us": round(kt * 1e3, 2), "algorithmic_bytes": kb,
-                "hbm_frac": round(kb / (kt * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "exp_rate_T_per_s": round(exps / (kt * 1e-3) / 1e12, 2),
-                "exp_frac": round(exps / (kt * 1e-3) / 1e12 / PEAK_EXP_T, 4),
-                "encode_and_merge_us": round(t_enc * 1e3, 2)}
+        # Roofline of the dominant kernel, the decode: it is the longest single
+        # kernel of the step in the committed kernel traces, and the decode entry
+        # point launches it alone, so events around that call time exactly it.
+        # The encode entry point launches the encode and the split merge; its
+        # phase time is reported beside it.
+        half_flops = 4.0 * B * H * N * M * D           # one of the two SDPA passes
+        kname, kt = "decode_kernel", t_dec
+        kb = B * H * N * D * 2 * 2                     # algorithmic: read K, write Y (bf16)
+        achieved = half_flops / (kt * 1e-3) / 1e12
+        exps = B * H * N * M                           # one exponential per score of the pass
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(kname, args.workload),
+                    "kernel": kname, "kernel_us": round(kt * 1e3, 2), "algorithmic_bytes": kb,
+                    "hbm_frac": round(kb / (kt * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "exp_rate_T_per_s": round(exps / (kt * 1e-3) / 1e12, 2),
+                    "exp_frac": round(exps / (kt * 1e-3) / 1e12 / PEAK_EXP_T, 4),
+                    "encode_and_merge_us": round(t_enc * 1e3, 2)}
 
     flops = (12.0 if pp else 8.0) * B * H * N * M * D
+    if norm:
+        # The normalising kernels are reached only through the whole forward
+        # (the encode and decode entry points take no norms), so this
+        # workload's roofline is the step's: its 12 BHNMD FLOPs over the step
+        # time.  Per-kernel times are in the kernel trace.
+        achieved = flops / (ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "whole step (5 launches)", "kernel_us": round(ms * 1e3, 2),
+                    "algorithmic_bytes": 4 * B * H * N * D * 2}
     tok_s = B * N / (ms * 1e-3)
     out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": ("FLARE++" if pp else "FLARE") + " routing forward, million-point surface mesh",
+           "config": {"workload": ("FLARE++" if pp else "FLARE") + " routing forward, million-point surface mesh"
+                      + (", per-head RMS norms fused" if norm else ""),
                       "B": B, "H": H, "N": N, "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "step_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
