@@ -228,3 +228,196 @@ int oracle_threads(int n) {
 #else
 int oracle_threads(int n) { (void)n; return 1; }
 #endif
+
+/* ------------------------------------------------------------------------
+ * Backward (reverse mode) of the encoder and the decoder.
+ *
+ * Encoder, App. B.5 "Local backward" with a single shard (R = 1): given the
+ * cotangents dZ and dL of the encoder outputs (Z, L), with
+ *   S = s Q K^T,  P = softmax over the tokens of S,  c_m = dZ_m . Z_m
+ *   (the row term of the softmax derivative, which the pages write as c),
+ *   dS = P o (dZ V^T - c + dL)     (c and dL broadcast along the tokens)
+ *   dV = P^T dZ,  dK = s dS^T Q,  dQ = s dS K.
+ * Decoder: the same derivative for Y = SDPA(K, Q, Z), whose softmax runs over
+ * the latents (App. A.1): with U = s K Q^T, W = softmax over the latents,
+ * delta_n = dY_n . Y_n and no log-normaliser output,
+ *   dU = W o (dY Z^T - delta)     (delta broadcast along the latents)
+ *   dZ = W^T dY,  dK = s dU Q,  dQ = s dU^T K.
+ * When Q is shared over the batch (q_batched == 0) its cotangent is the sum
+ * of the per-batch ones.
+ *
+ * Each output element is a plain sum in ascending index order; the row
+ * statistics (max shift, sum, row term) are formed first, so no parallel
+ * reduction is involved and results do not depend on the thread count.
+ * ------------------------------------------------------------------------ */
+
+/* Encoder row statistics of one head: L_m, Z_m (via encode_row) and c_m. */
+static void enc_stats(const double* Qh, const double* Kh, const double* Vh, const double* dZh, int N, int M,
+                      int D, double s, double* L, double* Zh, double* c) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        L[m] = encode_row(Qh + (size_t)m * D, Kh, Vh, N, D, s, Zh + (size_t)m * D);
+        c[m] = dot(dZh + (size_t)m * D, Zh + (size_t)m * D, D);
+    }
+}
+
+/* dS_mn of the encoder (see above); P = exp(S - L). */
+static double enc_dscore(const double* q, const double* k, const double* v, const double* dz, double Lm, double cm,
+                         double dLm, int D, double s, double* p) {
+    *p = exp(s * dot(q, k, D) - Lm);
+    return *p * (dot(dz, v, D) - cm + dLm);
+}
+
+int oracle_encode_backward(const double* Q, int q_batched, const double* K, const double* V, const double* dZ,
+                           const double* dL, int B, int H, int N, int M, int D, double scale, double* dQ,
+                           double* dK, double* dV) {
+    if (B <= 0 || H <= 0 || N < 0 || M <= 0 || D <= 0) return 1;
+    const double s = pick_scale(scale, D);
+    const size_t nq = (size_t)(q_batched ? B : 1) * H * M * D;
+    memset(dQ, 0, sizeof(double) * nq);
+    if (N == 0) return 0;
+    double* L = (double*)malloc(sizeof(double) * (size_t)M);
+    double* c = (double*)malloc(sizeof(double) * (size_t)M);
+    double* Zh = (double*)malloc(sizeof(double) * (size_t)M * D);
+    if (!L || !c || !Zh) { free(L); free(c); free(Zh); return 2; }
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const size_t bh = (size_t)b * H + h;
+            const double* Qh = q_ptr(Q, q_batched, b, h, H, M, D);
+            const double* Kh = K + bh * N * D;
+            const double* Vh = V + bh * N * D;
+            const double* dZh = dZ + bh * M * D;
+            const double* dLh = dL ? dL + bh * M : NULL;
+            enc_stats(Qh, Kh, Vh, dZh, N, M, D, s, L, Zh, c);
+            /* per token: dV_n = sum_m P_mn dZ_m, dK_n = s sum_m dS_mn q_m */
+#pragma omp parallel for schedule(static)
+            for (int n = 0; n < N; ++n) {
+                const double* k = Kh + (size_t)n * D;
+                const double* v = Vh + (size_t)n * D;
+                double* dk = dK + (bh * N + n) * D;
+                double* dv = dV + (bh * N + n) * D;
+                for (int d = 0; d < D; ++d) { dk[d] = 0.0; dv[d] = 0.0; }
+                for (int m = 0; m < M; ++m) {
+                    double p;
+                    const double* q = Qh + (size_t)m * D;
+                    const double* dz = dZh + (size_t)m * D;
+                    const double ds = enc_dscore(q, k, v, dz, L[m], c[m], dLh ? dLh[m] : 0.0, D, s, &p);
+                    for (int d = 0; d < D; ++d) {
+                        dv[d] += p * dz[d];
+                        dk[d] += s * ds * q[d];
+                    }
+                }
+            }
+            /* per latent: dQ_m += s sum_n dS_mn k_n */
+            double* dQh = dQ + (q_batched ? bh : (size_t)h) * M * D;
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int m = 0; m < M; ++m) {
+                const double* q = Qh + (size_t)m * D;
+                const double* dz = dZh + (size_t)m * D;
+                double* dq = dQh + (size_t)m * D;
+                for (int n = 0; n < N; ++n) {
+                    double p;
+                    const double* k = Kh + (size_t)n * D;
+                    const double ds = enc_dscore(q, k, Vh + (size_t)n * D, dz, L[m], c[m], dLh ? dLh[m] : 0.0, D, s, &p);
+                    for (int d = 0; d < D; ++d) dq[d] += s * ds * k[d];
+                }
+            }
+        }
+    free(L); free(c); free(Zh);
+    return 0;
+}
+
+/* Decoder token statistics of one head: shift cmax_n, sum l_n and delta_n. */
+static int dec_stats(const double* Qh, const double* Kh, const double* Zh, const double* dYh, int N, int M, int D,
+                     double s, double* cmax, double* l, double* delta) {
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* u = (double*)malloc(sizeof(double) * (size_t)M);
+        double* y = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!u || !y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int n = 0; n < N; ++n) {
+                const double* k = Kh + (size_t)n * D;
+                decode_row(k, Qh, Zh, M, D, s, y, u);
+                double c = -INFINITY, sum = 0.0;
+                for (int m = 0; m < M; ++m) c = u[m] > c ? u[m] : c;
+                for (int m = 0; m < M; ++m) sum += exp(u[m] - c);
+                cmax[n] = c;
+                l[n] = sum;
+                delta[n] = dot(dYh + (size_t)n * D, y, D);
+            }
+        }
+        free(u); free(y);
+    }
+    return bad;
+}
+
+/* dU_nm of the decoder (see above); W = exp(U - c) / l. */
+static double dec_dscore(const double* k, const double* q, const double* z, const double* dy, double c, double l,
+                         double delta, int D, double s, double* w) {
+    *w = exp(s * dot(k, q, D) - c) / l;
+    return *w * (dot(dy, z, D) - delta);
+}
+
+int oracle_decode_backward(const double* Q, int q_batched, const double* K, const double* Z, const double* dY,
+                           int B, int H, int N, int M, int D, double scale, double* dQ, double* dK, double* dZ) {
+    if (B <= 0 || H <= 0 || N < 0 || M <= 0 || D <= 0) return 1;
+    const double s = pick_scale(scale, D);
+    const size_t nq = (size_t)(q_batched ? B : 1) * H * M * D;
+    memset(dQ, 0, sizeof(double) * nq);
+    memset(dZ, 0, sizeof(double) * (size_t)B * H * M * D);
+    if (N == 0) return 0;
+    double* cmax = (double*)malloc(sizeof(double) * (size_t)N);
+    double* l = (double*)malloc(sizeof(double) * (size_t)N);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!cmax || !l || !delta) { free(cmax); free(l); free(delta); return 2; }
+    int bad = 0;
+    for (int b = 0; b < B && !bad; ++b)
+        for (int h = 0; h < H && !bad; ++h) {
+            const size_t bh = (size_t)b * H + h;
+            const double* Qh = q_ptr(Q, q_batched, b, h, H, M, D);
+            const double* Kh = K + bh * N * D;
+            const double* Zh = Z + bh * M * D;
+            const double* dYh = dY + bh * N * D;
+            if (dec_stats(Qh, Kh, Zh, dYh, N, M, D, s, cmax, l, delta)) { bad = 2; break; }
+            /* per token: dK_n = s sum_m dU_nm q_m */
+#pragma omp parallel for schedule(static)
+            for (int n = 0; n < N; ++n) {
+                const double* k = Kh + (size_t)n * D;
+                const double* dy = dYh + (size_t)n * D;
+                double* dk = dK + (bh * N + n) * D;
+                for (int d = 0; d < D; ++d) dk[d] = 0.0;
+                for (int m = 0; m < M; ++m) {
+                    double w;
+                    const double* q = Qh + (size_t)m * D;
+                    const double du = dec_dscore(k, q, Zh + (size_t)m * D, dy, cmax[n], l[n], delta[n], D, s, &w);
+                    for (int d = 0; d < D; ++d) dk[d] += s * du * q[d];
+                }
+            }
+            /* per latent: dZ_m = sum_n W_nm dY_n, dQ_m += s sum_n dU_nm k_n */
+            double* dQh = dQ + (q_batched ? bh : (size_t)h) * M * D;
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int m = 0; m < M; ++m) {
+                const double* q = Qh + (size_t)m * D;
+                const double* z = Zh + (size_t)m * D;
+                double* dq = dQh + (size_t)m * D;
+                double* dz = dZ + (bh * M + m) * D;
+                for (int n = 0; n < N; ++n) {
+                    double w;
+                    const double* k = Kh + (size_t)n * D;
+                    const double* dy = dYh + (size_t)n * D;
+                    const double du = dec_dscore(k, q, z, dy, cmax[n], l[n], delta[n], D, s, &w);
+                    for (int d = 0; d < D; ++d) {
+                        dz[d] += w * dy[d];
+                        dq[d] += s * du * k[d];
+                    }
+                }
+            }
+        }
+    free(cmax); free(l); free(delta);
+    return bad;
+}

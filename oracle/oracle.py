@@ -22,7 +22,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
-           "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed"]
+           "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed", "encode_backward",
+           "decode_backward", "flare_backward"]
 
 
 def build(force: bool = True) -> str:
@@ -55,8 +56,11 @@ def lib():
                                               dp, dp, dp, dp]
         L.oracle_materialize.argtypes = [dp, dp, i, i, i, ctypes.c_double, dp, dp]
         L.oracle_threads.argtypes = [i]
+        L.oracle_encode_backward.argtypes = [dp, i, dp, dp, dp, dp, i, i, i, i, i, ctypes.c_double, dp, dp, dp]
+        L.oracle_decode_backward.argtypes = [dp, i, dp, dp, dp, i, i, i, i, i, ctypes.c_double, dp, dp, dp]
         for fn in (L.oracle_encode, L.oracle_decode_rows, L.oracle_flare_forward, L.oracle_pp_queries,
-                   L.oracle_flare_pp_forward, L.oracle_materialize, L.oracle_threads):
+                   L.oracle_flare_pp_forward, L.oracle_materialize, L.oracle_threads, L.oracle_encode_backward,
+                   L.oracle_decode_backward):
             fn.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -218,3 +222,54 @@ def materialize(Q, K, scale: float = 0.0):
     if rc:
         raise RuntimeError(f"oracle_materialize failed ({rc})")
     return Wenc, Wdec
+
+
+def encode_backward(Q, K, V, dZ, dL=None, scale: float = 0.0):
+    """Reverse mode of the encoder (Z, L) = Enc(Q, K, V): FLARE++ paper, App.
+    B.5, local backward with one shard.  Given the cotangents dZ [B,H,M,D] and
+    dL [B,H,M] (None = 0) returns (dQ, dK, dV); dQ has Q's layout (summed
+    over the batch when Q is [H,M,D])."""
+    K, V, Q, dZ = _f64(K), _f64(V), _f64(Q), _f64(dZ)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    dL = None if dL is None else _f64(dL)
+    if V.shape != K.shape or dZ.shape != (B, H, M, D) or (dL is not None and dL.shape != (B, H, M)):
+        raise ValueError("shape mismatch")
+    dQ = np.empty(Q.shape)
+    dK = np.empty(K.shape)
+    dV = np.empty(V.shape)
+    rc = lib().oracle_encode_backward(_p(Q), _q_batched(Q, B), _p(K), _p(V), _p(dZ), _p(dL), B, H, N, M, D,
+                                      float(scale), _p(dQ), _p(dK), _p(dV))
+    if rc:
+        raise RuntimeError(f"oracle_encode_backward failed ({rc})")
+    return dQ, dK, dV
+
+
+def decode_backward(Q, K, Z, dY, scale: float = 0.0):
+    """Reverse mode of the decoder Y = SDPA(K, Q, Z) (softmax over the latents,
+    App. A.1): given dY [B,H,N,D] returns (dQ, dK, dZ)."""
+    K, Q, Z, dY = _f64(K), _f64(Q), _f64(Z), _f64(dY)
+    B, H, N, D = K.shape
+    M = Q.shape[-2]
+    if dY.shape != K.shape or Z.shape != (B, H, M, D):
+        raise ValueError("shape mismatch")
+    dQ = np.empty(Q.shape)
+    dK = np.empty(K.shape)
+    dZ = np.empty(Z.shape)
+    rc = lib().oracle_decode_backward(_p(Q), _q_batched(Q, B), _p(K), _p(Z), _p(dY), B, H, N, M, D, float(scale),
+                                      _p(dQ), _p(dK), _p(dZ))
+    if rc:
+        raise RuntimeError(f"oracle_decode_backward failed ({rc})")
+    return dQ, dK, dZ
+
+
+def flare_backward(Q, K, V, dY, scale: float = 0.0, return_dZ: bool = False):
+    """Reverse mode of the FLARE pair Y = Dec(Q, K, Enc(Q, K, V)): the decoder's
+    backward gives dZ and its shares of dQ and dK; the encoder's backward
+    (App. B.5, dL = 0) takes that dZ and gives dV and the other shares.
+    Returns (dQ, dK, dV), plus dZ when ``return_dZ``."""
+    _, Z, _ = flare_forward(Q, K, V, scale)
+    dQd, dKd, dZ = decode_backward(Q, K, Z, dY, scale)
+    dQe, dKe, dV = encode_backward(Q, K, V, dZ, None, scale)
+    out = (dQd + dQe, dKd + dKe, dV)
+    return out + (dZ,) if return_dZ else out
