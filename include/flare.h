@@ -73,6 +73,8 @@ extern "C" {
 #define FLARE_OP_DECODE 1
 #define FLARE_OP_FORWARD 2
 #define FLARE_OP_PP_FORWARD 3
+#define FLARE_OP_BACKWARD 4
+#define FLARE_OP_ENCODE_BACKWARD 5
 
 /* Scratch bytes that `op` needs for this problem (0 when none); returns 0 for
  * arguments the op would reject.  Depends only on its arguments and on the
@@ -149,6 +151,41 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
                           int B, int H, int N, int M, int D, int dtype, float scale, int norm_flags,
                           const float* alpha_qs, const float* alpha_ks, const float* alpha_k, float eps,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the FLARE pair Y = SDPA(K, Q, SDPA(Q, K, V)) (reverse mode;
+ * FLARE++ paper, App. B.5 "Local backward" for the encoder with one shard,
+ * and the derivative of the decoder's softmax over the latents, App. A.1).
+ * Given the output cotangent dY, with S = s Q K^T:
+ *   decoder  W = softmax over latents,  delta_n = dY_n . Y_n,
+ *            dS_dec = W o (Z dY^T - delta),  dZ = W dY
+ *   encoder  P = softmax over tokens,  c_m = dZ_m . Z_m,
+ *            dS_enc = P o (dZ V^T - c),  dV = P^T dZ
+ *   dK = s (dS_dec + dS_enc)^T Q,  dQ = s (dS_dec + dS_enc) K.
+ * Inputs: Q, K, V as for flare_forward (dtype FLARE_BF16 only, else
+ * FLARE_ERR_UNSUPPORTED); Z [B,H,M,D] f32 and L [B,H,M] f32 are the
+ * latents and log-normalisers flare_forward returned for the same Q, K, V
+ * (the scores are recomputed, never stored); dY [B,H,N,D] bf16.
+ * Outputs: dQ f32 in Q's layout ([H,M,D] shared queries receive the sum
+ * over the batch); dK, dV [B,H,N,D] bf16; dZ_out [B,H,M,D] f32 or NULL.
+ * All device pointers 16-byte aligned; ws of
+ * flare_workspace_size(FLARE_OP_BACKWARD, ...) bytes is required.  The result
+ * is deterministic (fixed split plan, fixed summation order). */
+int flare_backward(const void* Q, int q_batched, const void* K, const void* V, const float* Z, const float* L,
+                   const void* dY, float* dQ, void* dK, void* dV, float* dZ_out, int B, int H, int N, int M,
+                   int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the encoder alone (App. B.5 with one shard): given the
+ * cotangents dZ [B,H,M,D] f32 and dL [B,H,M] f32 (NULL = 0) of its outputs
+ * (Z, L) = flare_encode(Q, K, V),
+ *   P = softmax over tokens,  c_m = dZ_m . Z_m,
+ *   dS = P o (dZ V^T - c + dL),  dV = P^T dZ,  dK = s dS^T Q,  dQ = s dS K.
+ * Z and L are the encoder's own outputs for the same inputs.  Layouts,
+ * dtype and alignment as flare_backward; ws of
+ * flare_workspace_size(FLARE_OP_ENCODE_BACKWARD, ...) bytes. */
+int flare_encode_backward(const void* Q, int q_batched, const void* K, const void* V, const float* Z,
+                          const float* L, const float* dZ, const float* dL, float* dQ, void* dK, void* dV,
+                          int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* flare_status_string(int status);

@@ -1,0 +1,728 @@
+// backward.h -- reverse mode of the FLARE encoder / decoder pair on gfx950
+// (bf16 inputs, float32 accumulation).  Included once, by flare.hip, after
+// its device helpers and host planning; it reopens the same unnamed
+// namespace.
+//
+// What is computed (FLARE++ paper, App. B.5 "Local backward" with one shard,
+// and the derivative of the decoder's softmax over the latents, App. A.1),
+// per (b, h), with S = s Q K^T [M x N]:
+//   encoder  Z = P V,  P = softmax over tokens,  L = log-normaliser
+//            dS_enc = P o (dZ V^T - c + dL),  c_m = dZ_m . Z_m
+//            dV = P^T dZ,  dK += s dS_enc^T Q,  dQ += s dS_enc K
+//   decoder  Y = W^T Z with W[m,n] = softmax over latents of S[:, n]
+//            dS_dec = W o (Z dY^T - delta),  delta_n = dY_n . Y_n
+//            dZ = W dY,  dK += s dS_dec^T Q,  dQ += s dS_dec K
+// FLARE's backward runs the decoder's part first (it produces dZ) and then
+// the encoder's with that dZ (dL = 0).
+//
+// Scores are in log2 units from the forward's own bf16 operands (Q s log2 e
+// rounded, K), so P = 2^(S2 - L log2 e) with the forward's L and
+// W = 2^(S2 - lse2_n) with the per-token log2-normaliser of a statistics
+// pass: every exponential has its exact shift and lies in [0, 1].
+//
+// Conditioning.  The latents Z of a long sequence share a large common part
+// (each is an average over many tokens), so dY . Z_m - delta_n is a small
+// difference of large terms.  The decoder side works on Zc = Z - mean_m Z,
+// which changes nothing exactly (the weights of a token sum to one, so
+// delta shifts by dY . mean Z as every dY . Z_m does) but makes the bf16
+// rounding of the latents relative to their spread.  The encoder side takes
+// c_m from the bf16-rounded dZ_m that its score products use, so
+// dZ_m . V_n - c_m is the product of that dZ_m with V_n - Z_m.
+//
+// Launches (one call, one stream):
+//   center      Zc = Z - mean over latents                      [B,H,M,D] f32
+//   statistics  decode_kernel in statistics mode on Zc: per token
+//               (lse2_n, dY_n . (Y_n - mean Z))                 [B,H,N] float2
+//   col pass    (decode side) per split of the tokens, lanes = latents:
+//               partial sums over tokens of dZ and dQ_dec
+//   sum         dZ = sum of splits; c_m from the bf16-rounded dZ_m
+//   col pass    (encoder side) partial dQ_enc added onto the decode partials
+//   sum         dQ = s * sum of splits (and of the batch for shared queries)
+//   row pass    lanes = tokens: dK (both sides) and dV
+// The col passes reuse the encode's split plan and LDS tiles (K and the
+// second token tensor, DMA-filled, double-buffered, transposing reads for
+// the token-contracted products); the row pass reuses the decode's layout
+// (the latent-side operands of one head resident in LDS).
+namespace {
+
+// ----------------------------------------------------------------------------
+// Center the latents of every (b, h): Zc = Z - mean over latents.
+// One workgroup per (b, h).
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) center_kernel(const float* Z, float* Zc, int M, int D) {
+  __shared__ float red[kThreads];
+  __shared__ float mean[32];
+  const int t = threadIdx.x;
+  const size_t base = (size_t)blockIdx.x * M * D;
+  const int RG = kThreads / D;  // row groups
+  const int d = t % D;
+  float sum = 0.f;
+  for (int m = t / D; m < M; m += RG) sum += Z[base + (size_t)m * D + d];
+  red[t] = sum;
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+    for (int k = 0; k < RG; ++k) s += red[t + k * D];
+    mean[t] = s / (float)M;
+  }
+  __syncthreads();
+  for (int e = t; e < M * D; e += kThreads) Zc[base + e] = Z[base + e] - mean[e % D];
+}
+
+// ----------------------------------------------------------------------------
+// Col pass: lanes own latents (as in the encode), token tiles in LDS.
+//   decode side:  per token block, Sw = S2 - lse2 (MFMA accumulator input),
+//                 W = 2^Sw, E = Zc dY^T - delta, dS = W o E,
+//                 dZ^T += dY^T W^T,  dQ^T += K^T dS^T
+//   encoder side: Sp = S2 - L2, P = 2^Sp, E = dZ V^T - c, dS = P o E,
+//                 dQ^T += K^T dS^T
+// The partial dQ sums are in units of the natural-log scores without the
+// factor s (applied by the sum).
+// ----------------------------------------------------------------------------
+struct ColArgs {
+  const bf16* Q;        // [H,M,D] or [B,H,M,D]
+  const bf16* K;        // [B,H,N,D]
+  const bf16* X;        // decode side: dY; encoder side: V   [B,H,N,D]
+  const float* lat;     // decode side: Zc; encoder side: dZ  [B,H,M,D]
+  const float2* stats;  // decode side: per token (lse2, delta)
+  const float* L;       // encoder side: the forward's log-normaliser [B,H,M]
+  const float* c;       // encoder side: c_m [B,H,M]
+  float* part_dz;       // decode side: [BH][pmax][M][D]
+  float* part_dq;       // [BH][pmax][M][D]
+  long long total;      // BH * N
+  int q_batched, H, N, M, nwg, pmax, accumulate;
+  float qscale;         // s * log2(e)
+};
+
+template <int OFF = 0> __device__ inline bf16x4 tr_read_at(unsigned addr) { return tr_read<OFF>(addr); }
+
+// PV A operand (a transposed token tile, 32 token columns) by transposing reads.
+__device__ inline PVOp<bf16> tr_operand(const unsigned (&va)[4], unsigned off, int lane, int D) {
+  PVOp<bf16> o;
+  const bf16x4 r0 = tr_read_at(va[0] + off), r1 = tr_read_at(va[1] + off);
+  const bf16x4 r2 = tr_read_at(va[2] + off), r3 = tr_read_at(va[3] + off);
+  o.a0 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+  o.a1 = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);
+  pv_wait(o, lane, D);
+  return o;
+}
+
+__device__ inline void pack16(const f32x16& p, bf16x8& b0, bf16x8& b1) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) { b0[r] = (bf16)p[r]; b1[r] = (bf16)p[8 + r]; }
+}
+
+__device__ inline f32x16 splat16(float v) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = v;
+  return r;
+}
+
+template <int D, int NW, int WN, bool DEC>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) bwd_col_kernel(ColArgs a) {
+  constexpr int ROWS = dma_rows<NW>();
+  constexpr int TE = ROWS * D;                       // elements per tile
+  constexpr unsigned BUFB = 2 * TE * sizeof(bf16);   // bytes between the two buffers
+  constexpr int G = NW / WN;
+  static_assert(NW * 64 >= ROWS, "one statistics row per thread");
+  __shared__ __align__(16) bf16 tiles[4 * TE];       // [buffer][K, X][TE]
+  __shared__ __align__(16) float2 st[DEC ? 2 * ROWS : 2];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 31, g = lane >> 5;
+  const int mg = wave % G, ng = wave / G;
+  const int N = a.N, M = a.M;
+  bf16* const kt0 = tiles;
+  bf16* const xt0 = tiles + TE;
+
+  const TileOffs<D> to = tile_offsets<D>(lane);
+  unsigned ka[D / 16], kx[D / 16], va[4], vx[4];
+  {
+    const unsigned bk = lds_addr(kt0), bx = lds_addr(xt0);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) { ka[s] = bk + to.kq[s]; kx[s] = bx + to.kq[s]; }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { va[k] = bk + to.vq[k]; vx[k] = bx + to.vq[k]; }
+  }
+
+  long long x = piece_start(blockIdx.x, a.total, a.nwg);
+  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  while (x < xe) {
+    const int bh = (int)(x / N);
+    const long long hb = (long long)bh * N;
+    const int n_lo = (int)(x - hb);
+    const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
+    const int h = bh % a.H;
+    const int slot = (blockIdx.x - piece_of(hb, a.total, a.nwg)) * WN + ng;
+
+    // this wave's latent (B operand column): scaled query and latent-side row
+    const int m = mg * 32 + li;
+    const int mc = m < M ? m : M - 1;
+    QKOp<bf16, D> qop, lop;
+    load_op_scaled<D>(qop, a.Q + ((size_t)(a.q_batched ? bh : h) * M + mc) * D, g, a.qscale);
+    load_op_scaled<D>(lop, a.lat + ((size_t)bh * M + mc) * D, g, 1.f);
+    if (m >= M) { zero_op<D>(qop); zero_op<D>(lop); }
+    f32x16 cp = {}, cg = {};
+    if constexpr (!DEC) {
+      // latents past M: shift +inf, so their weights are exactly zero
+      cp = splat16(m < M ? -a.L[(size_t)bh * M + m] * kLog2e : -INFINITY);
+      cg = splat16(m < M ? -a.c[(size_t)bh * M + m] : 0.f);
+    }
+    f32x16 accq = {}, accz = {};
+
+    const bf16* Kh = a.K + (size_t)bh * N * D;
+    const bf16* Xh = a.X + (size_t)bh * N * D;
+    const float2* Sh = DEC ? a.stats + (size_t)bh * N : nullptr;
+    __syncthreads();  // the previous piece is done with the tiles
+    dma_tile<D, NW>(kt0, Kh, n_lo, n_hi, wave, lane);
+    dma_tile<D, NW>(xt0, Xh, n_lo, n_hi, wave, lane);
+    if constexpr (DEC) {
+      if ((int)threadIdx.x < ROWS) {
+        const int r = n_lo + (int)threadIdx.x;
+        st[threadIdx.x] = Sh[r < n_hi ? r : n_hi - 1];
+      }
+    }
+    wait_dma();
+    __syncthreads();
+    int buf = 0;
+    for (int t0 = n_lo; t0 < n_hi; t0 += ROWS) {
+      const int tn = t0 + ROWS;
+      float2 snext = make_float2(0.f, 0.f);
+      if (tn < n_hi) {
+        dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE, Kh, tn, n_hi, wave, lane);
+        dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE + TE, Xh, tn, n_hi, wave, lane);
+        if constexpr (DEC) {
+          if ((int)threadIdx.x < ROWS) {
+            const int r = tn + (int)threadIdx.x;
+            snext = Sh[r < n_hi ? r : n_hi - 1];
+          }
+        }
+      }
+      for (int nb = ng; nb < ROWS / 32; nb += WN) {
+        const int row0 = t0 + 32 * nb;
+        if (row0 >= n_hi) break;
+        const unsigned off = buf * BUFB + nb * 64 * D;
+        QKOp<bf16, D> kop, xop;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          kop.v[s] = lds_load<bf16x8>(ka[s] + off);
+          xop.v[s] = lds_load<bf16x8>(kx[s] + off);
+        }
+        if constexpr (DEC) {
+          // the rows' (lse2, delta): rows acc_row(r, g) come in four runs of four
+          const float2* sr = st + buf * ROWS + 32 * nb + 4 * g;
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(sr + 8 * c4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sr + 8 * c4 + 2);
+            cp[4 * c4] = -u[0]; cg[4 * c4] = -u[1]; cp[4 * c4 + 1] = -u[2]; cg[4 * c4 + 1] = -u[3];
+            cp[4 * c4 + 2] = -v[0]; cg[4 * c4 + 2] = -v[1]; cp[4 * c4 + 3] = -v[2]; cg[4 * c4 + 3] = -v[3];
+          }
+        }
+        f32x16 s = qk_mma<D>(kop, qop, cp);
+        const f32x16 e = qk_mma<D>(xop, lop, cg);
+        if (row0 + 32 > n_hi) mask_rows(s, n_hi - row0, g);
+        f32x16 p, ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(s[r]);
+          ds[r] = p[r] * e[r];
+        }
+        bf16x8 d0, d1;
+        pack16(ds, d0, d1);
+        accq = pv_mma(tr_operand(va, off, lane, D), d0, d1, accq);
+        if constexpr (DEC) {
+          bf16x8 w0, w1;
+          pack16(p, w0, w1);
+          accz = pv_mma(tr_operand(vx, off, lane, D), w0, w1, accz);
+        }
+      }
+      if constexpr (DEC) {
+        if (tn < n_hi && (int)threadIdx.x < ROWS) st[(buf ^ 1) * ROWS + threadIdx.x] = snext;
+      }
+      wait_dma();
+      __syncthreads();
+      buf ^= 1;
+    }
+    if (m < M) {
+      const size_t pi = ((size_t)bh * a.pmax + slot) * M + m;
+      float* dq = a.part_dq + pi * D;
+      float* dz = DEC ? a.part_dz + pi * D : nullptr;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        if (8 * c4 + 4 * g < D) {
+          f32x4 v = {accq[4 * c4], accq[4 * c4 + 1], accq[4 * c4 + 2], accq[4 * c4 + 3]};
+          if (a.accumulate) v = v + *reinterpret_cast<const f32x4*>(dq + 8 * c4 + 4 * g);
+          *reinterpret_cast<f32x4*>(dq + 8 * c4 + 4 * g) = v;
+          if constexpr (DEC) {
+            const f32x4 w = {accz[4 * c4], accz[4 * c4 + 1], accz[4 * c4 + 2], accz[4 * c4 + 3]};
+            *reinterpret_cast<f32x4*>(dz + 8 * c4 + 4 * g) = w;
+          }
+        }
+      }
+    }
+    x = hb + n_hi;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Sums over the splits, in ascending split order.
+// ----------------------------------------------------------------------------
+struct SumArgs {
+  const float* part;    // [BH][pmax][M][D]
+  long long total;      // BH * N (piece plan of the col passes)
+  int nwg, WN, pmax, B, H, N, M, D;
+  // dZ mode: dZ = sum (or dz_in when given), c_m = bf16(dZ_m) . Z_m - dL_m
+  const float* dz_in;   // [B,H,M,D] given cotangent of Z, or null
+  const float* Z;       // [B,H,M,D]
+  const float* dL;      // [B,H,M] or null
+  float* dz;            // [B,H,M,D]
+  float* c;             // [B,H,M]
+  float* dz_out;        // [B,H,M,D] copy for the caller, or null
+  // dQ mode: dQ = s * sum (over the batch too when Q is shared)
+  float* dq;
+  int q_batched;
+  float s;
+};
+
+__device__ inline int split_count(const SumArgs& a, int bh) {
+  if (a.N == 0) return 0;
+  const long long hb = (long long)bh * a.N;
+  return (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
+}
+
+__device__ inline float split_sum(const SumArgs& a, int bh, int md) {
+  const int cnt = split_count(a, bh);
+  const float* p = a.part + (size_t)bh * a.pmax * a.M * a.D + md;
+  const size_t stride = (size_t)a.M * a.D;
+  float s = 0.f;
+  for (int i = 0; i < cnt; ++i) s += p[i * stride];
+  return s;
+}
+
+// One thread per (b, h, m, d); the D threads of a latent are consecutive
+// lanes of one wave (D divides 64 and B H M D is a multiple of D).
+__global__ void __launch_bounds__(kThreads) sum_dz_kernel(SumArgs a) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long n = (long long)a.B * a.H * a.M * a.D;
+  const bool on = i < n;
+  const long long ic = on ? i : 0;
+  const int bh = (int)(ic / ((long long)a.M * a.D));
+  const int md = (int)(ic % ((long long)a.M * a.D));
+  const float v = a.dz_in ? a.dz_in[ic] : split_sum(a, bh, md);
+  float prod = (float)(bf16)v * a.Z[ic];
+  for (int o = 1; o < a.D; o <<= 1) prod += __shfl_xor(prod, o);
+  if (on) {
+    a.dz[i] = v;
+    if (a.dz_out) a.dz_out[i] = v;
+    if (md % a.D == 0) {
+      const long long row = ic / a.D;
+      a.c[row] = prod - (a.dL ? a.dL[row] : 0.f);
+    }
+  }
+}
+
+// One thread per (head of Q, m, d).
+__global__ void __launch_bounds__(kThreads) sum_dq_kernel(SumArgs a) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const int QH = a.q_batched ? a.B * a.H : a.H;
+  if (i >= (long long)QH * a.M * a.D) return;
+  const int hq = (int)(i / ((long long)a.M * a.D));
+  const int md = (int)(i % ((long long)a.M * a.D));
+  float s = 0.f;
+  if (a.q_batched) {
+    s = split_sum(a, hq, md);
+  } else {
+    for (int b = 0; b < a.B; ++b) s += split_sum(a, b * a.H + hq, md);
+  }
+  a.dq[i] = a.s * s;
+}
+
+// ----------------------------------------------------------------------------
+// Row pass: lanes own tokens (as in the decode); the latent-side operands of
+// one head are resident in LDS.  Per latent block of 32:
+//   decode side:  W = 2^(S2 - lse2_n), E = Zc dY_n - delta_n, dS = W o E
+//   encoder side: P = 2^(S2 - L2_m),   E = dZ V_n - c_m,      dS += P o E,
+//                 dV^T += dZ^T P
+//   dK^T += (Q s log2 e)^T dS          (dK = that / log2 e)
+// ----------------------------------------------------------------------------
+struct RowArgs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;        // encoder side
+  const bf16* dY;       // decode side
+  const float* Zc;      // decode side
+  const float2* stats;  // decode side
+  const float* dZ;      // encoder side
+  const float* L;       // encoder side
+  const float* c;       // encoder side
+  bf16* dK;
+  bf16* dV;             // encoder side
+  long long total;
+  int q_batched, H, N, M, MB, nwg;
+  float qscale;
+};
+
+template <int D> struct RowLds {
+  static constexpr int RST = D + 8;  // row stride (bf16)
+  __host__ __device__ static int tst(int MB) { return MB * 32 + 4; }  // transposed stride
+  // qs, zr, dzr rows; qt, dzt transposed; L2 and c per latent (float)
+  static size_t bytes(int MB) {
+    return (size_t)(3 * MB * 32 * RST + 2 * D * tst(MB)) * sizeof(bf16) + (size_t)2 * MB * 32 * sizeof(float);
+  }
+};
+
+template <int D, bool TAIL, bool DEC, bool ENC>
+__global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
+  using RL = RowLds<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
+  const int tst = RL::tst(MB);
+  bf16* qs = reinterpret_cast<bf16*>(smem);
+  bf16* zr = qs + (size_t)Mp * RL::RST;
+  bf16* dzr = zr + (size_t)Mp * RL::RST;
+  bf16* qt = dzr + (size_t)Mp * RL::RST;
+  bf16* dzt = qt + (size_t)D * tst;
+  float* l2 = reinterpret_cast<float*>(dzt + (size_t)D * tst);
+  float* cc = l2 + Mp;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 31, g = lane >> 5;
+  __builtin_assume(MB >= 1);
+
+  long long x = piece_start(blockIdx.x, a.total, a.nwg);
+  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  while (x < xe) {
+    const int bh = (int)(x / N);
+    const long long hb = (long long)bh * N;
+    const int n_lo = (int)(x - hb);
+    const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
+    const int h = bh % a.H;
+
+    __syncthreads();  // the previous piece is done with the staged head
+    {
+      const bf16* Qh = a.Q + (size_t)(a.q_batched ? bh : h) * M * D;
+      for (int e = threadIdx.x; e < Mp * D; e += kThreads) {
+        const int m = e / D, d = e % D;
+        const bool in = m < M;
+        const bf16 q = (bf16)(in ? (float)Qh[(size_t)m * D + d] * a.qscale : 0.f);
+        qs[m * RL::RST + d] = q;
+        qt[d * tst + m] = q;
+        if constexpr (DEC) zr[m * RL::RST + d] = (bf16)(in ? a.Zc[((size_t)bh * M + m) * D + d] : 0.f);
+        if constexpr (ENC) {
+          const bf16 z = (bf16)(in ? a.dZ[((size_t)bh * M + m) * D + d] : 0.f);
+          dzr[m * RL::RST + d] = z;
+          dzt[d * tst + m] = z;
+        }
+      }
+      if constexpr (ENC) {
+        for (int m = threadIdx.x; m < Mp; m += kThreads) {
+          // latents past M: shift +inf, zero weight
+          l2[m] = m < M ? -a.L[(size_t)bh * M + m] * kLog2e : -INFINITY;
+          cc[m] = m < M ? -a.c[(size_t)bh * M + m] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    const bf16* Kh = a.K + (size_t)bh * N * D;
+    for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += kDecGroup) {
+      // lanes past the piece recompute its last token and store the same values there
+      const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
+      QKOp<bf16, D> kop, yop, vop;
+      load_op<D>(kop, Kh + (size_t)n * D, g);
+      f32x16 cw = {}, cd = {};
+      if constexpr (DEC) {
+        load_op<D>(yop, a.dY + ((size_t)bh * N + n) * D, g);
+        const float2 sn = a.stats[(size_t)bh * N + n];
+        cw = splat16(-sn.x);
+        cd = splat16(-sn.y);
+      }
+      if constexpr (ENC) load_op<D>(vop, a.V + ((size_t)bh * N + n) * D, g);
+      f32x16 acck = {}, accv = {};
+      for (int mb = 0; mb < MB; ++mb) {
+        QKOp<bf16, D> qop;
+        load_op<D>(qop, qs + (mb * 32 + li) * RL::RST, g);
+        f32x16 ds = {};
+        if constexpr (DEC) {
+          QKOp<bf16, D> zop;
+          load_op<D>(zop, zr + (mb * 32 + li) * RL::RST, g);
+          f32x16 s = qk_mma<D>(qop, kop, cw);
+          const f32x16 e = qk_mma<D>(zop, yop, cd);
+          if (TAIL && mb == MB - 1) mask_rows(s, M - mb * 32, g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(s[r]) * e[r];
+        }
+        if constexpr (ENC) {
+          QKOp<bf16, D> zop;
+          load_op<D>(zop, dzr + (mb * 32 + li) * RL::RST, g);
+          f32x16 cp, cg;
+          const float* lr = l2 + mb * 32 + 4 * g;
+          const float* cr = cc + mb * 32 + 4 * g;
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(lr + 8 * c4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(cr + 8 * c4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { cp[4 * c4 + i] = u[i]; cg[4 * c4 + i] = v[i]; }
+          }
+          const f32x16 s = qk_mma<D>(qop, kop, cp);
+          const f32x16 e = qk_mma<D>(zop, vop, cg);
+          f32x16 p;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            p[r] = fast_exp2(s[r]);
+            ds[r] += p[r] * e[r];
+          }
+          PVOp<bf16> zt;
+          if (li < D) load_pv(zt, dzt + li * tst + mb * 32, g);
+          else ones_pv(zt, li, D);
+          bf16x8 p0, p1;
+          pack16(p, p0, p1);
+          accv = pv_mma(zt, p0, p1, accv);
+        }
+        PVOp<bf16> qtop;
+        if (li < D) load_pv(qtop, qt + li * tst + mb * 32, g);
+        else ones_pv(qtop, li, D);
+        bf16x8 d0, d1;
+        pack16(ds, d0, d1);
+        acck = pv_mma(qtop, d0, d1, acck);
+      }
+      constexpr float kInvLog2e = 0.69314718055994531f;
+      bf16* dk = a.dK + ((size_t)bh * N + n) * D;
+      bf16* dv = ENC ? a.dV + ((size_t)bh * N + n) * D : nullptr;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        if (8 * c4 + 4 * g < D) {
+          bf16x4 u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[i] = (bf16)(acck[4 * c4 + i] * kInvLog2e);
+          *reinterpret_cast<bf16x4*>(dk + 8 * c4 + 4 * g) = u;
+          if constexpr (ENC) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)accv[4 * c4 + i];
+            *reinterpret_cast<bf16x4*>(dv + 8 * c4 + 4 * g) = v;
+          }
+        }
+      }
+    }
+    x = hb + n_hi;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+struct BwdLayout {
+  size_t zc = 0, stats = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D) {
+  BwdLayout w;
+  const int BH = B * H;
+  const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  const size_t part = align256((size_t)BH * p.pmax * M * D * sizeof(float));
+  const size_t lat = align256((size_t)BH * M * D * sizeof(float));
+  size_t off = 0;
+  w.part_dq = off; off += part;
+  w.dz = off; off += lat;
+  w.c = off; off += align256((size_t)BH * M * sizeof(float));
+  if (dec) {
+    w.zc = off; off += lat;
+    w.stats = off; off += align256((size_t)BH * N * sizeof(float2));
+    w.part_dz = off; off += part;
+  }
+  w.total = off;
+  return w;
+}
+
+size_t row_lds(int D, int M) {
+  const int MB = (int)cdiv(M, 32);
+  return D == 16 ? RowLds<16>::bytes(MB) : RowLds<32>::bytes(MB);
+}
+
+template <int D, int NW, int WN, bool DEC>
+int launch_col_k(const ColArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_col_kernel<D, NW, WN, DEC>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
+  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+template <int D, bool DEC>
+int launch_col_d(const ColArgs& a, int NW, int WN, hipStream_t st) {
+  if (NW == 8) return launch_col_k<D, 8, 1, DEC>(a, st);
+  if (WN == 4) return launch_col_k<D, 4, 4, DEC>(a, st);
+  if (WN == 2) return launch_col_k<D, 4, 2, DEC>(a, st);
+  return launch_col_k<D, 4, 1, DEC>(a, st);
+}
+
+int launch_col(const ColArgs& a, int D, bool dec, const EncPlan& p, hipStream_t st) {
+  if (dec) return D == 16 ? launch_col_d<16, true>(a, p.NW, p.WN, st) : launch_col_d<32, true>(a, p.NW, p.WN, st);
+  return D == 16 ? launch_col_d<16, false>(a, p.NW, p.WN, st) : launch_col_d<32, false>(a, p.NW, p.WN, st);
+}
+
+template <int D, bool TAIL, bool DEC, bool ENC>
+int launch_row_k(const RowArgs& a, size_t lds, hipStream_t st) {
+  const void* fn = (const void*)bwd_row_kernel<D, TAIL, DEC, ENC>;
+  if (lds > 65536) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return FLARE_ERR_HIP;
+  }
+  hipLaunchKernelGGL((bwd_row_kernel<D, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+template <int D, bool DEC, bool ENC>
+int launch_row_t(const RowArgs& a, size_t lds, hipStream_t st) {
+  return (a.M & 31) ? launch_row_k<D, true, DEC, ENC>(a, lds, st) : launch_row_k<D, false, DEC, ENC>(a, lds, st);
+}
+
+int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, hipStream_t st) {
+  const size_t lds = row_lds(D, a.M);
+  if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  // LDS-resident workgroups per compute unit (160 KB of LDS each)
+  const long long per_cu = lds <= 80 * 1024 ? 2 : 1;
+  const long long want = (long long)dev.cus * per_cu;
+  const long long maxw = cdiv(a.total, 32);
+  a.nwg = (int)(want < maxw ? want : maxw);
+  if (dec && enc) return D == 16 ? launch_row_t<16, true, true>(a, lds, st) : launch_row_t<32, true, true>(a, lds, st);
+  if (enc) return D == 16 ? launch_row_t<16, false, true>(a, lds, st) : launch_row_t<32, false, true>(a, lds, st);
+  return D == 16 ? launch_row_t<16, true, false>(a, lds, st) : launch_row_t<32, true, false>(a, lds, st);
+}
+
+int launch_stats(const Dev& dev, const bf16* Q, int q_batched, const bf16* K, const float* Zc, const bf16* dY,
+                 float2* stats, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
+  DecArgs a{};
+  a.Q = Q; a.K = K; a.Z = Zc; a.Y = nullptr;
+  a.total = (long long)BH * N;
+  a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = 0;
+  a.qscale = qscale;
+  a.qmul = nullptr; a.eps = 0.f;
+  a.dY = dY; a.stats = stats;
+  const long long want = (long long)dev.cus * kDecWgPerCu;
+  const long long maxw = cdiv(a.total, 32);
+  a.nwg = (int)(want < maxw ? want : maxw);
+  const size_t lds = decode_lds(FLARE_BF16, D, M);
+  if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const bool tail = M & 31;
+  if (D == 16)
+    return tail ? launch_decode_k<bf16, bf16, 16, true, false, true>(a, lds, st)
+                : launch_decode_k<bf16, bf16, 16, false, false, true>(a, lds, st);
+  return tail ? launch_decode_k<bf16, bf16, 32, true, false, true>(a, lds, st)
+              : launch_decode_k<bf16, bf16, 32, false, false, true>(a, lds, st);
+}
+
+// The backward of the encoder (enc), of the decoder (dec) or of both (FLARE),
+// one stream.  dZ_in (encoder only): the given cotangent of Z; dL: of L.
+int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, const bf16* K, const bf16* V,
+             const float* Z, const float* L, const bf16* dY, const float* dZ_in, const float* dL, float* dQ,
+             bf16* dK, bf16* dV, float* dZ_out, int B, int H, int N, int M, int D, float scale, char* ws,
+             const BwdLayout& w, hipStream_t st) {
+  const int BH = B * H;
+  const float qs = scale * kLog2e;
+  const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  float* part_dq = (float*)(ws + w.part_dq);
+  float* dz = (float*)(ws + w.dz);
+  float* c = (float*)(ws + w.c);
+  int rc;
+  SumArgs sa{};
+  sa.total = p.total; sa.nwg = p.nwg; sa.WN = p.WN; sa.pmax = p.pmax;
+  sa.B = B; sa.H = H; sa.N = N; sa.M = M; sa.D = D;
+  sa.Z = Z; sa.dL = dL; sa.dz = dz; sa.c = c; sa.dz_out = dZ_out;
+  sa.dq = dQ; sa.q_batched = q_batched; sa.s = scale;
+  const unsigned lat_grid = (unsigned)cdiv((long long)BH * M * D, kThreads);
+  ColArgs ca{};
+  ca.Q = Q; ca.K = K; ca.total = p.total;
+  ca.q_batched = q_batched; ca.H = H; ca.N = N; ca.M = M; ca.nwg = p.nwg; ca.pmax = p.pmax;
+  ca.qscale = qs; ca.part_dq = part_dq;
+  float* zc = dec ? (float*)(ws + w.zc) : nullptr;
+  float2* stats = dec ? (float2*)(ws + w.stats) : nullptr;
+  if (N > 0) {
+    if (dec) {
+      hipLaunchKernelGGL(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
+      if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+      rc = launch_stats(dev, Q, q_batched, K, zc, dY, stats, BH, H, N, M, D, qs, st);
+      if (rc) return rc;
+      ColArgs cd = ca;
+      cd.X = dY; cd.lat = zc; cd.stats = stats; cd.part_dz = (float*)(ws + w.part_dz); cd.accumulate = 0;
+      rc = launch_col(cd, D, true, p, st);
+      if (rc) return rc;
+      sa.part = cd.part_dz;
+    } else {
+      sa.dz_in = dZ_in;
+    }
+  } else {
+    sa.dz_in = dZ_in;  // no tokens: no partials (the split sums are empty)
+  }
+  if (dec || enc) {
+    hipLaunchKernelGGL(sum_dz_kernel, dim3(lat_grid), dim3(kThreads), 0, st, sa);
+    if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  }
+  if (N > 0 && enc) {
+    ColArgs ce = ca;
+    ce.X = V; ce.lat = dz; ce.L = L; ce.c = c; ce.accumulate = dec ? 1 : 0;
+    rc = launch_col(ce, D, false, p, st);
+    if (rc) return rc;
+  }
+  SumArgs sq = sa;
+  sq.part = part_dq;
+  const int QH = q_batched ? BH : H;
+  hipLaunchKernelGGL(sum_dq_kernel, dim3((unsigned)cdiv((long long)QH * M * D, kThreads)), dim3(kThreads), 0, st, sq);
+  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  if (N == 0) return FLARE_OK;
+  RowArgs ra{};
+  ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.stats = stats; ra.dZ = dz; ra.L = L; ra.c = c;
+  ra.dK = dK; ra.dV = dV;
+  ra.total = (long long)BH * N;
+  ra.q_batched = q_batched; ra.H = H; ra.N = N; ra.M = M; ra.MB = (int)cdiv(M, 32);
+  ra.qscale = qs;
+  return launch_row(dev, ra, D, dec, enc, st);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI of the backward
+// ----------------------------------------------------------------------------
+extern "C" {
+
+int flare_backward(const void* Q, int q_batched, const void* K, const void* V, const float* Z, const float* L,
+                   const void* dY, float* dQ, void* dK, void* dV, float* dZ_out, int B, int H, int N, int M, int D,
+                   int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(B, H, N, M, D, dtype, q_batched);
+  if (rc) return rc;
+  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
+  if (!Q || !Z || !L || !dQ || (N > 0 && (!K || !V || !dY || !dK || !dV))) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {Q, K, V, Z, L, dY, dQ, dK, dV, dZ_out, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  if (row_lds(D, M) > dev.lds_max || decode_lds(FLARE_BF16, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const BwdLayout w = bwd_layout(dev, true, B, H, N, M, D);
+  if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+  return backward(dev, true, true, (const bf16*)Q, q_batched, (const bf16*)K, (const bf16*)V, Z, L, (const bf16*)dY,
+                  nullptr, nullptr, dQ, (bf16*)dK, (bf16*)dV, dZ_out, B, H, N, M, D, pick_scale(scale, D),
+                  (char*)ws, w, (hipStream_t)stream);
+}
+
+int flare_encode_backward(const void* Q, int q_batched, const void* K, const void* V, const float* Z, const float* L,
+                          const float* dZ, const float* dL, float* dQ, void* dK, void* dV, int B, int H, int N, int M,
+                          int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(B, H, N, M, D, dtype, q_batched);
+  if (rc) return rc;
+  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
+  if (!Q || !Z || !L || !dZ || !dQ || (N > 0 && (!K || !V || !dK || !dV))) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {Q, K, V, Z, L, dZ, dL, dQ, dK, dV, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  if (row_lds(D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const BwdLayout w = bwd_layout(dev, false, B, H, N, M, D);
+  if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+  return backward(dev, false, true, (const bf16*)Q, q_batched, (const bf16*)K, (const bf16*)V, Z, L, nullptr, dZ,
+                  dL, dQ, (bf16*)dK, (bf16*)dV, nullptr, B, H, N, M, D, pick_scale(scale, D), (char*)ws, w,
+                  (hipStream_t)stream);
+}
+
+}  // extern "C"

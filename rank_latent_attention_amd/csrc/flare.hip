@@ -1035,6 +1035,10 @@ struct DecArgs {
   float qscale;
   const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
   float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
+  // statistics mode (the kernel's ST flag, bf16): instead of Y, per token
+  // (log2 of the weight sum over the latents, dY . Y) into stats [B,H,N]
+  const void* dY;     // [B,H,N,D], type T
+  float2* stats;
 };
 
 template <typename T, int D> struct DecLds {
@@ -1048,9 +1052,13 @@ template <typename T, int D> struct DecLds {
 
 // TAIL: M is not a multiple of 32, so the last latent block has rows past M
 // that must not receive weight (compiled out for whole blocks).  NK: each
-// token's key row is N_0-normalised in registers once per step (bf16).
-template <typename T, typename QT, int D, bool TAIL, bool NK>
+// token's key row is N_0-normalised in registers once per step (bf16).  ST:
+// statistics mode for the backward (bf16): the log-normaliser of every
+// token's softmax over the latents (log2 units, the queries' scaling) and
+// the dot product of the token's output cotangent with its output.
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
+  static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
@@ -1164,7 +1172,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         load_op<D>(knext, Kh + (size_t)(tn < n_hi ? tn : n_hi - 1) * D, g);
       }
       f32x16 acc;
-      float lsum = 0.f, den;
+      float lsum = 0.f, den, shift = 0.f;
       if constexpr (sizeof(T) == 2) {
         // Fast path: unshifted weights exp2(score) (see fast_ok).  The
         // scores of latent block mb + 1 go to the MFMA unit before the
@@ -1224,6 +1232,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
             acc = pv_mma(zop, b0, b1, acc);
           } while (++mc < MB);
           den = pair_sum(lsum);
+          shift = -negs[0];
         }
       } else {
         f32x16 negs = zero16;
@@ -1249,7 +1258,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       // for them to reach memory.
       const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
       const float inv = __builtin_amdgcn_rcpf(den);
-      {
+      if constexpr (ST) {
+        const T* dy = reinterpret_cast<const T*>(a.dY) + ((size_t)bh * N + n) * D;
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (8 * c + 4 * g < D) {
+            const bf16x4 v = *reinterpret_cast<const bf16x4*>(dy + 8 * c + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += acc[4 * c + i] * (float)v[i];
+          }
+        }
+        const float dot = pair_sum(part) * inv;
+        if (g == 0) a.stats[(size_t)bh * N + n] = make_float2(shift + __builtin_amdgcn_logf(den), dot);
+      } else {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1458,14 +1480,14 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename T, typename QT, int D, bool TAIL, bool NK>
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false>
 int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK>;
+  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK, ST>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK, ST>), dim3(a.nwg), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
@@ -1551,6 +1573,8 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
 
 }  // namespace
 
+#include "backward.h"
+
 // ----------------------------------------------------------------------------
 // C ABI
 // ----------------------------------------------------------------------------
@@ -1569,10 +1593,14 @@ const char* flare_status_string(int status) {
 
 size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype) {
   if (check_common(B, H, N, M, D, dtype, 0) != FLARE_OK) return 0;
-  if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_FORWARD) return 0;
+  if (op < FLARE_OP_ENCODE || op > FLARE_OP_ENCODE_BACKWARD) return 0;
   if (op == FLARE_OP_DECODE) return 0;
   Dev dev;
   if (query_dev(dev) != FLARE_OK) return 0;
+  if (op == FLARE_OP_BACKWARD || op == FLARE_OP_ENCODE_BACKWARD) {
+    if (dtype != FLARE_BF16) return 0;
+    return bwd_layout(dev, op == FLARE_OP_BACKWARD, B, H, N, M, D).total;
+  }
   const bool need_z = op == FLARE_OP_FORWARD || op == FLARE_OP_PP_FORWARD;
   const bool need_q = op == FLARE_OP_PP_FORWARD;
   return ws_layout(dev, op, B, H, N, M, D, dtype, need_z, need_q).total;

@@ -23,7 +23,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libflare.so")
 
 F32, BF16 = 0, 1
-OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD = 0, 1, 2, 3
+OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD, OP_BACKWARD, OP_ENCODE_BACKWARD = 0, 1, 2, 3, 4, 5
 #: input normalisation flags of flare_pp_forward_norm (include/flare.h)
 NORM_QS, NORM_KS, NORM_QF, NORM_K = 1, 2, 4, 8
 NORM_FLAREPP = NORM_QS | NORM_KS | NORM_QF | NORM_K  # FLARE++ (Table 2)
@@ -32,7 +32,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
-           "flare_pp_forward_norm", "flare_status_string")
+           "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_status_string")
 
 _lib = None
 
@@ -60,7 +60,10 @@ def load(path: str = LIB_PATH):
     L.flare_pp_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_forward_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, vp, f,
                                         vp, sz, vp]
-    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm):
+    L.flare_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_encode_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm,
+               L.flare_backward, L.flare_encode_backward):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -225,3 +228,53 @@ def flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, norm_flags: int, alpha_qs=
                                       0 if ws is None else ws.numel(), _stream(K.device))
     _check("flare_pp_forward_norm", rc)
     return Y, Q_out, Z, L
+
+
+def _grads(Q, K, dQ, dK, dV):
+    dQ = torch.empty(Q.shape, dtype=torch.float32, device=K.device) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(K) if dV is None else dV
+    return dQ, dK, dV
+
+
+def flare_backward(Q, K, V, Z, L, dY, scale: float = 0.0, dQ=None, dK=None, dV=None, dZ=None, ws=None):
+    """Backward of the FLARE pair (flare_backward in include/flare.h): given
+    the forward's Z [B,H,M,D] and L [B,H,M] (float32) and the output
+    cotangent dY, returns (dQ, dK, dV, dZ); dQ is float32 in Q's layout,
+    dK and dV bf16; dZ only when passed in."""
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or V.dtype != K.dtype or dY.dtype != K.dtype or V.shape != K.shape or dY.shape != K.shape:
+        raise ValueError("Q, K, V, dY must share dtype and K, V, dY shape")
+    if Z.dtype != torch.float32 or tuple(Z.shape) != (B, H, M, D) or L.dtype != torch.float32 or \
+            tuple(L.shape) != (B, H, M):
+        raise ValueError("Z must be float32 [B,H,M,D] and L float32 [B,H,M]")
+    dQ, dK, dV = _grads(Q, K, dQ, dK, dV)
+    _same(K, Q, V, Z, L, dY, dQ, dK, dV, dZ)
+    ws = workspace(OP_BACKWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_backward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQ), _ptr(dK),
+                               _ptr(dV), _ptr(dZ), B, H, N, M, D, dt, float(scale), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_backward", rc)
+    return dQ, dK, dV, dZ
+
+
+def flare_encode_backward(Q, K, V, Z, L, dZ, dL=None, scale: float = 0.0, dQ=None, dK=None, dV=None, ws=None):
+    """Backward of the encoder (flare_encode_backward in include/flare.h):
+    given its outputs Z, L and their cotangents dZ, dL (float32; dL may be
+    None), returns (dQ, dK, dV)."""
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("Q, K, V must share dtype and K, V shape")
+    for t, shp in ((Z, (B, H, M, D)), (L, (B, H, M)), (dZ, (B, H, M, D)), (dL, (B, H, M))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shp):
+            raise ValueError("Z, dZ must be float32 [B,H,M,D]; L, dL float32 [B,H,M]")
+    dQ, dK, dV = _grads(Q, K, dQ, dK, dV)
+    _same(K, Q, V, Z, L, dZ, dL, dQ, dK, dV)
+    ws = workspace(OP_ENCODE_BACKWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
+    rc = load().flare_encode_backward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), _ptr(dZ), _ptr(dL),
+                                      _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, M, D, dt, float(scale), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(K.device))
+    _check("flare_encode_backward", rc)
+    return dQ, dK, dV

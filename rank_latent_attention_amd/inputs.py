@@ -40,7 +40,7 @@ _TAGS = {
     "q": 1, "k": 2, "v": 3, "x": 4, "wk": 5, "wv": 6, "noise": 7, "lift": 8,
     "pts": 9, "omega": 10, "ids": 11, "emb": 12, "qs": 13, "qf": 14, "wks": 15,
     "vs": 16, "wvs": 17, "ks": 18, "qs_mag": 19, "ks_mag": 20, "k_mag": 21, "qf_mag": 22,
-    "alpha_qs": 23, "alpha_ks": 24, "alpha_k": 25,
+    "alpha_qs": 23, "alpha_ks": 24, "alpha_k": 25, "dy": 26, "dz": 27, "dl": 28,
 }
 
 
@@ -283,6 +283,12 @@ def config4(seed=4, B=32, N=4096):
                     Q=to_dtype(Qf, "bf16"), K=to_dtype(K, "bf16"), V=to_dtype(V, "bf16"),
                     pp=True, Qs=to_dtype(Qs, "bf16"), Ks=Ks_b, Vs=Ks_b, Qf=to_dtype(Qf, "bf16"), gate=g,
                     recipe="ids~U{0..255}, X=E[ids], Ks=N0(XWks/sqrt C)=Vs, K=N0(XWk/sqrt C), V=XWv/sqrt C")
+
+
+def cotangent(seed: int, tag: str, shape, dtype: str = "bf16", std: float = 1.0) -> np.ndarray:
+    """Seeded output cotangent for the backward (tags "dy", "dz", "dl"):
+    i.i.d. N(0, std^2), rounded to ``dtype`` ("bf16", or "f32")."""
+    return to_dtype(_gauss(seed, tag, tuple(shape), std), dtype)
 
 
 def sphere_points(seed: int, B: int, N: int) -> np.ndarray:

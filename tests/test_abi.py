@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
-                                           "flare_pp_forward", "flare_pp_forward_norm", "flare_status_string"])
+                                           "flare_pp_forward", "flare_pp_forward_norm", "flare_backward",
+                                           "flare_encode_backward", "flare_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -91,3 +92,28 @@ def ppn(lib, flags=15, eps=1e-6, dt=1, D=16, aqs=None, aks=None, ak=None):
 ])
 def test_pp_forward_norm_rejects_bad_arguments(lib, kw, status):
     assert ppn(lib, **kw) == status
+
+
+def bwd(lib, dt=1, D=16, M=8, Q=FAKE, Z=FAKE, L=FAKE, dY=FAKE, dQ=FAKE, dK=FAKE, dZo=None):
+    return lib.flare_backward(Q, 0, FAKE, FAKE, Z, L, dY, dQ, dK, FAKE, dZo, 1, 1, 8, M, D, dt, 0.0, FAKE, 1 << 30,
+                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=0), 2), (dict(D=24), 2), (dict(M=300), 2),              # float32, head size, latent count
+    (dict(Q=None), 1), (dict(Z=None), 1), (dict(L=None), 1), (dict(dY=None), 1), (dict(dQ=None), 1),
+    (dict(dK=None), 1), (dict(dQ=MISALIGNED), 1), (dict(dZo=MISALIGNED), 1),
+])
+def test_backward_rejects_bad_arguments(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_encode_backward_rejects_bad_arguments(lib):
+    eb = lib.flare_encode_backward
+    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 1, 0.0, FAKE, 1 << 30,
+              None) == 1   # dZ is required
+    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 1, 0.0, FAKE,
+              1 << 30, None) == 1
+    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 0, 0.0, FAKE, 1 << 30,
+              None) == 2
+    assert lib.flare_workspace_size(4, 1, 1, 8, 8, 16, 0) == 0   # the backward is bf16 only
