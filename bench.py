@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FLARE routing fwd tokens/s at N=1M,M=256 (1 GPU); % of bf16 MFMA roofline"
+METRIC_BWD = "FLARE routing bwd tokens/s at N=1M,M=256 (1 GPU); % of bf16 MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # v_exp_f32 issue rate: 1024 SIMDs x 2.4 GHz x 64 lanes per 9.8 cycles (the
@@ -33,12 +34,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_EXP_T = 16.0
 
 
-KERNEL_SRC = os.path.join(ROOT, "rank_latent_attention_amd", "csrc", "flare.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "rank_latent_attention_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha256() -> str:
+    """sha256 over the kernel sources (csrc/*.hip and *.h, by name)."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(KERNEL_SRC_DIR, f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -49,9 +60,8 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_sha256") != src:
+    if not ent or ent.get("source_sha256") != kernel_source_sha256():
         return None
     return ent.get("bytes_per_launch")
 
@@ -158,6 +168,31 @@ def time_configs(names: str) -> None:
         torch.cuda.empty_cache()
 
 
+def cpu_baseline_backward(w, dY, target_s: float = 15.0):
+    """The fp64 oracle of the FLARE backward (forward recompute, decoder and
+    encoder backward) on a bounded sample: the first n tokens of head 0, n
+    chosen from a 2^16-token timing so the sample takes about target_s."""
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.threads()
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.flare_backward(w.Q[:1], np.ascontiguousarray(w.K[:, :1, :n]), np.ascontiguousarray(w.V[:, :1, :n]),
+                              np.ascontiguousarray(dY[:, :1, :n]))
+        return time.perf_counter() - t0
+
+    n1 = min(w.N, 1 << 16)
+    t1 = run(n1)
+    n = int(min(w.N, max(n1, n1 * target_s / max(t1, 1e-3))))
+    t = run(n) if n > n1 else t1
+    value = w.B * n / (t * w.H)   # a token of the whole pass needs all H heads
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle FLARE backward (forward recompute, decoder and encoder backward) on head 0 of "
+                      f"{w.H}, first {n} of {w.N} tokens, M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; "
+                      f"tokens/s scaled by 1/{w.H} heads (the work is linear in the token count)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,9 +200,10 @@ def main():
     # MFMA + transcendental load; 30 warmup steps (about 90 launches) reach it
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm"], default="flare",
+    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_backward"], default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
-                         "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels")
+                         "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels; "
+                         "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--configs", default="",
                     help="instead of the bench line, time the forward of these workloads (comma-separated names "
@@ -188,6 +224,9 @@ def main():
 
     if args.configs:
         time_configs(args.configs)
+        return
+    if args.workload == "flare_backward":
+        bench_backward(args)
         return
 
     pp = args.workload in ("flare_pp", "flare_pp_norm")
@@ -292,7 +331,8 @@ def main():
         # time.  Per-kernel times are in the kernel trace.
         achieved = flops / (ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic("whole_step", args.workload),
                     "kernel": "whole step (5 launches)", "kernel_us": round(ms * 1e3, 2),
                     "algorithmic_bytes": 4 * B * H * N * D * 2}
     tok_s = B * N / (ms * 1e-3)
@@ -307,6 +347,75 @@ def main():
            "roofline": roofline}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+def bench_backward(args):
+    """One step = one flare_backward call (center, statistics, decode-side
+    col pass, dZ sum, encoder-side col pass, dQ sum, row pass) over the
+    million-point workload, given Z and L of one untimed forward."""
+    import torch
+    import rank_latent_attention_amd as flare
+    from rank_latent_attention_amd.inputs import config5, cotangent
+    t0 = time.perf_counter()
+    w = config5(pp=False)
+    dYh = cotangent(101, "dy", w.K.shape)
+    log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    B, H, N, M, D = w.B, w.H, w.N, w.M, w.D
+    Q, K, V, dY = up(w.Q), up(w.K), up(w.V), up(dYh)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    flare.flare_forward(Q, K, V, Z=Z, L=L)
+    dQ = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+    dK, dV = torch.empty_like(K), torch.empty_like(K)
+    ws = flare.workspace(flare.flare.OP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
+
+    def step():
+        flare.flare_backward(Q, K, V, Z, L, dY, dQ=dQ, dK=dK, dV=dV, ws=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = src * 1.0
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps: {ms:.3f} ms/step")
+    # Algorithmic FLOPs: the backward of each of the two attention passes is
+    # five products of 2 BHNMD each (scores recomputed, the output-cotangent
+    # product, and the three gradients), 20 BHNMD for the pair.  The kernels
+    # of one call are reached only through the whole entry point, so the
+    # roofline is the step's; per-kernel times are in the kernel trace.
+    flops = 20.0 * B * H * N * M * D
+    achieved = flops / (ms * 1e-3) / 1e12
+    kb = 5 * B * H * N * D * 2   # read K, V, dY and write dK, dV once each, bf16
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("whole_step", args.workload),
+                "kernel": "whole step (7 launches)", "kernel_us": round(ms * 1e3, 2), "algorithmic_bytes": kb,
+                "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out = {"metric": METRIC_BWD, "value": B * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "FLARE routing backward, million-point surface mesh", "B": B, "H": H, "N": N,
+                      "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
+           "tflops": round(achieved, 2), "roofline": roofline}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_backward(w, dYh)
     print(json.dumps(out), flush=True)
 
 

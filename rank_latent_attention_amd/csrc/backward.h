@@ -32,7 +32,7 @@
 // Launches (one call, one stream):
 //   center      Zc = Z - mean over latents                      [B,H,M,D] f32
 //   statistics  decode_kernel in statistics mode on Zc: per token
-//               (lse2_n, dY_n . (Y_n - mean Z))                 [B,H,N] float2
+//               -lse2_n and -dY_n . (Y_n - mean Z)              2 x [B,H,N] f32
 //   col pass    (decode side) per split of the tokens, lanes = latents:
 //               partial sums over tokens of dZ and dQ_dec
 //   sum         dZ = sum of splits; c_m from the bf16-rounded dZ_m
@@ -84,7 +84,8 @@ struct ColArgs {
   const bf16* K;        // [B,H,N,D]
   const bf16* X;        // decode side: dY; encoder side: V   [B,H,N,D]
   const float* lat;     // decode side: Zc; encoder side: dZ  [B,H,M,D]
-  const float2* stats;  // decode side: per token (lse2, delta)
+  const float* nlse;    // decode side: per token -lse2
+  const float* ndot;    // decode side: per token -delta
   const float* L;       // encoder side: the forward's log-normaliser [B,H,M]
   const float* c;       // encoder side: c_m [B,H,M]
   float* part_dz;       // decode side: [BH][pmax][M][D]
@@ -127,7 +128,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   constexpr int G = NW / WN;
   static_assert(NW * 64 >= ROWS, "one statistics row per thread");
   __shared__ __align__(16) bf16 tiles[4 * TE];       // [buffer][K, X][TE]
-  __shared__ __align__(16) float2 st[DEC ? 2 * ROWS : 2];
+  // decode side: the tile rows' -lse2 and -delta, [buffer][ROWS] each
+  __shared__ __align__(16) float stl[DEC ? 2 * ROWS : 4];
+  __shared__ __align__(16) float std_[DEC ? 2 * ROWS : 4];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int mg = wave % G, ng = wave / G;
@@ -172,14 +175,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 
     const bf16* Kh = a.K + (size_t)bh * N * D;
     const bf16* Xh = a.X + (size_t)bh * N * D;
-    const float2* Sh = DEC ? a.stats + (size_t)bh * N : nullptr;
+    const float* Sl = DEC ? a.nlse + (size_t)bh * N : nullptr;
+    const float* Sd = DEC ? a.ndot + (size_t)bh * N : nullptr;
     __syncthreads();  // the previous piece is done with the tiles
     dma_tile<D, NW>(kt0, Kh, n_lo, n_hi, wave, lane);
     dma_tile<D, NW>(xt0, Xh, n_lo, n_hi, wave, lane);
     if constexpr (DEC) {
       if ((int)threadIdx.x < ROWS) {
-        const int r = n_lo + (int)threadIdx.x;
-        st[threadIdx.x] = Sh[r < n_hi ? r : n_hi - 1];
+        int r = n_lo + (int)threadIdx.x;
+        r = r < n_hi ? r : n_hi - 1;
+        stl[threadIdx.x] = Sl[r];
+        std_[threadIdx.x] = Sd[r];
       }
     }
     wait_dma();
@@ -187,14 +193,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     int buf = 0;
     for (int t0 = n_lo; t0 < n_hi; t0 += ROWS) {
       const int tn = t0 + ROWS;
-      float2 snext = make_float2(0.f, 0.f);
+      float sl_next = 0.f, sd_next = 0.f;
       if (tn < n_hi) {
         dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE, Kh, tn, n_hi, wave, lane);
         dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE + TE, Xh, tn, n_hi, wave, lane);
         if constexpr (DEC) {
           if ((int)threadIdx.x < ROWS) {
-            const int r = tn + (int)threadIdx.x;
-            snext = Sh[r < n_hi ? r : n_hi - 1];
+            int r = tn + (int)threadIdx.x;
+            r = r < n_hi ? r : n_hi - 1;
+            sl_next = Sl[r];
+            sd_next = Sd[r];
           }
         }
       }
@@ -209,14 +217,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
           xop.v[s] = lds_load<bf16x8>(kx[s] + off);
         }
         if constexpr (DEC) {
-          // the rows' (lse2, delta): rows acc_row(r, g) come in four runs of four
-          const float2* sr = st + buf * ROWS + 32 * nb + 4 * g;
+          // the rows' -lse2 and -delta: rows acc_row(r, g) come in four runs of four
+          const int r0 = buf * ROWS + 32 * nb + 4 * g;
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(sr + 8 * c4);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sr + 8 * c4 + 2);
-            cp[4 * c4] = -u[0]; cg[4 * c4] = -u[1]; cp[4 * c4 + 1] = -u[2]; cg[4 * c4 + 1] = -u[3];
-            cp[4 * c4 + 2] = -v[0]; cg[4 * c4 + 2] = -v[1]; cp[4 * c4 + 3] = -v[2]; cg[4 * c4 + 3] = -v[3];
+            const f32x4 u = *reinterpret_cast<const f32x4*>(stl + r0 + 8 * c4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(std_ + r0 + 8 * c4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { cp[4 * c4 + i] = u[i]; cg[4 * c4 + i] = v[i]; }
           }
         }
         f32x16 s = qk_mma<D>(kop, qop, cp);
@@ -238,7 +246,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
         }
       }
       if constexpr (DEC) {
-        if (tn < n_hi && (int)threadIdx.x < ROWS) st[(buf ^ 1) * ROWS + threadIdx.x] = snext;
+        if (tn < n_hi && (int)threadIdx.x < ROWS) {
+          stl[(buf ^ 1) * ROWS + threadIdx.x] = sl_next;
+          std_[(buf ^ 1) * ROWS + threadIdx.x] = sd_next;
+        }
       }
       wait_dma();
       __syncthreads();
@@ -291,12 +302,24 @@ __device__ inline int split_count(const SumArgs& a, int bh) {
   return (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
 }
 
+// Splits in ascending order, loaded kSumBatch at a time before any is
+// added, so a batch costs one memory round trip.
+constexpr int kSumBatch = 8;
 __device__ inline float split_sum(const SumArgs& a, int bh, int md) {
   const int cnt = split_count(a, bh);
+  if (cnt == 0) return 0.f;
   const float* p = a.part + (size_t)bh * a.pmax * a.M * a.D + md;
   const size_t stride = (size_t)a.M * a.D;
   float s = 0.f;
-  for (int i = 0; i < cnt; ++i) s += p[i * stride];
+  for (int i0 = 0; i0 < cnt; i0 += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) v[j] = p[(size_t)(i0 + j < cnt ? i0 + j : 0) * stride];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) asm volatile("" ::"v"(v[j]));
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) s += i0 + j < cnt ? v[j] : 0.f;
+  }
   return s;
 }
 
@@ -352,7 +375,8 @@ struct RowArgs {
   const bf16* V;        // encoder side
   const bf16* dY;       // decode side
   const float* Zc;      // decode side
-  const float2* stats;  // decode side
+  const float* nlse;    // decode side: per token -lse2
+  const float* ndot;    // decode side: per token -delta
   const float* dZ;      // encoder side
   const float* L;       // encoder side
   const float* c;       // encoder side
@@ -372,8 +396,11 @@ template <int D> struct RowLds {
   }
 };
 
-template <int D, bool TAIL, bool DEC, bool ENC>
-__global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
+// NW waves per workgroup share the staged head: at the largest sizes the
+// LDS holds one workgroup per compute unit, so 8 waves keep two per SIMD.
+template <int D, int NW, bool TAIL, bool DEC, bool ENC>
+__global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
+  constexpr int NT = NW * 64;
   using RL = RowLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
@@ -401,7 +428,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
     __syncthreads();  // the previous piece is done with the staged head
     {
       const bf16* Qh = a.Q + (size_t)(a.q_batched ? bh : h) * M * D;
-      for (int e = threadIdx.x; e < Mp * D; e += kThreads) {
+      for (int e = threadIdx.x; e < Mp * D; e += NT) {
         const int m = e / D, d = e % D;
         const bool in = m < M;
         const bf16 q = (bf16)(in ? (float)Qh[(size_t)m * D + d] * a.qscale : 0.f);
@@ -415,7 +442,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
         }
       }
       if constexpr (ENC) {
-        for (int m = threadIdx.x; m < Mp; m += kThreads) {
+        for (int m = threadIdx.x; m < Mp; m += NT) {
           // latents past M: shift +inf, zero weight
           l2[m] = m < M ? -a.L[(size_t)bh * M + m] * kLog2e : -INFINITY;
           cc[m] = m < M ? -a.c[(size_t)bh * M + m] : 0.f;
@@ -425,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
     __syncthreads();
 
     const bf16* Kh = a.K + (size_t)bh * N * D;
-    for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += kDecGroup) {
+    for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += 32 * NW) {
       // lanes past the piece recompute its last token and store the same values there
       const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
       QKOp<bf16, D> kop, yop, vop;
@@ -433,9 +460,8 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
       f32x16 cw = {}, cd = {};
       if constexpr (DEC) {
         load_op<D>(yop, a.dY + ((size_t)bh * N + n) * D, g);
-        const float2 sn = a.stats[(size_t)bh * N + n];
-        cw = splat16(-sn.x);
-        cd = splat16(-sn.y);
+        cw = splat16(a.nlse[(size_t)bh * N + n]);
+        cd = splat16(a.ndot[(size_t)bh * N + n]);
       }
       if constexpr (ENC) load_op<D>(vop, a.V + ((size_t)bh * N + n) * D, g);
       f32x16 acck = {}, accv = {};
@@ -514,7 +540,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(RowArgs a) {
 // Host side
 // ----------------------------------------------------------------------------
 struct BwdLayout {
-  size_t zc = 0, stats = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
+  size_t zc = 0, nlse = 0, ndot = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D) {
@@ -529,7 +555,8 @@ BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D
   w.c = off; off += align256((size_t)BH * M * sizeof(float));
   if (dec) {
     w.zc = off; off += lat;
-    w.stats = off; off += align256((size_t)BH * N * sizeof(float2));
+    w.nlse = off; off += align256((size_t)BH * N * sizeof(float));
+    w.ndot = off; off += align256((size_t)BH * N * sizeof(float));
     w.part_dz = off; off += part;
   }
   w.total = off;
@@ -560,14 +587,16 @@ int launch_col(const ColArgs& a, int D, bool dec, const EncPlan& p, hipStream_t 
   return D == 16 ? launch_col_d<16, false>(a, p.NW, p.WN, st) : launch_col_d<32, false>(a, p.NW, p.WN, st);
 }
 
+constexpr int kRowWaves = 8;
+
 template <int D, bool TAIL, bool DEC, bool ENC>
 int launch_row_k(const RowArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)bwd_row_kernel<D, TAIL, DEC, ENC>;
+  const void* fn = (const void*)bwd_row_kernel<D, kRowWaves, TAIL, DEC, ENC>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((bwd_row_kernel<D, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((bwd_row_kernel<D, kRowWaves, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
@@ -590,14 +619,14 @@ int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, hipStream_t
 }
 
 int launch_stats(const Dev& dev, const bf16* Q, int q_batched, const bf16* K, const float* Zc, const bf16* dY,
-                 float2* stats, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
+                 float* nlse, float* ndot, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
   DecArgs a{};
   a.Q = Q; a.K = K; a.Z = Zc; a.Y = nullptr;
   a.total = (long long)BH * N;
   a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = 0;
   a.qscale = qscale;
   a.qmul = nullptr; a.eps = 0.f;
-  a.dY = dY; a.stats = stats;
+  a.dY = dY; a.nlse = nlse; a.ndot = ndot;
   const long long want = (long long)dev.cus * kDecWgPerCu;
   const long long maxw = cdiv(a.total, 32);
   a.nwg = (int)(want < maxw ? want : maxw);
@@ -635,15 +664,17 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   ca.q_batched = q_batched; ca.H = H; ca.N = N; ca.M = M; ca.nwg = p.nwg; ca.pmax = p.pmax;
   ca.qscale = qs; ca.part_dq = part_dq;
   float* zc = dec ? (float*)(ws + w.zc) : nullptr;
-  float2* stats = dec ? (float2*)(ws + w.stats) : nullptr;
+  float* nlse = dec ? (float*)(ws + w.nlse) : nullptr;
+  float* ndot = dec ? (float*)(ws + w.ndot) : nullptr;
   if (N > 0) {
     if (dec) {
       hipLaunchKernelGGL(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
       if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
-      rc = launch_stats(dev, Q, q_batched, K, zc, dY, stats, BH, H, N, M, D, qs, st);
+      rc = launch_stats(dev, Q, q_batched, K, zc, dY, nlse, ndot, BH, H, N, M, D, qs, st);
       if (rc) return rc;
       ColArgs cd = ca;
-      cd.X = dY; cd.lat = zc; cd.stats = stats; cd.part_dz = (float*)(ws + w.part_dz); cd.accumulate = 0;
+      cd.X = dY; cd.lat = zc; cd.nlse = nlse; cd.ndot = ndot; cd.part_dz = (float*)(ws + w.part_dz);
+      cd.accumulate = 0;
       rc = launch_col(cd, D, true, p, st);
       if (rc) return rc;
       sa.part = cd.part_dz;
@@ -670,7 +701,8 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
   if (N == 0) return FLARE_OK;
   RowArgs ra{};
-  ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.stats = stats; ra.dZ = dz; ra.L = L; ra.c = c;
+  ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.nlse = nlse; ra.ndot = ndot; ra.dZ = dz; ra.L = L;
+  ra.c = c;
   ra.dK = dK; ra.dV = dV;
   ra.total = (long long)BH * N;
   ra.q_batched = q_batched; ra.H = H; ra.N = N; ra.M = M; ra.MB = (int)cdiv(M, 32);

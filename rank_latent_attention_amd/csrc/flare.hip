@@ -1036,9 +1036,11 @@ struct DecArgs {
   const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
   float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
   // statistics mode (the kernel's ST flag, bf16): instead of Y, per token
-  // (log2 of the weight sum over the latents, dY . Y) into stats [B,H,N]
+  // the negated log2 of the weight sum over the latents into nlse [B,H,N]
+  // and the negated dY . Y into ndot [B,H,N]
   const void* dY;     // [B,H,N,D], type T
-  float2* stats;
+  float* nlse;
+  float* ndot;
 };
 
 template <typename T, int D> struct DecLds {
@@ -1270,7 +1272,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           }
         }
         const float dot = pair_sum(part) * inv;
-        if (g == 0) a.stats[(size_t)bh * N + n] = make_float2(shift + __builtin_amdgcn_logf(den), dot);
+        if (g == 0) {
+          a.nlse[(size_t)bh * N + n] = -(shift + __builtin_amdgcn_logf(den));
+          a.ndot[(size_t)bh * N + n] = -dot;
+        }
       } else {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
