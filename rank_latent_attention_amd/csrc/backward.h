@@ -32,7 +32,10 @@
 // Launches (one call, one stream):
 //   center      Zc = Z - mean over latents                      [B,H,M,D] f32
 //   statistics  decode_kernel in statistics mode on Zc: per token
-//               -lse2_n and -dY_n . (Y_n - mean Z)              2 x [B,H,N] f32
+//               -lse2_n and -dY_n . (Y_n - mean Z), as one record of
+//               three-part bf16 splits                          [B,H,N] 16 B
+//               (the passes add them to score tiles through one extra
+//               matrix-core step whose other operand selects the parts)
 //   col pass    (decode side) per split of the tokens, lanes = latents:
 //               partial sums over tokens of dZ and dQ_dec
 //   sum         dZ = sum of splits; c_m from the bf16-rounded dZ_m
@@ -84,8 +87,7 @@ struct ColArgs {
   const bf16* K;        // [B,H,N,D]
   const bf16* X;        // decode side: dY; encoder side: V   [B,H,N,D]
   const float* lat;     // decode side: Zc; encoder side: dZ  [B,H,M,D]
-  const float* nlse;    // decode side: per token -lse2
-  const float* ndot;    // decode side: per token -delta
+  const uint4* srec;    // decode side: per token record (-lse2, -delta)
   const float* L;       // encoder side: the forward's log-normaliser [B,H,M]
   const float* c;       // encoder side: c_m [B,H,M]
   float* part_dz;       // decode side: [BH][pmax][M][D]
@@ -108,9 +110,49 @@ __device__ inline PVOp<bf16> tr_operand(const unsigned (&va)[4], unsigned off, i
   return o;
 }
 
+// LDS reads of tiles that a DMA completed before the last barrier, issued
+// as inline assembly like the transposing reads: as ordinary loads the
+// compiler cannot tell them apart from the DMA into the other buffer (or from
+// the statistics prefetch) and makes each wait for all outstanding memory
+// operations.  lds_wait() must run before any of them is used.
+__device__ inline bf16x8 lds_read16(unsigned addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+template <int D> __device__ inline void lds_wait(QKOp<bf16, D>& a, QKOp<bf16, D>& b, bf16x8& c) {
+  if constexpr (D == 32)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(a.v[1]), "+v"(b.v[0]), "+v"(b.v[1]), "+v"(c));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(b.v[0]), "+v"(c));
+}
+
 __device__ inline void pack16(const f32x16& p, bf16x8& b0, bf16x8& b1) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) { b0[r] = (bf16)p[r]; b1[r] = (bf16)p[8 + r]; }
+}
+
+// B operand of the record step: ones at the three parts of the first (y:
+// second) value of a split3_record, in the lanes of k = 0..7; zero elsewhere.
+__device__ inline bf16x8 record_select(int g, bool second) {
+  bf16x8 r;
+  const bf16 one = (bf16)(g == 0 ? 1.f : 0.f), zero = (bf16)0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = ((i & 3) != 3 && (i >= 4) == second) ? one : zero;
+  return r;
+}
+
+// acc + the record's x (sel = record_select(g, false)) or y on every column:
+// the A operand is the row's record, in both halves of the lane's k range.
+__device__ inline f32x16 record_add(const uint4& rec, const bf16x8& sel, const f32x16& acc) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(&rec);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sel, acc, 0, 0, 0);
+}
+
+__device__ inline float record_value(const uint4& rec, bool second) {
+  const bf16x8 r = *reinterpret_cast<const bf16x8*>(&rec);
+  const int o = second ? 4 : 0;
+  return ((float)r[o] + (float)r[o + 1]) + (float)r[o + 2];
 }
 
 __device__ inline f32x16 splat16(float v) {
@@ -128,9 +170,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   constexpr int G = NW / WN;
   static_assert(NW * 64 >= ROWS, "one statistics row per thread");
   __shared__ __align__(16) bf16 tiles[4 * TE];       // [buffer][K, X][TE]
-  // decode side: the tile rows' -lse2 and -delta, [buffer][ROWS] each
-  __shared__ __align__(16) float stl[DEC ? 2 * ROWS : 4];
-  __shared__ __align__(16) float std_[DEC ? 2 * ROWS : 4];
+  // decode side: the tile rows' statistics records, [buffer][ROWS]
+  __shared__ __align__(16) uint4 srl[DEC ? 2 * ROWS : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int mg = wave % G, ng = wave / G;
@@ -139,6 +180,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   bf16* const xt0 = tiles + TE;
 
   const TileOffs<D> to = tile_offsets<D>(lane);
+  const unsigned sra = lds_addr(srl) + (unsigned)li * 16u;  // this lane's record row in buffer 0
   unsigned ka[D / 16], kx[D / 16], va[4], vx[4];
   {
     const unsigned bk = lds_addr(kt0), bx = lds_addr(xt0);
@@ -166,6 +208,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     load_op_scaled<D>(lop, a.lat + ((size_t)bh * M + mc) * D, g, 1.f);
     if (m >= M) { zero_op<D>(qop); zero_op<D>(lop); }
     f32x16 cp = {}, cg = {};
+    const bf16x8 sel_s = record_select(g, false), sel_e = record_select(g, true);
     if constexpr (!DEC) {
       // latents past M: shift +inf, so their weights are exactly zero
       cp = splat16(m < M ? -a.L[(size_t)bh * M + m] * kLog2e : -INFINITY);
@@ -175,17 +218,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 
     const bf16* Kh = a.K + (size_t)bh * N * D;
     const bf16* Xh = a.X + (size_t)bh * N * D;
-    const float* Sl = DEC ? a.nlse + (size_t)bh * N : nullptr;
-    const float* Sd = DEC ? a.ndot + (size_t)bh * N : nullptr;
+    const uint4* Sr = DEC ? a.srec + (size_t)bh * N : nullptr;
     __syncthreads();  // the previous piece is done with the tiles
     dma_tile<D, NW>(kt0, Kh, n_lo, n_hi, wave, lane);
     dma_tile<D, NW>(xt0, Xh, n_lo, n_hi, wave, lane);
     if constexpr (DEC) {
       if ((int)threadIdx.x < ROWS) {
-        int r = n_lo + (int)threadIdx.x;
-        r = r < n_hi ? r : n_hi - 1;
-        stl[threadIdx.x] = Sl[r];
-        std_[threadIdx.x] = Sd[r];
+        const int r = n_lo + (int)threadIdx.x;
+        srl[threadIdx.x] = Sr[r < n_hi ? r : n_hi - 1];
       }
     }
     wait_dma();
@@ -193,16 +233,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     int buf = 0;
     for (int t0 = n_lo; t0 < n_hi; t0 += ROWS) {
       const int tn = t0 + ROWS;
-      float sl_next = 0.f, sd_next = 0.f;
+      uint4 rnext = make_uint4(0, 0, 0, 0);
       if (tn < n_hi) {
         dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE, Kh, tn, n_hi, wave, lane);
         dma_tile<D, NW>(tiles + (buf ^ 1) * 2 * TE + TE, Xh, tn, n_hi, wave, lane);
         if constexpr (DEC) {
           if ((int)threadIdx.x < ROWS) {
-            int r = tn + (int)threadIdx.x;
-            r = r < n_hi ? r : n_hi - 1;
-            sl_next = Sl[r];
-            sd_next = Sd[r];
+            const int r = tn + (int)threadIdx.x;
+            rnext = Sr[r < n_hi ? r : n_hi - 1];
           }
         }
       }
@@ -213,19 +251,18 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
         QKOp<bf16, D> kop, xop;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          kop.v[s] = lds_load<bf16x8>(ka[s] + off);
-          xop.v[s] = lds_load<bf16x8>(kx[s] + off);
+          kop.v[s] = lds_read16(ka[s] + off);
+          xop.v[s] = lds_read16(kx[s] + off);
         }
+        bf16x8 recv = {};
+        if constexpr (DEC) recv = lds_read16(sra + (unsigned)(buf * ROWS + 32 * nb) * 16u);
+        lds_wait<D>(kop, xop, recv);
         if constexpr (DEC) {
-          // the rows' -lse2 and -delta: rows acc_row(r, g) come in four runs of four
-          const int r0 = buf * ROWS + 32 * nb + 4 * g;
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(stl + r0 + 8 * c4);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(std_ + r0 + 8 * c4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { cp[4 * c4 + i] = u[i]; cg[4 * c4 + i] = v[i]; }
-          }
+          // the token rows' -lse2 and -delta enter through the record step
+          // (A operand row = token li of the block)
+          const uint4 rec = *reinterpret_cast<const uint4*>(&recv);
+          cp = record_add(rec, sel_s, f32x16{});
+          cg = record_add(rec, sel_e, f32x16{});
         }
         f32x16 s = qk_mma<D>(kop, qop, cp);
         const f32x16 e = qk_mma<D>(xop, lop, cg);
@@ -246,10 +283,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
         }
       }
       if constexpr (DEC) {
-        if (tn < n_hi && (int)threadIdx.x < ROWS) {
-          stl[(buf ^ 1) * ROWS + threadIdx.x] = sl_next;
-          std_[(buf ^ 1) * ROWS + threadIdx.x] = sd_next;
-        }
+        if (tn < n_hi && (int)threadIdx.x < ROWS) srl[(buf ^ 1) * ROWS + threadIdx.x] = rnext;
       }
       wait_dma();
       __syncthreads();
@@ -375,8 +409,7 @@ struct RowArgs {
   const bf16* V;        // encoder side
   const bf16* dY;       // decode side
   const float* Zc;      // decode side
-  const float* nlse;    // decode side: per token -lse2
-  const float* ndot;    // decode side: per token -delta
+  const uint4* srec;    // decode side: per token record (-lse2, -delta)
   const float* dZ;      // encoder side
   const float* L;       // encoder side
   const float* c;       // encoder side
@@ -390,9 +423,9 @@ struct RowArgs {
 template <int D> struct RowLds {
   static constexpr int RST = D + 8;  // row stride (bf16)
   __host__ __device__ static int tst(int MB) { return MB * 32 + 4; }  // transposed stride
-  // qs, zr, dzr rows; qt, dzt transposed; L2 and c per latent (float)
+  // qs, zr, dzr rows; qt, dzt transposed; per latent record (-L2, -c)
   static size_t bytes(int MB) {
-    return (size_t)(3 * MB * 32 * RST + 2 * D * tst(MB)) * sizeof(bf16) + (size_t)2 * MB * 32 * sizeof(float);
+    return (size_t)(3 * MB * 32 * RST + 2 * D * tst(MB)) * sizeof(bf16) + (size_t)MB * 32 * sizeof(uint4);
   }
 };
 
@@ -410,8 +443,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
   bf16* dzr = zr + (size_t)Mp * RL::RST;
   bf16* qt = dzr + (size_t)Mp * RL::RST;
   bf16* dzt = qt + (size_t)D * tst;
-  float* l2 = reinterpret_cast<float*>(dzt + (size_t)D * tst);
-  float* cc = l2 + Mp;
+  uint4* lrec = reinterpret_cast<uint4*>(dzt + (size_t)D * tst);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31, g = lane >> 5;
   __builtin_assume(MB >= 1);
@@ -443,15 +475,16 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
       }
       if constexpr (ENC) {
         for (int m = threadIdx.x; m < Mp; m += NT) {
-          // latents past M: shift +inf, zero weight
-          l2[m] = m < M ? -a.L[(size_t)bh * M + m] * kLog2e : -INFINITY;
-          cc[m] = m < M ? -a.c[(size_t)bh * M + m] : 0.f;
+          // latents past M: a shift far beyond any score, zero weight
+          lrec[m] = m < M ? split3_record(-a.L[(size_t)bh * M + m] * kLog2e, -a.c[(size_t)bh * M + m])
+                          : split3_record(-1e30f, 0.f);
         }
       }
     }
     __syncthreads();
 
     const bf16* Kh = a.K + (size_t)bh * N * D;
+    const bf16x8 sel_s = record_select(g, false), sel_e = record_select(g, true);
     for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += 32 * NW) {
       // lanes past the piece recompute its last token and store the same values there
       const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
@@ -460,8 +493,9 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
       f32x16 cw = {}, cd = {};
       if constexpr (DEC) {
         load_op<D>(yop, a.dY + ((size_t)bh * N + n) * D, g);
-        cw = splat16(a.nlse[(size_t)bh * N + n]);
-        cd = splat16(a.ndot[(size_t)bh * N + n]);
+        const uint4 rec = a.srec[(size_t)bh * N + n];
+        cw = splat16(record_value(rec, false));
+        cd = splat16(record_value(rec, true));
       }
       if constexpr (ENC) load_op<D>(vop, a.V + ((size_t)bh * N + n) * D, g);
       f32x16 acck = {}, accv = {};
@@ -481,18 +515,11 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
         if constexpr (ENC) {
           QKOp<bf16, D> zop;
           load_op<D>(zop, dzr + (mb * 32 + li) * RL::RST, g);
-          f32x16 cp, cg;
-          const float* lr = l2 + mb * 32 + 4 * g;
-          const float* cr = cc + mb * 32 + 4 * g;
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(lr + 8 * c4);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(cr + 8 * c4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { cp[4 * c4 + i] = u[i]; cg[4 * c4 + i] = v[i]; }
-          }
-          const f32x16 s = qk_mma<D>(qop, kop, cp);
-          const f32x16 e = qk_mma<D>(zop, vop, cg);
+          // the latent rows' -L2 and -c through the record step (A operand
+          // row = latent li of the block)
+          const uint4 rec = lrec[mb * 32 + li];
+          const f32x16 s = qk_mma<D>(qop, kop, record_add(rec, sel_s, f32x16{}));
+          const f32x16 e = qk_mma<D>(zop, vop, record_add(rec, sel_e, f32x16{}));
           f32x16 p;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -540,7 +567,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
 // Host side
 // ----------------------------------------------------------------------------
 struct BwdLayout {
-  size_t zc = 0, nlse = 0, ndot = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
+  size_t zc = 0, srec = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D) {
@@ -555,8 +582,7 @@ BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D
   w.c = off; off += align256((size_t)BH * M * sizeof(float));
   if (dec) {
     w.zc = off; off += lat;
-    w.nlse = off; off += align256((size_t)BH * N * sizeof(float));
-    w.ndot = off; off += align256((size_t)BH * N * sizeof(float));
+    w.srec = off; off += align256((size_t)BH * N * sizeof(uint4));
     w.part_dz = off; off += part;
   }
   w.total = off;
@@ -619,14 +645,14 @@ int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, hipStream_t
 }
 
 int launch_stats(const Dev& dev, const bf16* Q, int q_batched, const bf16* K, const float* Zc, const bf16* dY,
-                 float* nlse, float* ndot, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
+                 uint4* srec, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
   DecArgs a{};
   a.Q = Q; a.K = K; a.Z = Zc; a.Y = nullptr;
   a.total = (long long)BH * N;
   a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = 0;
   a.qscale = qscale;
   a.qmul = nullptr; a.eps = 0.f;
-  a.dY = dY; a.nlse = nlse; a.ndot = ndot;
+  a.dY = dY; a.srec = srec;
   const long long want = (long long)dev.cus * kDecWgPerCu;
   const long long maxw = cdiv(a.total, 32);
   a.nwg = (int)(want < maxw ? want : maxw);
@@ -664,16 +690,15 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   ca.q_batched = q_batched; ca.H = H; ca.N = N; ca.M = M; ca.nwg = p.nwg; ca.pmax = p.pmax;
   ca.qscale = qs; ca.part_dq = part_dq;
   float* zc = dec ? (float*)(ws + w.zc) : nullptr;
-  float* nlse = dec ? (float*)(ws + w.nlse) : nullptr;
-  float* ndot = dec ? (float*)(ws + w.ndot) : nullptr;
+  uint4* srec = dec ? (uint4*)(ws + w.srec) : nullptr;
   if (N > 0) {
     if (dec) {
       hipLaunchKernelGGL(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
       if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
-      rc = launch_stats(dev, Q, q_batched, K, zc, dY, nlse, ndot, BH, H, N, M, D, qs, st);
+      rc = launch_stats(dev, Q, q_batched, K, zc, dY, srec, BH, H, N, M, D, qs, st);
       if (rc) return rc;
       ColArgs cd = ca;
-      cd.X = dY; cd.lat = zc; cd.nlse = nlse; cd.ndot = ndot; cd.part_dz = (float*)(ws + w.part_dz);
+      cd.X = dY; cd.lat = zc; cd.srec = srec; cd.part_dz = (float*)(ws + w.part_dz);
       cd.accumulate = 0;
       rc = launch_col(cd, D, true, p, st);
       if (rc) return rc;
@@ -701,7 +726,7 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
   if (N == 0) return FLARE_OK;
   RowArgs ra{};
-  ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.nlse = nlse; ra.ndot = ndot; ra.dZ = dz; ra.L = L;
+  ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.srec = srec; ra.dZ = dz; ra.L = L;
   ra.c = c;
   ra.dK = dK; ra.dV = dV;
   ra.total = (long long)BH * N;

@@ -1036,12 +1036,29 @@ struct DecArgs {
   const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
   float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
   // statistics mode (the kernel's ST flag, bf16): instead of Y, per token
-  // the negated log2 of the weight sum over the latents into nlse [B,H,N]
-  // and the negated dY . Y into ndot [B,H,N]
+  // one record of 8 bf16 (see split3_record): the negated log2 of the
+  // weight sum over the latents and the negated dY . Y, each as three parts
   const void* dY;     // [B,H,N,D], type T
-  float* nlse;
-  float* ndot;
+  uint4* srec;        // [B,H,N]
 };
+
+// Record of two float32 values x, y as 8 bf16: x = x0 + x1 + x2 and
+// y = y0 + y1 + y2 (each part the bf16 rounding of what the previous parts
+// leave, so the sum carries the float's full precision), as
+// [x0, x1, x2, 0, y0, y1, y2, 0].  A matrix product whose other operand holds
+// ones at those positions adds x or y to a result exactly.
+__device__ inline uint4 split3_record(float x, float y) {
+  bf16x8 r;
+  float t = x;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) { r[i] = (bf16)t; t -= (float)r[i]; }
+  r[3] = (bf16)0.f;
+  t = y;
+#pragma unroll
+  for (int i = 4; i < 7; ++i) { r[i] = (bf16)t; t -= (float)r[i]; }
+  r[7] = (bf16)0.f;
+  return *reinterpret_cast<uint4*>(&r);
+}
 
 template <typename T, int D> struct DecLds {
   static constexpr int E = 16 / sizeof(T);
@@ -1272,10 +1289,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           }
         }
         const float dot = pair_sum(part) * inv;
-        if (g == 0) {
-          a.nlse[(size_t)bh * N + n] = -(shift + __builtin_amdgcn_logf(den));
-          a.ndot[(size_t)bh * N + n] = -dot;
-        }
+        if (g == 0) a.srec[(size_t)bh * N + n] = split3_record(-(shift + __builtin_amdgcn_logf(den)), -dot);
       } else {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
