@@ -23,7 +23,7 @@ _lib = None
 
 __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
            "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed", "encode_backward",
-           "decode_backward", "flare_backward"]
+           "decode_backward", "flare_backward", "flare_pp_backward"]
 
 
 def build(force: bool = True) -> str:
@@ -273,3 +273,27 @@ def flare_backward(Q, K, V, dY, scale: float = 0.0, return_dZ: bool = False):
     dQe, dKe, dV = encode_backward(Q, K, V, dZ, None, scale)
     out = (dQd + dQe, dKd + dKe, dV)
     return out + (dZ,) if return_dZ else out
+
+
+def flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, dY, scale: float = 0.0, shared_vs=None):
+    """Reverse mode of the FLARE++ forward (FLARE++ paper, App. B.5, last
+    paragraph): the routing pair's backward gives the cotangent dQ of the
+    per-batch routing queries (plus dK, dV); the blend Q = Qf + g Qd passes
+    dQf = sum_b dQ, dg_h = sum_{b,m,d} dQ Qd and dQd = g dQ; dQd is handed
+    once to the synthesis encoder's backward (dL = 0), which gives dQs (summed
+    over the batch), dKs and dVs.  With shared synthesis keys and values
+    (``shared_vs``, default: Vs is Ks) the value cotangent is added to the
+    key cotangent and dVs is returned as None.
+    Returns (dQs, dKs, dVs, dQf, dgate, dK, dV)."""
+    shared = (Vs is Ks) if shared_vs is None else bool(shared_vs)
+    Qs, Ks, Vs, Qf, gate = _f64(Qs), _f64(Ks), _f64(Vs), _f64(Qf), _f64(gate)
+    Qd, _ = encode(Qs, Ks, Vs, scale)                       # [B,H,M,D]
+    Q = Qf[None] + gate[None, :, None, None] * Qd
+    dQ, dK, dV = flare_backward(Q, K, V, dY, scale)
+    dQf = dQ.sum(axis=0)
+    dgate = np.einsum("bhmd,bhmd->h", dQ, Qd)
+    dQd = gate[None, :, None, None] * dQ
+    dQs, dKs, dVs = encode_backward(Qs, Ks, Vs, dQd, None, scale)
+    if shared:
+        return dQs, dKs + dVs, None, dQf, dgate, dK, dV
+    return dQs, dKs, dVs, dQf, dgate, dK, dV

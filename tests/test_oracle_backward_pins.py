@@ -199,3 +199,64 @@ def test_shared_queries_sum_the_batch(orc):
     np.testing.assert_allclose(dQ, dQb.sum(axis=0), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(dK, dKb, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(dV, dVb, rtol=1e-13, atol=1e-15)
+
+
+# --- FLARE++ (App. B.5: the synthesis encoder receives the reduced query cotangent) ---
+
+def _pp_problem(seed, B=2, H=2, N=9, M=5, D=4):
+    r = [_rand(seed + i, *s) for i, s in enumerate([(H, M, D), (B, H, N, D), (B, H, N, D), (H, M, D), (B, H, N, D),
+                                                     (B, H, N, D)])]
+    Qs, Ks, Vs, Qf, K, V = r
+    gate = 0.3 + 0.5 * np.abs(_rand(seed + 9, H))
+    return Qs, Ks, Vs, Qf, gate, K, V
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_pp_backward_matches_finite_differences(orc, shared):
+    Qs, Ks, Vs, Qf, gate, K, V = _pp_problem(131)
+    if shared:
+        Vs = Ks
+    dY = _rand(140, *K.shape)
+    dQs, dKs, dVs, dQf, dg, dK, dV = orc.flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, dY)
+    names = ["Qs", "Ks", "Vs", "Qf", "gate", "K", "V"]
+    grads = {"Qs": dQs, "Ks": dKs, "Vs": dVs, "Qf": dQf, "gate": dg, "K": dK, "V": dV}
+    base = dict(Qs=Qs, Ks=Ks, Vs=Vs, Qf=Qf, gate=gate, K=K, V=V)
+
+    def loss(**a):
+        vs = a["Ks"] if shared else a["Vs"]
+        return _inner(dY, orc.flare_pp_forward(a["Qs"], a["Ks"], vs, a["Qf"], a["gate"], a["K"], a["V"])[0])
+
+    for i, n in enumerate(names):
+        if shared and n == "Vs":
+            assert dVs is None
+            continue
+        u = _rand(150 + i, *base[n].shape)
+
+        def f(y, n=n):
+            a = dict(base)
+            a[n] = y
+            return loss(**a)
+
+        g = grads[n]
+        assert abs(_fd(f, base[n], u) - _inner(g, u)) <= 1e-7 * max(1.0, abs(_inner(g, u))), n
+
+
+def test_pp_backward_matches_torch_autograd(orc):
+    torch = pytest.importorskip("torch")
+    Qs, Ks, Vs, Qf, gate, K, V = _pp_problem(161, B=2, H=2, N=30, M=8, D=8)
+    dY = _rand(170, *K.shape)
+    s = 1.0 / np.sqrt(8.0)
+    t = {n: torch.tensor(x, requires_grad=True) for n, x in dict(Qs=Qs, Ks=Ks, Qf=Qf, gate=gate, K=K, V=V).items()}
+
+    def sdpa(q, k, v):
+        return torch.matmul(torch.softmax(s * torch.matmul(q, k.transpose(-1, -2)), dim=-1), v)
+
+    qd = sdpa(t["Qs"].unsqueeze(0), t["Ks"], t["Ks"])                       # shared keys and values
+    q = t["Qf"].unsqueeze(0) + t["gate"][None, :, None, None] * qd
+    z = sdpa(q, t["K"], t["V"])
+    y = sdpa(t["K"], q, z)
+    y.backward(torch.tensor(dY))
+    dQs, dKs, dVs, dQf, dg, dK, dV = orc.flare_pp_backward(Qs, Ks, Ks, Qf, gate, K, V, dY)
+    assert dVs is None
+    for n, g in dict(Qs=dQs, Ks=dKs, Qf=dQf, gate=dg, K=dK, V=dV).items():
+        np.testing.assert_allclose(g, t[n].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=n)
