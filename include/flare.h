@@ -75,6 +75,7 @@ extern "C" {
 #define FLARE_OP_PP_FORWARD 3
 #define FLARE_OP_BACKWARD 4
 #define FLARE_OP_ENCODE_BACKWARD 5
+#define FLARE_OP_PP_BACKWARD 6
 
 /* Scratch bytes that `op` needs for this problem (0 when none); returns 0 for
  * arguments the op would reject.  Depends only on its arguments and on the
@@ -186,6 +187,27 @@ int flare_encode_backward(const void* Q, int q_batched, const void* K, const voi
                           const float* L, const float* dZ, const float* dL, float* dQ, void* dK, void* dV,
                           int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* Backward of the FLARE++ forward (App. B.5, last paragraph; App. A.4 for
+ * the blend): the routing pair's backward gives dK, dV and the cotangent dQ
+ * of the per-batch routing queries; the blend Q = Qf + g Qd gives
+ *   dQf[h] = sum_b dQ[b,h],  dgate[h] = sum_{b,m,d} dQ Qd,  dQd = g dQ;
+ * and dQd is handed once to the synthesis encoder's backward (as
+ * flare_encode_backward with dL = 0), which gives dQs (summed over the
+ * batch), dKs and dVs.  The synthesis latents Qd are recomputed.
+ * Inputs: those of flare_pp_forward (dtype FLARE_BF16 only, inputs already
+ * normalised) plus what it returned for them: Q [B,H,M,D] f32 (its Q_out),
+ * Z [B,H,M,D] f32 and L [B,H,M] f32; dY [B,H,N,D] bf16.
+ * Outputs: dQs, dQf [H,M,D] f32; dgate [H] f32; dKs, dVs, dK, dV [B,H,N,D]
+ * bf16; dQ_out [B,H,M,D] f32 or NULL.  When Vs == Ks (shared synthesis keys
+ * and values, App. A.6) dKs receives the sum of the key and value
+ * cotangents and dVs is not written (it may be NULL).
+ * ws of flare_workspace_size(FLARE_OP_PP_BACKWARD, ...) bytes. */
+int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                      const void* K, const void* V, const float* Q, const float* Z, const float* L, const void* dY,
+                      float* dQs, void* dKs, void* dVs, float* dQf, float* dgate, float* dQ_out, void* dK, void* dV,
+                      int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* flare_status_string(int status);

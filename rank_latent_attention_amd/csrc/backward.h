@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kThreads) center_kernel(const float* Z, float*
 // factor s (applied by the sum).
 // ----------------------------------------------------------------------------
 struct ColArgs {
-  const bf16* Q;        // [H,M,D] or [B,H,M,D]
+  const void* Q;        // [H,M,D] or [B,H,M,D], type QT (bf16, or float32 routing queries)
   const bf16* K;        // [B,H,N,D]
   const bf16* X;        // decode side: dY; encoder side: V   [B,H,N,D]
   const float* lat;     // decode side: Zc; encoder side: dZ  [B,H,M,D]
@@ -162,7 +162,7 @@ __device__ inline f32x16 splat16(float v) {
   return r;
 }
 
-template <int D, int NW, int WN, bool DEC>
+template <typename QT, int D, int NW, int WN, bool DEC>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) bwd_col_kernel(ColArgs a) {
   constexpr int ROWS = dma_rows<NW>();
   constexpr int TE = ROWS * D;                       // elements per tile
@@ -204,7 +204,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     const int m = mg * 32 + li;
     const int mc = m < M ? m : M - 1;
     QKOp<bf16, D> qop, lop;
-    load_op_scaled<D>(qop, a.Q + ((size_t)(a.q_batched ? bh : h) * M + mc) * D, g, a.qscale);
+    load_op_scaled<D>(qop, reinterpret_cast<const QT*>(a.Q) + ((size_t)(a.q_batched ? bh : h) * M + mc) * D, g,
+                      a.qscale);
     load_op_scaled<D>(lop, a.lat + ((size_t)bh * M + mc) * D, g, 1.f);
     if (m >= M) { zero_op<D>(qop); zero_op<D>(lop); }
     f32x16 cp = {}, cg = {};
@@ -404,7 +405,7 @@ __global__ void __launch_bounds__(kThreads) sum_dq_kernel(SumArgs a) {
 //   dK^T += (Q s log2 e)^T dS          (dK = that / log2 e)
 // ----------------------------------------------------------------------------
 struct RowArgs {
-  const bf16* Q;
+  const void* Q;        // type QT
   const bf16* K;
   const bf16* V;        // encoder side
   const bf16* dY;       // decode side
@@ -415,6 +416,7 @@ struct RowArgs {
   const float* c;       // encoder side
   bf16* dK;
   bf16* dV;             // encoder side
+  int v_alias;          // encoder side: V is K, so dK receives dK + dV and dV is not written
   long long total;
   int q_batched, H, N, M, MB, nwg;
   float qscale;
@@ -431,7 +433,7 @@ template <int D> struct RowLds {
 
 // NW waves per workgroup share the staged head: at the largest sizes the
 // LDS holds one workgroup per compute unit, so 8 waves keep two per SIMD.
-template <int D, int NW, bool TAIL, bool DEC, bool ENC>
+template <typename QT, int D, int NW, bool TAIL, bool DEC, bool ENC>
 __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
   constexpr int NT = NW * 64;
   using RL = RowLds<D>;
@@ -459,11 +461,11 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
 
     __syncthreads();  // the previous piece is done with the staged head
     {
-      const bf16* Qh = a.Q + (size_t)(a.q_batched ? bh : h) * M * D;
+      const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
       for (int e = threadIdx.x; e < Mp * D; e += NT) {
         const int m = e / D, d = e % D;
         const bool in = m < M;
-        const bf16 q = (bf16)(in ? (float)Qh[(size_t)m * D + d] * a.qscale : 0.f);
+        const bf16 q = (bf16)(in ? to_f(Qh[(size_t)m * D + d]) * a.qscale : 0.f);
         qs[m * RL::RST + d] = q;
         qt[d * tst + m] = q;
         if constexpr (DEC) zr[m * RL::RST + d] = (bf16)(in ? a.Zc[((size_t)bh * M + m) * D + d] : 0.f);
@@ -542,15 +544,19 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
       }
       constexpr float kInvLog2e = 0.69314718055994531f;
       bf16* dk = a.dK + ((size_t)bh * N + n) * D;
-      bf16* dv = ENC ? a.dV + ((size_t)bh * N + n) * D : nullptr;
+      bf16* dv = ENC && !a.v_alias ? a.dV + ((size_t)bh * N + n) * D : nullptr;
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         if (8 * c4 + 4 * g < D) {
           bf16x4 u;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) u[i] = (bf16)(acck[4 * c4 + i] * kInvLog2e);
+          for (int i = 0; i < 4; ++i) {
+            float v = acck[4 * c4 + i] * kInvLog2e;
+            if constexpr (ENC) v += a.v_alias ? accv[4 * c4 + i] : 0.f;
+            u[i] = (bf16)v;
+          }
           *reinterpret_cast<bf16x4*>(dk + 8 * c4 + 4 * g) = u;
-          if constexpr (ENC) {
+          if (ENC && !a.v_alias) {
             bf16x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = (bf16)accv[4 * c4 + i];
@@ -594,44 +600,55 @@ size_t row_lds(int D, int M) {
   return D == 16 ? RowLds<16>::bytes(MB) : RowLds<32>::bytes(MB);
 }
 
-template <int D, int NW, int WN, bool DEC>
+template <typename QT, int D, int NW, int WN, bool DEC>
 int launch_col_k(const ColArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_col_kernel<D, NW, WN, DEC>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((bwd_col_kernel<QT, D, NW, WN, DEC>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <int D, bool DEC>
+template <typename QT, int D, bool DEC>
 int launch_col_d(const ColArgs& a, int NW, int WN, hipStream_t st) {
-  if (NW == 8) return launch_col_k<D, 8, 1, DEC>(a, st);
-  if (WN == 4) return launch_col_k<D, 4, 4, DEC>(a, st);
-  if (WN == 2) return launch_col_k<D, 4, 2, DEC>(a, st);
-  return launch_col_k<D, 4, 1, DEC>(a, st);
+  if (NW == 8) return launch_col_k<QT, D, 8, 1, DEC>(a, st);
+  if (WN == 4) return launch_col_k<QT, D, 4, 4, DEC>(a, st);
+  if (WN == 2) return launch_col_k<QT, D, 4, 2, DEC>(a, st);
+  return launch_col_k<QT, D, 4, 1, DEC>(a, st);
 }
 
-int launch_col(const ColArgs& a, int D, bool dec, const EncPlan& p, hipStream_t st) {
-  if (dec) return D == 16 ? launch_col_d<16, true>(a, p.NW, p.WN, st) : launch_col_d<32, true>(a, p.NW, p.WN, st);
-  return D == 16 ? launch_col_d<16, false>(a, p.NW, p.WN, st) : launch_col_d<32, false>(a, p.NW, p.WN, st);
+template <typename QT>
+int launch_col_q(const ColArgs& a, int D, bool dec, const EncPlan& p, hipStream_t st) {
+  if (dec)
+    return D == 16 ? launch_col_d<QT, 16, true>(a, p.NW, p.WN, st) : launch_col_d<QT, 32, true>(a, p.NW, p.WN, st);
+  return D == 16 ? launch_col_d<QT, 16, false>(a, p.NW, p.WN, st) : launch_col_d<QT, 32, false>(a, p.NW, p.WN, st);
+}
+
+// qf32: the queries are float32 (FLARE++ routing), else bf16.
+int launch_col(const ColArgs& a, int D, bool dec, bool qf32, const EncPlan& p, hipStream_t st) {
+  return qf32 ? launch_col_q<float>(a, D, dec, p, st) : launch_col_q<bf16>(a, D, dec, p, st);
 }
 
 constexpr int kRowWaves = 8;
 
-template <int D, bool TAIL, bool DEC, bool ENC>
+template <typename QT, int D, bool TAIL, bool DEC, bool ENC>
 int launch_row_k(const RowArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)bwd_row_kernel<D, kRowWaves, TAIL, DEC, ENC>;
+  const void* fn = (const void*)bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((bwd_row_kernel<D, kRowWaves, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st, a);
+  hipLaunchKernelGGL((bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st,
+                     a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <int D, bool DEC, bool ENC>
+template <typename QT, int D, bool DEC, bool ENC>
 int launch_row_t(const RowArgs& a, size_t lds, hipStream_t st) {
-  return (a.M & 31) ? launch_row_k<D, true, DEC, ENC>(a, lds, st) : launch_row_k<D, false, DEC, ENC>(a, lds, st);
+  return (a.M & 31) ? launch_row_k<QT, D, true, DEC, ENC>(a, lds, st)
+                    : launch_row_k<QT, D, false, DEC, ENC>(a, lds, st);
 }
 
-int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, hipStream_t st) {
+// Both sides (FLARE, FLARE++ routing; bf16 or float32 queries) or the
+// encoder side alone (bf16 queries).
+int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, bool qf32, hipStream_t st) {
   const size_t lds = row_lds(D, a.M);
   if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   // LDS-resident workgroups per compute unit (160 KB of LDS each)
@@ -639,13 +656,28 @@ int launch_row(const Dev& dev, RowArgs a, int D, bool dec, bool enc, hipStream_t
   const long long want = (long long)dev.cus * per_cu;
   const long long maxw = cdiv(a.total, 32);
   a.nwg = (int)(want < maxw ? want : maxw);
-  if (dec && enc) return D == 16 ? launch_row_t<16, true, true>(a, lds, st) : launch_row_t<32, true, true>(a, lds, st);
-  if (enc) return D == 16 ? launch_row_t<16, false, true>(a, lds, st) : launch_row_t<32, false, true>(a, lds, st);
-  return D == 16 ? launch_row_t<16, true, false>(a, lds, st) : launch_row_t<32, true, false>(a, lds, st);
+  if (dec && enc) {
+    if (qf32)
+      return D == 16 ? launch_row_t<float, 16, true, true>(a, lds, st) : launch_row_t<float, 32, true, true>(a, lds, st);
+    return D == 16 ? launch_row_t<bf16, 16, true, true>(a, lds, st) : launch_row_t<bf16, 32, true, true>(a, lds, st);
+  }
+  if (enc && !qf32)
+    return D == 16 ? launch_row_t<bf16, 16, false, true>(a, lds, st) : launch_row_t<bf16, 32, false, true>(a, lds, st);
+  return FLARE_ERR_UNSUPPORTED;
 }
 
-int launch_stats(const Dev& dev, const bf16* Q, int q_batched, const bf16* K, const float* Zc, const bf16* dY,
-                 uint4* srec, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
+template <typename QT>
+int launch_stats_q(const DecArgs& a, size_t lds, int D, hipStream_t st) {
+  const bool tail = a.M & 31;
+  if (D == 16)
+    return tail ? launch_decode_k<bf16, QT, 16, true, false, true>(a, lds, st)
+                : launch_decode_k<bf16, QT, 16, false, false, true>(a, lds, st);
+  return tail ? launch_decode_k<bf16, QT, 32, true, false, true>(a, lds, st)
+              : launch_decode_k<bf16, QT, 32, false, false, true>(a, lds, st);
+}
+
+int launch_stats(const Dev& dev, const void* Q, bool qf32, int q_batched, const bf16* K, const float* Zc,
+                 const bf16* dY, uint4* srec, int BH, int H, int N, int M, int D, float qscale, hipStream_t st) {
   DecArgs a{};
   a.Q = Q; a.K = K; a.Z = Zc; a.Y = nullptr;
   a.total = (long long)BH * N;
@@ -658,20 +690,17 @@ int launch_stats(const Dev& dev, const bf16* Q, int q_batched, const bf16* K, co
   a.nwg = (int)(want < maxw ? want : maxw);
   const size_t lds = decode_lds(FLARE_BF16, D, M);
   if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
-  const bool tail = M & 31;
-  if (D == 16)
-    return tail ? launch_decode_k<bf16, bf16, 16, true, false, true>(a, lds, st)
-                : launch_decode_k<bf16, bf16, 16, false, false, true>(a, lds, st);
-  return tail ? launch_decode_k<bf16, bf16, 32, true, false, true>(a, lds, st)
-              : launch_decode_k<bf16, bf16, 32, false, false, true>(a, lds, st);
+  return qf32 ? launch_stats_q<float>(a, lds, D, st) : launch_stats_q<bf16>(a, lds, D, st);
 }
 
-// The backward of the encoder (enc), of the decoder (dec) or of both (FLARE),
-// one stream.  dZ_in (encoder only): the given cotangent of Z; dL: of L.
-int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, const bf16* K, const bf16* V,
-             const float* Z, const float* L, const bf16* dY, const float* dZ_in, const float* dL, float* dQ,
-             bf16* dK, bf16* dV, float* dZ_out, int B, int H, int N, int M, int D, float scale, char* ws,
-             const BwdLayout& w, hipStream_t st) {
+// The backward of the encoder alone (dec false) or of both sides (FLARE),
+// one stream.  Q is float32 when qf32 (FLARE++ routing queries), else bf16.
+// dZ_in (encoder alone): the given cotangent of Z; dL: of L.  v_alias
+// (encoder alone): V is K, and dK receives the sum of both cotangents.
+int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q_batched, const bf16* K,
+             const bf16* V, const float* Z, const float* L, const bf16* dY, const float* dZ_in, const float* dL,
+             float* dQ, bf16* dK, bf16* dV, bool v_alias, float* dZ_out, int B, int H, int N, int M, int D,
+             float scale, char* ws, const BwdLayout& w, hipStream_t st) {
   const int BH = B * H;
   const float qs = scale * kLog2e;
   const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
@@ -695,12 +724,12 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
     if (dec) {
       hipLaunchKernelGGL(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
       if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
-      rc = launch_stats(dev, Q, q_batched, K, zc, dY, srec, BH, H, N, M, D, qs, st);
+      rc = launch_stats(dev, Q, qf32, q_batched, K, zc, dY, srec, BH, H, N, M, D, qs, st);
       if (rc) return rc;
       ColArgs cd = ca;
       cd.X = dY; cd.lat = zc; cd.srec = srec; cd.part_dz = (float*)(ws + w.part_dz);
       cd.accumulate = 0;
-      rc = launch_col(cd, D, true, p, st);
+      rc = launch_col(cd, D, true, qf32, p, st);
       if (rc) return rc;
       sa.part = cd.part_dz;
     } else {
@@ -716,7 +745,7 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   if (N > 0 && enc) {
     ColArgs ce = ca;
     ce.X = V; ce.lat = dz; ce.L = L; ce.c = c; ce.accumulate = dec ? 1 : 0;
-    rc = launch_col(ce, D, false, p, st);
+    rc = launch_col(ce, D, false, qf32, p, st);
     if (rc) return rc;
   }
   SumArgs sq = sa;
@@ -728,11 +757,78 @@ int backward(const Dev& dev, bool dec, bool enc, const bf16* Q, int q_batched, c
   RowArgs ra{};
   ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.srec = srec; ra.dZ = dz; ra.L = L;
   ra.c = c;
-  ra.dK = dK; ra.dV = dV;
+  ra.dK = dK; ra.dV = dV; ra.v_alias = v_alias ? 1 : 0;
   ra.total = (long long)BH * N;
   ra.q_batched = q_batched; ra.H = H; ra.N = N; ra.M = M; ra.MB = (int)cdiv(M, 32);
   ra.qscale = qs;
-  return launch_row(dev, ra, D, dec, enc, st);
+  return launch_row(dev, ra, D, dec, enc, qf32, st);
+}
+
+// ----------------------------------------------------------------------------
+// FLARE++ blend, reverse mode (FLARE++ paper, App. A.4 and B.5): with
+// Q[b,h] = Qf[h] + g_h Qd[b,h] and the routing queries' cotangent dQ,
+//   dQf[h] = sum_b dQ[b,h],  dg_h = sum_{b,m,d} dQ Qd,  dQd = g_h dQ.
+// One workgroup per head; every sum runs in a fixed order.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) blend_backward_kernel(const float* dQ, const float* Qd, const float* gate,
+                                                                  float* dQd, float* dQf, float* dgate, int B,
+                                                                  int H, int M, int D) {
+  __shared__ float red[kThreads];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int MD = M * D;
+  const float g = gate[h];
+  float part = 0.f;
+  for (int e = t; e < MD; e += kThreads) {
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) {
+      const size_t i = ((size_t)b * H + h) * MD + e;
+      const float dq = dQ[i];
+      s += dq;
+      part += dq * Qd[i];
+      dQd[i] = g * dq;
+    }
+    dQf[(size_t)h * MD + e] = s;
+  }
+  red[t] = part;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) dgate[h] = red[0];
+}
+
+// Workspace of flare_pp_backward: one region reused by the synthesis
+// recomputation, the routing backward and the synthesis backward (they run
+// in that order on one stream), then the synthesis latents and
+// log-normalisers, the routing queries' cotangent and the synthesis
+// latents' cotangent.
+struct PpBwdLayout {
+  size_t region = 0, zs = 0, ls = 0, dq = 0, dqd = 0, total = 0;
+  size_t part_acc = 0, part_al = 0;  // the recomputation's split partials, inside the region
+};
+
+PpBwdLayout pp_bwd_layout(const Dev& dev, int B, int H, int N, int M, int D) {
+  PpBwdLayout w;
+  const int BH = B * H;
+  const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  const size_t acc = align256((size_t)BH * p.pmax * M * D * sizeof(float));
+  const size_t al = align256((size_t)BH * p.pmax * M * sizeof(float2));
+  size_t r = acc + al;
+  const size_t r1 = bwd_layout(dev, true, B, H, N, M, D).total;
+  const size_t r2 = bwd_layout(dev, false, B, H, N, M, D).total;
+  r = r > r1 ? r : r1;
+  r = r > r2 ? r : r2;
+  const size_t lat = align256((size_t)BH * M * D * sizeof(float));
+  w.part_acc = 0;
+  w.part_al = acc;
+  w.region = 0;
+  w.zs = r;
+  w.ls = w.zs + lat;
+  w.dq = w.ls + align256((size_t)BH * M * sizeof(float));
+  w.dqd = w.dq + lat;
+  w.total = w.dqd + lat;
+  return w;
 }
 
 }  // namespace
@@ -757,8 +853,8 @@ int flare_backward(const void* Q, int q_batched, const void* K, const void* V, c
   if (row_lds(D, M) > dev.lds_max || decode_lds(FLARE_BF16, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const BwdLayout w = bwd_layout(dev, true, B, H, N, M, D);
   if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
-  return backward(dev, true, true, (const bf16*)Q, q_batched, (const bf16*)K, (const bf16*)V, Z, L, (const bf16*)dY,
-                  nullptr, nullptr, dQ, (bf16*)dK, (bf16*)dV, dZ_out, B, H, N, M, D, pick_scale(scale, D),
+  return backward(dev, true, true, Q, false, q_batched, (const bf16*)K, (const bf16*)V, Z, L, (const bf16*)dY,
+                  nullptr, nullptr, dQ, (bf16*)dK, (bf16*)dV, false, dZ_out, B, H, N, M, D, pick_scale(scale, D),
                   (char*)ws, w, (hipStream_t)stream);
 }
 
@@ -777,9 +873,62 @@ int flare_encode_backward(const void* Q, int q_batched, const void* K, const voi
   if (row_lds(D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const BwdLayout w = bwd_layout(dev, false, B, H, N, M, D);
   if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
-  return backward(dev, false, true, (const bf16*)Q, q_batched, (const bf16*)K, (const bf16*)V, Z, L, nullptr, dZ,
-                  dL, dQ, (bf16*)dK, (bf16*)dV, nullptr, B, H, N, M, D, pick_scale(scale, D), (char*)ws, w,
+  return backward(dev, false, true, Q, false, q_batched, (const bf16*)K, (const bf16*)V, Z, L, nullptr, dZ, dL, dQ,
+                  (bf16*)dK, (bf16*)dV, false, nullptr, B, H, N, M, D, pick_scale(scale, D), (char*)ws, w,
                   (hipStream_t)stream);
+}
+
+int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                      const void* K, const void* V, const float* Q, const float* Z, const float* L, const void* dY,
+                      float* dQs, void* dKs, void* dVs, float* dQf, float* dgate, float* dQ_out, void* dK, void* dV,
+                      int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_common(B, H, N, M, D, dtype, 0);
+  if (rc) return rc;
+  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
+  const bool alias = Ks == Vs;
+  if (!Qs || !Qf || !gate || !Q || !Z || !L || !dQs || !dQf || !dgate) return FLARE_ERR_INVALID_ARG;
+  if (N > 0 && (!Ks || !Vs || !K || !V || !dY || !dKs || (!alias && !dVs) || !dK || !dV)) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, dQs, dKs, dVs, dQf, dgate, dQ_out, dK, dV, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  if (row_lds(D, M) > dev.lds_max || decode_lds(FLARE_BF16, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const PpBwdLayout w = pp_bwd_layout(dev, B, H, N, M, D);
+  if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  hipStream_t st = (hipStream_t)stream;
+  const float s = pick_scale(scale, D);
+  const int BH = B * H;
+  float* Zs = (float*)(wsc + w.zs);
+  float* Ls = (float*)(wsc + w.ls);
+  float* dQb = dQ_out ? dQ_out : (float*)(wsc + w.dq);
+  float* dQd = (float*)(wsc + w.dqd);
+  // 1. the synthesis latents Qd = SDPA(Qs, Ks, Vs) and their log-normalisers
+  const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  if (N > 0) {
+    rc = launch_encode(Qs, FLARE_BF16, 0, Ks, Vs, 0, H, N, M, D, FLARE_BF16, s * kLog2e, (float*)(wsc + w.part_acc),
+                       (float2*)(wsc + w.part_al), p, Norms{}, st);
+    if (rc) return rc;
+  }
+  rc = launch_merge(p, (float*)(wsc + w.part_acc), (float2*)(wsc + w.part_al), 0, BH, H, N, M, D, Zs, Ls, nullptr,
+                    FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+  if (rc) return rc;
+  // 2. the routing pair's backward with the float32 per-batch queries
+  const BwdLayout wr = bwd_layout(dev, true, B, H, N, M, D);
+  rc = backward(dev, true, true, Q, true, 1, (const bf16*)K, (const bf16*)V, Z, L, (const bf16*)dY, nullptr, nullptr,
+                dQb, (bf16*)dK, (bf16*)dV, false, nullptr, B, H, N, M, D, s, wsc + w.region, wr, st);
+  if (rc) return rc;
+  // 3. the blend
+  hipLaunchKernelGGL(blend_backward_kernel, dim3(H), dim3(kThreads), 0, st, dQb, Zs, gate, dQd, dQf, dgate, B, H, M,
+                     D);
+  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  // 4. the synthesis encoder's backward with dZ = dQd (dL = 0), the seeds
+  //    shared over the batch
+  const BwdLayout we = bwd_layout(dev, false, B, H, N, M, D);
+  return backward(dev, false, true, Qs, false, 0, (const bf16*)Ks, (const bf16*)Vs, Zs, Ls, nullptr, dQd, nullptr,
+                  dQs, (bf16*)dKs, (bf16*)dVs, alias, nullptr, B, H, N, M, D, s, wsc + w.region, we, st);
 }
 
 }  // extern "C"

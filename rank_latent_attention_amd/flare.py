@@ -23,7 +23,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libflare.so")
 
 F32, BF16 = 0, 1
-OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD, OP_BACKWARD, OP_ENCODE_BACKWARD = 0, 1, 2, 3, 4, 5
+OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD, OP_BACKWARD, OP_ENCODE_BACKWARD, OP_PP_BACKWARD = 0, 1, 2, 3, 4, 5, 6
 #: input normalisation flags of flare_pp_forward_norm (include/flare.h)
 NORM_QS, NORM_KS, NORM_QF, NORM_K = 1, 2, 4, 8
 NORM_FLAREPP = NORM_QS | NORM_KS | NORM_QF | NORM_K  # FLARE++ (Table 2)
@@ -32,7 +32,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
-           "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_status_string")
+           "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_pp_backward",
+           "flare_status_string")
 
 _lib = None
 
@@ -62,8 +63,9 @@ def load(path: str = LIB_PATH):
                                         vp, sz, vp]
     L.flare_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_encode_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_pp_backward.argtypes = [vp] * 19 + [i, i, i, i, i, i, f, vp, sz, vp]
     for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm,
-               L.flare_backward, L.flare_encode_backward):
+               L.flare_backward, L.flare_encode_backward, L.flare_pp_backward):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -278,3 +280,43 @@ def flare_encode_backward(Q, K, V, Z, L, dZ, dL=None, scale: float = 0.0, dQ=Non
                                       0 if ws is None else ws.numel(), _stream(K.device))
     _check("flare_encode_backward", rc)
     return dQ, dK, dV
+
+
+def flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, scale: float = 0.0, dQ_out=None, ws=None):
+    """Backward of the FLARE++ forward (flare_pp_backward in include/flare.h).
+    Q, Z, L are the forward's routing queries (its Q_out), latents and
+    log-normalisers for the same inputs.  Returns
+    (dQs, dKs, dVs, dQf, dgate, dK, dV, dQ_out); dVs is None when Vs is Ks
+    (its cotangent is then added into dKs), dQ_out only when passed in."""
+    if K.dim() != 4:
+        raise ValueError("K must be [B,H,N,D]")
+    B, H, N, D = K.shape
+    if Qs.dim() != 3 or Qs.shape[0] != H or Qs.shape[2] != D or Qf.shape != Qs.shape:
+        raise ValueError("Qs and Qf must be [H,M,D]")
+    M = Qs.shape[1]
+    dt = _dtype_code(K)
+    for t in (Qs, Ks, Vs, Qf, V, dY):
+        if t.dtype != K.dtype:
+            raise ValueError("Qs, Ks, Vs, Qf, K, V, dY must share one dtype")
+    if Ks.shape != K.shape or Vs.shape != K.shape or V.shape != K.shape or dY.shape != K.shape:
+        raise ValueError("Ks, Vs, K, V, dY must all be [B,H,N,D]")
+    if gate.dtype != torch.float32 or gate.numel() != H:
+        raise ValueError("gate must be float32 [H]")
+    for t, shp in ((Q, (B, H, M, D)), (Z, (B, H, M, D)), (L, (B, H, M))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp:
+            raise ValueError("Q, Z must be float32 [B,H,M,D] and L float32 [B,H,M]")
+    alias = Vs.data_ptr() == Ks.data_ptr()
+    dev = K.device
+    dQs = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+    dQf = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+    dgate = torch.empty((H,), dtype=torch.float32, device=dev)
+    dKs, dK, dV = torch.empty_like(K), torch.empty_like(K), torch.empty_like(K)
+    dVs = None if alias else torch.empty_like(K)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out)
+    ws = workspace(OP_PP_BACKWARD, B, H, N, M, D, dt, dev) if ws is None else ws
+    rc = load().flare_pp_backward(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Q),
+                                  _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQs), _ptr(dKs), _ptr(dVs), _ptr(dQf),
+                                  _ptr(dgate), _ptr(dQ_out), _ptr(dK), _ptr(dV), B, H, N, M, D, dt, float(scale),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check("flare_pp_backward", rc)
+    return dQs, dKs, dVs, dQf, dgate, dK, dV, dQ_out

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
                                            "flare_pp_forward", "flare_pp_forward_norm", "flare_backward",
-                                           "flare_encode_backward", "flare_status_string"])
+                                           "flare_encode_backward", "flare_pp_backward", "flare_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -117,3 +117,17 @@ def test_encode_backward_rejects_bad_arguments(lib):
     assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 0, 0.0, FAKE, 1 << 30,
               None) == 2
     assert lib.flare_workspace_size(4, 1, 1, 8, 8, 16, 0) == 0   # the backward is bf16 only
+
+
+def ppb(lib, dt=1, D=16, Vs=FAKE, dVs=FAKE, Q=FAKE, dgate=FAKE, dQo=None):
+    return lib.flare_pp_backward(FAKE, FAKE, Vs, FAKE, FAKE, FAKE, FAKE, Q, FAKE, FAKE, FAKE, FAKE, FAKE, dVs, FAKE,
+                                 dgate, dQo, FAKE, FAKE, 1, 1, 8, 8, D, dt, 0.0, FAKE, 1 << 30, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=0), 2), (dict(D=20), 2), (dict(Q=None), 1), (dict(dgate=None), 1),
+    (dict(Vs=ctypes.c_void_p(2 << 20), dVs=None), 1),   # separate synthesis values need their cotangent
+    (dict(dQo=MISALIGNED), 1),
+])
+def test_pp_backward_rejects_bad_arguments(lib, kw, status):
+    assert ppb(lib, **kw) == status

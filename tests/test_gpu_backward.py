@@ -1,10 +1,11 @@
-"""GPU parity of the backward (flare_backward, flare_encode_backward through
-the C ABI) against the fp64 oracle's flare_backward / encode_backward.
+"""GPU parity of the backward (flare_backward, flare_encode_backward and
+flare_pp_backward through the C ABI) against the fp64 oracle's
+flare_backward, encode_backward and flare_pp_backward.
 
-The forward runs on the GPU first (its Z and L are what the backward takes,
-as in training); the oracle recomputes everything from the same bf16 inputs
-in fp64.  Bar: rel-L2 1e-2 on dQ, dK, dV and dZ (bf16 inputs, float32
-accumulation, bf16 matrix-core operands).
+The forward runs on the GPU first (its Z, L and, for FLARE++, routing
+queries are what the backward takes, as in training); the oracle recomputes
+everything from the same bf16 inputs in fp64.  Bar: rel-L2 1e-2 on every
+gradient (bf16 inputs, float32 accumulation, bf16 matrix-core operands).
 """
 import sys
 
@@ -174,3 +175,77 @@ def test_million_token_backward_one_head(flare, orc):
     ref = orc.flare_backward(w.Q[sl], w.K[:, sl], w.V[:, sl], dY[:, sl], return_dZ=True)
     for n, g, r in zip(("dQ", "dK", "dV", "dZ"), (dQ[sl], dK[:, sl], dV[:, sl], dZ[:, sl]), ref):
         check(f"head {h} {n}", g, r)
+
+
+# --- FLARE++ (App. B.5: the synthesis encoder receives the reduced query cotangent) ---
+
+def gpu_pp_backward(flare, w, dY, shared=True):
+    """GPU FLARE++ forward then backward; returns the host gradients in the
+    oracle's order (dQs, dKs, dVs or None, dQf, dgate, dK, dV)."""
+    import torch
+    d = "bf16"
+    Qs, Ks, Qf, K, V = dev(w.Qs, d), dev(w.Ks, d), dev(w.Qf, d), dev(w.K, d), dev(w.V, d)
+    Vs = Ks if shared else dev(w.Vs, d)
+    gate = dev(w.gate, "f32")
+    B, H, N, D = K.shape
+    M = Qs.shape[1]
+    Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    flare.flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)
+    out = flare.flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, Qo, Z, L, dev(dY, d))
+    torch.cuda.synchronize()
+    return tuple(None if x is None else host(x) for x in out[:7])
+
+
+PP_NAMES = ("dQs", "dKs", "dVs", "dQf", "dgate", "dK", "dV")
+
+
+def compare_pp(got, ref, prefix=""):
+    for n, g, r in zip(PP_NAMES, got, ref):
+        if r is None:
+            assert g is None, n
+            continue
+        assert np.all(np.isfinite(g)), n
+        check(prefix + n, g, r)
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 3000, 64, 32, True), (2, 2, 3000, 64, 32, False),
+                                   (1, 3, 1000, 48, 16, True), (2, 1, 777, 33, 32, False)],
+                         ids=lambda s: "B{}H{}N{}M{}D{}shared{}".format(*s))
+def test_pp_backward(flare, orc, shape):
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian_pp
+    B, H, N, M, D, shared = shape
+    w = make_gaussian_pp(B, H, N, M, D, "bf16", seed=111, share_vs=shared)
+    dY = cotangent(112, "dy", w.K.shape)
+    say(f"[pp backward] B{B} H{H} N{N} M{M} D{D} shared {shared}")
+    got = gpu_pp_backward(flare, w, dY, shared)
+    ref = orc.flare_pp_backward(w.Qs, w.Ks, w.Ks if shared else w.Vs, w.Qf, w.gate, w.K, w.V, dY, shared_vs=shared)
+    compare_pp(got, ref)
+
+
+def test_pp_backward_long_sequence_workload(flare, orc):
+    # the long-sequence classification workload (B32 H4 N4096 M64 D32), whole
+    from rank_latent_attention_amd.inputs import config4, cotangent
+    w = config4()
+    dY = cotangent(113, "dy", w.K.shape)
+    say(f"[pp backward] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D}")
+    got = gpu_pp_backward(flare, w, dY, True)
+    ref = orc.flare_pp_backward(w.Qs, w.Ks, w.Ks, w.Qf, w.gate, w.K, w.V, dY, shared_vs=True)
+    compare_pp(got, ref)
+
+
+def test_pp_million_token_backward_one_head(flare, orc):
+    # the million-point FLARE++ workload launched whole; one head checked in
+    # full (dQs, dQf, dgate and dZ-like reductions run over all 2^20 tokens)
+    from rank_latent_attention_amd.inputs import config5, cotangent
+    w = config5(True)
+    dY = cotangent(114, "dy", w.K.shape)
+    say(f"[c5pp backward] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D}")
+    got = gpu_pp_backward(flare, w, dY, True)
+    h = 6
+    sl = slice(h, h + 1)
+    ref = orc.flare_pp_backward(w.Qs[sl], w.Ks[:, sl], w.Ks[:, sl], w.Qf[sl], w.gate[sl], w.K[:, sl], w.V[:, sl],
+                                dY[:, sl], shared_vs=True)
+    heads = (got[0][sl], got[1][:, sl], None, got[3][sl], got[4][sl], got[5][:, sl], got[6][:, sl])
+    compare_pp(heads, ref, prefix=f"head {h} ")
