@@ -169,17 +169,24 @@ def time_configs(names: str) -> None:
 
 
 def cpu_baseline_backward(w, dY, target_s: float = 15.0):
-    """The fp64 oracle of the FLARE backward (forward recompute, decoder and
-    encoder backward) on a bounded sample: the first n tokens of head 0, n
-    chosen from a 2^16-token timing so the sample takes about target_s."""
+    """The fp64 oracle of the FLARE (or FLARE++) backward (forward recompute,
+    decoder and encoder backward, and for FLARE++ the blend and synthesis
+    backward) on a bounded sample: the first n tokens of head 0, n chosen
+    from a 2^16-token timing so the sample takes about target_s."""
     import oracle
     oracle.build(force=False)
     cores = oracle.threads()
 
+    def tok(x, n):
+        return np.ascontiguousarray(x[:, :1, :n])
+
     def run(n):
         t0 = time.perf_counter()
-        oracle.flare_backward(w.Q[:1], np.ascontiguousarray(w.K[:, :1, :n]), np.ascontiguousarray(w.V[:, :1, :n]),
-                              np.ascontiguousarray(dY[:, :1, :n]))
+        if w.pp:
+            Ks = tok(w.Ks, n)
+            oracle.flare_pp_backward(w.Qs[:1], Ks, Ks, w.Qf[:1], w.gate[:1], tok(w.K, n), tok(w.V, n), tok(dY, n))
+        else:
+            oracle.flare_backward(w.Q[:1], tok(w.K, n), tok(w.V, n), tok(dY, n))
         return time.perf_counter() - t0
 
     n1 = min(w.N, 1 << 16)
@@ -188,7 +195,8 @@ def cpu_baseline_backward(w, dY, target_s: float = 15.0):
     t = run(n) if n > n1 else t1
     value = w.B * n / (t * w.H)   # a token of the whole pass needs all H heads
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle FLARE backward (forward recompute, decoder and encoder backward) on head 0 of "
+            "sample": f"fp64 oracle {'FLARE++' if w.pp else 'FLARE'} backward (forward recompute, decoder and "
+                      f"encoder backward{', blend and synthesis backward' if w.pp else ''}) on head 0 of "
                       f"{w.H}, first {n} of {w.N} tokens, M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; "
                       f"tokens/s scaled by 1/{w.H} heads (the work is linear in the token count)"}
 
@@ -200,10 +208,12 @@ def main():
     # MFMA + transcendental load; 30 warmup steps (about 90 launches) reach it
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_backward"], default="flare",
+    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_backward", "flare_pp_backward"],
+                    default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
                          "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels; "
-                         "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward")
+                         "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward; "
+                         "flare_pp_backward the FLARE++ backward likewise")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--configs", default="",
                     help="instead of the bench line, time the forward of these workloads (comma-separated names "
@@ -225,8 +235,8 @@ def main():
     if args.configs:
         time_configs(args.configs)
         return
-    if args.workload == "flare_backward":
-        bench_backward(args)
+    if args.workload in ("flare_backward", "flare_pp_backward"):
+        bench_backward(args, pp=args.workload == "flare_pp_backward")
         return
 
     pp = args.workload in ("flare_pp", "flare_pp_norm")
@@ -350,16 +360,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_backward(args):
+def bench_backward(args, pp=False):
     """One step = one flare_backward call (center, statistics, decode-side
     col pass, dZ sum, encoder-side col pass, dQ sum, row pass) over the
-    million-point workload, given Z and L of one untimed forward."""
+    million-point workload, given Z and L of one untimed forward; with pp,
+    one flare_pp_backward call (synthesis recomputation, that routing
+    backward with float32 queries, blend backward, synthesis encoder
+    backward) given the routing queries, Z and L of one untimed FLARE++
+    forward."""
     import torch
     import rank_latent_attention_amd as flare
     from rank_latent_attention_amd.inputs import config5, cotangent
     t0 = time.perf_counter()
-    w = config5(pp=False)
-    dYh = cotangent(101, "dy", w.K.shape)
+    w = config5(pp=pp)
+    dYh = cotangent(114 if pp else 101, "dy", w.K.shape)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
 
@@ -367,16 +381,27 @@ def bench_backward(args):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
 
     B, H, N, M, D = w.B, w.H, w.N, w.M, w.D
-    Q, K, V, dY = up(w.Q), up(w.K), up(w.V), up(dYh)
+    K, V, dY = up(w.K), up(w.V), up(dYh)
     Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
     L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
-    flare.flare_forward(Q, K, V, Z=Z, L=L)
-    dQ = torch.empty((H, M, D), dtype=torch.float32, device=dev)
-    dK, dV = torch.empty_like(K), torch.empty_like(K)
-    ws = flare.workspace(flare.flare.OP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
+    if pp:
+        Qs, Ks, Qf = up(w.Qs), up(w.Ks), up(w.Qf)
+        gate = torch.from_numpy(w.gate).to(dev)
+        Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+        flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)
+        ws = flare.workspace(flare.flare.OP_PP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
 
-    def step():
-        flare.flare_backward(Q, K, V, Z, L, dY, dQ=dQ, dK=dK, dV=dV, ws=ws)
+        def step():
+            flare.flare_pp_backward(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dY, ws=ws)
+    else:
+        Q = up(w.Q)
+        flare.flare_forward(Q, K, V, Z=Z, L=L)
+        dQ = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+        dK, dV = torch.empty_like(K), torch.empty_like(K)
+        ws = flare.workspace(flare.flare.OP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
+
+        def step():
+            flare.flare_backward(Q, K, V, Z, L, dY, dQ=dQ, dK=dK, dV=dV, ws=ws)
 
     stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
@@ -395,23 +420,26 @@ def bench_backward(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} steps: {ms:.3f} ms/step")
-    # Algorithmic FLOPs: the backward of each of the two attention passes is
-    # five products of 2 BHNMD each (scores recomputed, the output-cotangent
-    # product, and the three gradients), 20 BHNMD for the pair.  The kernels
-    # of one call are reached only through the whole entry point, so the
-    # roofline is the step's; per-kernel times are in the kernel trace.
-    flops = 20.0 * B * H * N * M * D
+    # Algorithmic FLOPs: the backward of each attention pass is five
+    # products of 2 BHNMD each (scores recomputed, the output-cotangent
+    # product, and the three gradients): 20 BHNMD for the FLARE pair, 30 with
+    # the FLARE++ synthesis pass.  The kernels of one call are reached only
+    # through the whole entry point, so the roofline is the step's; per-kernel
+    # times are in the kernel trace.
+    flops = (30.0 if pp else 20.0) * B * H * N * M * D
     achieved = flops / (ms * 1e-3) / 1e12
-    kb = 5 * B * H * N * D * 2   # read K, V, dY and write dK, dV once each, bf16
+    # read K, V, dY (and the synthesis keys = values) and write dK, dV (and dKs) once each, bf16
+    kb = (7 if pp else 5) * B * H * N * D * 2
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("whole_step", args.workload),
-                "kernel": "whole step (7 launches)", "kernel_us": round(ms * 1e3, 2), "algorithmic_bytes": kb,
-                "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                "kernel": "whole step (%d launches)" % (13 if pp else 7), "kernel_us": round(ms * 1e3, 2),
+                "algorithmic_bytes": kb, "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    what = "FLARE++" if pp else "FLARE"
     out = {"metric": METRIC_BWD, "value": B * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "FLARE routing backward, million-point surface mesh", "B": B, "H": H, "N": N,
+           "config": {"workload": f"{what} routing backward, million-point surface mesh", "B": B, "H": H, "N": N,
                       "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
            "tflops": round(achieved, 2), "roofline": roofline}
     if not args.no_cpu:
