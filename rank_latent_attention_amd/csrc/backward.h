@@ -163,7 +163,7 @@ __device__ inline f32x16 splat16(float v) {
 }
 
 template <typename QT, int D, int NW, int WN, bool DEC>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) bwd_col_kernel(ColArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) bwd_col_kernel(ColArgs a) {
   constexpr int ROWS = dma_rows<NW>();
   constexpr int TE = ROWS * D;                       // elements per tile
   constexpr unsigned BUFB = 2 * TE * sizeof(bf16);   // bytes between the two buffers
@@ -329,6 +329,7 @@ struct SumArgs {
   float* dq;
   int q_batched;
   float s;
+  int* flags;           // [B H] row-pass flags, cleared here (one thread per head)
 };
 
 __device__ inline int split_count(const SumArgs& a, int bh) {
@@ -371,6 +372,7 @@ __global__ void __launch_bounds__(kThreads) sum_dz_kernel(SumArgs a) {
   float prod = (float)(bf16)v * a.Z[ic];
   for (int o = 1; o < a.D; o <<= 1) prod += __shfl_xor(prod, o);
   if (on) {
+    if (md == 0 && a.flags) a.flags[bh] = 0;
     a.dz[i] = v;
     if (a.dz_out) a.dz_out[i] = v;
     if (md % a.D == 0) {
@@ -414,9 +416,12 @@ struct RowArgs {
   const float* dZ;      // encoder side
   const float* L;       // encoder side
   const float* c;       // encoder side
+  const float* Zf;      // encoder side: the encoder's latents Z (the factored pass forms c from them)
+  const float* dL;      // encoder side: the cotangent of L, or null (the factored pass adds it to c)
   bf16* dK;
   bf16* dV;             // encoder side
   int v_alias;          // encoder side: V is K, so dK receives dK + dV and dV is not written
+  int* flags;           // [B H]: heads the factored pass left to the exact-weight pass
   long long total;
   int q_batched, H, N, M, MB, nwg;
   float qscale;
@@ -431,6 +436,9 @@ template <int D> struct RowLds {
   }
 };
 
+// Row pass with exact per-row shifts: the encoder weights P = 2^(S2 - L2_m)
+// from their own exponentials.  It completes only the heads that the
+// factored pass (below) flagged, and skips the others.
 // NW waves per workgroup share the staged head: at the largest sizes the
 // LDS holds one workgroup per compute unit, so 8 waves keep two per SIMD.
 template <typename QT, int D, int NW, bool TAIL, bool DEC, bool ENC>
@@ -458,6 +466,10 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
     const int n_lo = (int)(x - hb);
     const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
     const int h = bh % a.H;
+    if (a.flags[bh] == 0) {  // the factored pass completed this head (uniform over the workgroup)
+      x = hb + n_hi;
+      continue;
+    }
 
     __syncthreads();  // the previous piece is done with the staged head
     {
@@ -570,10 +582,193 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_kernel(RowArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Row pass, factored.  With mu the largest L2_m of the head, the encoder
+// weights factor exactly into a per-token, a per-pair and a per-latent part:
+//   P[m,n] = 2^(S2 - L2_m) = a_n * W[m,n] * b_m,
+//   a_n = 2^(lse2_n - mu),  W = 2^(S2 - lse2_n),  b_m = 2^(mu - L2_m),
+// so P needs no exponential or score product of its own.  b_m moves onto
+// the staged latent-side rows (dZ' = b_m dZ, c' = b_m c, so
+// P o (dZ V^T - c) = a_n W o (dZ' V^T - c')), and a_n is one scalar per
+// lane:
+//   dS = W o (E_dec + a_n E'),  dV = a_n sum_m W dZ'_m.
+// Without the decoder side (the encoder's backward alone) the pass uses
+// W = 2^(S2 - mu) and a_n = 1.  The factors stay in range when the head's
+// L2 spread is at most kRangeMax and a_n lies in [2^-120, 2^120]; a head
+// outside is flagged (flags[bh] = 1) and left to the exact-weight pass.
+// ----------------------------------------------------------------------------
+constexpr float kRangeMax = 64.f;
+
+template <typename QT, int D, int NW, bool TAIL, bool DEC>
+__global__ void __launch_bounds__(NW * 64) bwd_row_fast_kernel(RowArgs a) {
+  constexpr int NT = NW * 64;
+  using RL = RowLds<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float wred[2][NW];
+  const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
+  const int tst = RL::tst(MB);
+  bf16* qs = reinterpret_cast<bf16*>(smem);
+  bf16* zr = qs + (size_t)Mp * RL::RST;
+  bf16* dzr = zr + (size_t)Mp * RL::RST;
+  bf16* qt = dzr + (size_t)Mp * RL::RST;
+  bf16* dzt = qt + (size_t)D * tst;
+  uint4* crec = reinterpret_cast<uint4*>(dzt + (size_t)D * tst);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 31, g = lane >> 5;
+  __builtin_assume(MB >= 1);
+
+  long long x = piece_start(blockIdx.x, a.total, a.nwg);
+  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  while (x < xe) {
+    const int bh = (int)(x / N);
+    const long long hb = (long long)bh * N;
+    const int n_lo = (int)(x - hb);
+    const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
+    const int h = bh % a.H;
+    const float* Lh = a.L + (size_t)bh * M;
+
+    __syncthreads();  // the previous piece is done with the staged head
+    // mu and the spread of L2 over the head's latents (every thread ends
+    // with the same values: the same reductions in the same order)
+    float mx = -INFINITY, mn = INFINITY;
+    for (int m = threadIdx.x; m < M; m += NT) {
+      const float l2 = Lh[m] * kLog2e;
+      mx = fmaxf(mx, l2);
+      mn = fminf(mn, l2);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+      mn = fminf(mn, __shfl_xor(mn, o));
+    }
+    if (lane == 0) { wred[0][wave] = mx; wred[1][wave] = mn; }
+    __syncthreads();
+    mx = wred[0][0];
+    mn = wred[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, wred[0][w]); mn = fminf(mn, wred[1][w]); }
+    const float mu = mx;
+    if (!(mx - mn <= kRangeMax)) {  // also when L holds a non-finite value
+      if (threadIdx.x == 0) a.flags[bh] = 1;
+      x = hb + n_hi;
+      continue;
+    }
+    {
+      const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
+      // Mp D is a multiple of NT, so every thread runs every iteration and
+      // the D threads of one latent (consecutive lanes) can shuffle
+      for (int e = threadIdx.x; e < Mp * D; e += NT) {
+        const int m = e / D, d = e % D;
+        const bool in = m < M;
+        const size_t i = ((size_t)bh * M + (in ? m : 0)) * D + d;
+        const bf16 q = (bf16)(in ? to_f(Qh[(size_t)(in ? m : 0) * D + d]) * a.qscale : 0.f);
+        qs[m * RL::RST + d] = q;
+        qt[d * tst + m] = q;
+        if constexpr (DEC) zr[m * RL::RST + d] = (bf16)(in ? a.Zc[i] : 0.f);
+        const float b = in ? fast_exp2(mu - Lh[in ? m : 0] * kLog2e) : 0.f;
+        const bf16 z = (bf16)(b * a.dZ[i]);
+        dzr[m * RL::RST + d] = z;
+        dzt[d * tst + m] = z;
+        float cp = in ? (float)z * a.Zf[i] : 0.f;
+        for (int o = 1; o < D; o <<= 1) cp += __shfl_xor(cp, o);
+        if (d == 0) {
+          if (a.dL && in) cp -= b * a.dL[(size_t)bh * M + m];  // c' = b (bf16(dZ) . Z - dL)
+          crec[m] = split3_record(-cp, 0.f);
+        }
+      }
+    }
+    __syncthreads();
+
+    const bf16* Kh = a.K + (size_t)bh * N * D;
+    const bf16x8 sel = record_select(g, false);
+    for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += 32 * NW) {
+      // lanes past the piece recompute its last token and store the same values there
+      const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
+      QKOp<bf16, D> kop, yop, vop;
+      load_op<D>(kop, Kh + (size_t)n * D, g);
+      load_op<D>(vop, a.V + ((size_t)bh * N + n) * D, g);
+      f32x16 cw, cd = {};
+      float an = 1.f;
+      if constexpr (DEC) {
+        load_op<D>(yop, a.dY + ((size_t)bh * N + n) * D, g);
+        const uint4 rec = a.srec[(size_t)bh * N + n];
+        const float nl = record_value(rec, false);  // -lse2
+        cw = splat16(nl);
+        cd = splat16(record_value(rec, true));
+        an = fast_exp2(-nl - mu);
+        if (__builtin_amdgcn_ballot_w64(!(an >= 0x1p-120f && an <= 0x1p120f)) != 0) {
+          if (lane == 0) a.flags[bh] = 1;  // the exact-weight pass redoes this head
+          continue;
+        }
+      } else {
+        cw = splat16(-mu);
+      }
+      f32x16 acck = {}, accv = {};
+      for (int mb = 0; mb < MB; ++mb) {
+        QKOp<bf16, D> qop, zop;
+        load_op<D>(qop, qs + (mb * 32 + li) * RL::RST, g);
+        load_op<D>(zop, dzr + (mb * 32 + li) * RL::RST, g);
+        f32x16 s = qk_mma<D>(qop, kop, cw);
+        // E' = dZ' V^T - c' (the latent rows' -c' through the record step)
+        f32x16 e = qk_mma<D>(zop, vop, record_add(crec[mb * 32 + li], sel, f32x16{}));
+        if constexpr (DEC) {
+          QKOp<bf16, D> wop;
+          load_op<D>(wop, zr + (mb * 32 + li) * RL::RST, g);
+          const f32x16 ed = qk_mma<D>(wop, yop, cd);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e[r] = ed[r] + an * e[r];
+        }
+        if (TAIL && mb == MB - 1) mask_rows(s, M - mb * 32, g);
+        f32x16 w, ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          w[r] = fast_exp2(s[r]);
+          ds[r] = w[r] * e[r];
+        }
+        PVOp<bf16> zt, qtop;
+        if (li < D) {
+          load_pv(zt, dzt + li * tst + mb * 32, g);
+          load_pv(qtop, qt + li * tst + mb * 32, g);
+        } else {
+          ones_pv(zt, li, D);
+          ones_pv(qtop, li, D);
+        }
+        bf16x8 w0, w1, d0, d1;
+        pack16(w, w0, w1);
+        pack16(ds, d0, d1);
+        accv = pv_mma(zt, w0, w1, accv);
+        acck = pv_mma(qtop, d0, d1, acck);
+      }
+      constexpr float kInvLog2e = 0.69314718055994531f;
+      bf16* dk = a.dK + ((size_t)bh * N + n) * D;
+      bf16* dv = a.v_alias ? nullptr : a.dV + ((size_t)bh * N + n) * D;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        if (8 * c4 + 4 * g < D) {
+          bf16x4 u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = acck[4 * c4 + i] * kInvLog2e;
+            if (a.v_alias) v += an * accv[4 * c4 + i];
+            u[i] = (bf16)v;
+          }
+          *reinterpret_cast<bf16x4*>(dk + 8 * c4 + 4 * g) = u;
+          if (!a.v_alias) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)(an * accv[4 * c4 + i]);
+            *reinterpret_cast<bf16x4*>(dv + 8 * c4 + 4 * g) = v;
+          }
+        }
+      }
+    }
+    x = hb + n_hi;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
 struct BwdLayout {
-  size_t zc = 0, srec = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, total = 0;
+  size_t zc = 0, srec = 0, part_dz = 0, part_dq = 0, dz = 0, c = 0, flags = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D) {
@@ -586,6 +781,7 @@ BwdLayout bwd_layout(const Dev& dev, bool dec, int B, int H, int N, int M, int D
   w.part_dq = off; off += part;
   w.dz = off; off += lat;
   w.c = off; off += align256((size_t)BH * M * sizeof(float));
+  w.flags = off; off += align256((size_t)BH * sizeof(int));
   if (dec) {
     w.zc = off; off += lat;
     w.srec = off; off += align256((size_t)BH * N * sizeof(uint4));
@@ -626,15 +822,25 @@ int launch_col(const ColArgs& a, int D, bool dec, bool qf32, const EncPlan& p, h
   return qf32 ? launch_col_q<float>(a, D, dec, p, st) : launch_col_q<bf16>(a, D, dec, p, st);
 }
 
-constexpr int kRowWaves = 8;
+#ifndef FLARE_ROW_WAVES
+#define FLARE_ROW_WAVES 8
+#endif
+constexpr int kRowWaves = FLARE_ROW_WAVES;
 
+// The factored pass, then the exact-weight pass for the heads it flagged.
 template <typename QT, int D, bool TAIL, bool DEC, bool ENC>
 int launch_row_k(const RowArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>;
+  static_assert(ENC, "the row pass always has the encoder side");
+  const void* ff = (const void*)bwd_row_fast_kernel<QT, D, kRowWaves, TAIL, DEC>;
+  const void* fs = (const void*)bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>;
   if (lds > 65536) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute(ff, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+        hipFuncSetAttribute(fs, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
+  hipLaunchKernelGGL((bwd_row_fast_kernel<QT, D, kRowWaves, TAIL, DEC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st,
+                     a);
+  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
   hipLaunchKernelGGL((bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st,
                      a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
@@ -713,6 +919,7 @@ int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q
   sa.B = B; sa.H = H; sa.N = N; sa.M = M; sa.D = D;
   sa.Z = Z; sa.dL = dL; sa.dz = dz; sa.c = c; sa.dz_out = dZ_out;
   sa.dq = dQ; sa.q_batched = q_batched; sa.s = scale;
+  sa.flags = (int*)(ws + w.flags);
   const unsigned lat_grid = (unsigned)cdiv((long long)BH * M * D, kThreads);
   ColArgs ca{};
   ca.Q = Q; ca.K = K; ca.total = p.total;
@@ -758,6 +965,7 @@ int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q
   ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.srec = srec; ra.dZ = dz; ra.L = L;
   ra.c = c;
   ra.dK = dK; ra.dV = dV; ra.v_alias = v_alias ? 1 : 0;
+  ra.Zf = Z; ra.dL = dL; ra.flags = (int*)(ws + w.flags);
   ra.total = (long long)BH * N;
   ra.q_batched = q_batched; ra.H = H; ra.N = N; ra.M = M; ra.MB = (int)cdiv(M, 32);
   ra.qscale = qs;

@@ -249,3 +249,52 @@ def test_pp_million_token_backward_one_head(flare, orc):
                                 dY[:, sl], shared_vs=True)
     heads = (got[0][sl], got[1][:, sl], None, got[3][sl], got[4][sl], got[5][:, sl], got[6][:, sl])
     compare_pp(heads, ref, prefix=f"head {h} ")
+
+
+def _spread_inputs(seed, N=700, M=40, D=32):
+    """Two heads.  Head 0: four latent queries are 3 x a token's sign key, the
+    others zero; with scale 1/log2(e) its log2 scores are exact integers up to
+    96, so the latents' log-normalisers spread by more than 64 (log2) and
+    the row pass leaves that head to its exact-weight kernel.  Head 1:
+    ordinary Gaussian inputs (the factored kernel).  Every input is exact in
+    bf16."""
+    rng = np.random.default_rng(seed)
+    K = np.empty((1, 2, N, D), np.float32)
+    K[0, 0] = rng.integers(0, 2, size=(N, D)) * 2 - 1
+    K[0, 1] = np.round(rng.standard_normal((N, D)) * 8) / 8
+    V = (np.round(rng.standard_normal((1, 2, N, D)) * 8) / 8).astype(np.float32)
+    Q = np.zeros((2, M, D), np.float32)
+    pick = rng.choice(N, size=4, replace=False)
+    Q[0, :4] = 3 * K[0, 0, pick]
+    Q[1] = np.round(rng.standard_normal((M, D)) * 2) / 16
+    return Q, K, V
+
+
+def test_backward_wide_log_normaliser_spread(flare, orc):
+    import math
+    from rank_latent_attention_amd.inputs import cotangent
+    Q, K, V = _spread_inputs(121)
+    dY = cotangent(122, "dy", K.shape)
+    scale = 1.0 / math.log2(math.e)
+    _, _, L = orc.flare_forward(Q, K, V, scale)
+    spread = (L.max(axis=-1) - L.min(axis=-1)) / math.log(2)
+    say(f"[backward spread] log2 spread of L per head {spread.ravel()}")
+    assert spread[0, 0] > 64 and spread[0, 1] < 64
+    compare(orc, flare, Q, K, V, dY, scale=scale)
+
+
+def test_encode_backward_wide_log_normaliser_spread(flare, orc):
+    import math
+    import torch
+    from rank_latent_attention_amd.inputs import cotangent
+    Q, K, V = _spread_inputs(123)
+    scale = 1.0 / math.log2(math.e)
+    dZ = cotangent(124, "dz", (1, 2, Q.shape[1], Q.shape[2]), "f32")
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    Z, L = flare.flare_encode(Qd, Kd, Vd, scale=scale)
+    dQ, dK, dV = flare.flare_encode_backward(Qd, Kd, Vd, Z, L, dev(dZ, "f32"), None, scale=scale)
+    torch.cuda.synchronize()
+    ref = orc.encode_backward(Q, K, V, dZ, None, scale)
+    say("[encode backward spread]")
+    for n, g, r in zip(("dQ", "dK", "dV"), (host(dQ), host(dK), host(dV)), ref):
+        check(n, g, r)
