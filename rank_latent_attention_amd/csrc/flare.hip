@@ -1289,7 +1289,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           }
         }
         const float dot = pair_sum(part) * inv;
-        if (g == 0) a.srec[(size_t)bh * N + n] = split3_record(-(shift + __builtin_amdgcn_logf(den)), -dot);
+        // both lanes of the pair store the same record: a store in a divergent
+        // branch would make the wait for the prefetched keys cover it
+        a.srec[(size_t)bh * N + n] = split3_record(-(shift + __builtin_amdgcn_logf(den)), -dot);
       } else {
         T* dst = Yh + (size_t)n * D;
 #pragma unroll
