@@ -298,3 +298,22 @@ def test_encode_backward_wide_log_normaliser_spread(flare, orc):
     say("[encode backward spread]")
     for n, g, r in zip(("dQ", "dK", "dV"), (host(dQ), host(dK), host(dV)), ref):
         check(n, g, r)
+
+
+def test_backward_scores_beyond_the_unshifted_range(flare, orc):
+    # log2 scores up to 160 (exact integers: sign keys, queries 5 x a key,
+    # scale 1/log2(e)): the forward's encode and decode and the backward's
+    # statistics pass overflow their unshifted weights and recompute with the
+    # exact maxima, and the row pass leaves the head to its exact-weight kernel
+    import math
+    from rank_latent_attention_amd.inputs import cotangent
+    rng = np.random.default_rng(141)
+    N, M, D = 900, 36, 32
+    K = (rng.integers(0, 2, size=(1, 1, N, D)) * 2 - 1).astype(np.float32)
+    V = (np.round(rng.standard_normal((1, 1, N, D)) * 8) / 8).astype(np.float32)
+    Q = np.zeros((1, M, D), np.float32)
+    pick = rng.choice(N, size=M, replace=False)
+    Q[0] = K[0, 0, pick] * rng.integers(1, 6, size=(M, 1))
+    dY = cotangent(142, "dy", K.shape)
+    say("[backward] log2 scores up to 160")
+    compare(orc, flare, Q, K, V, dY, scale=1.0 / math.log2(math.e))
