@@ -47,6 +47,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Softmax sums of the unshifted bf16 loops on the matrix core (see sum_mma and
+// pad_pv) rather than with float adds.
+#ifndef FLARE_MFMA_SUM
+#define FLARE_MFMA_SUM 1
+#endif
+
 constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kTile = 128;         // tokens per float32 encode LDS tile (4 blocks of 32)
 #ifndef FLARE_DMA_TILE
@@ -267,7 +273,7 @@ template <typename T, int D> __device__ inline float col_sum(float lsum, const f
 // PV A operand of a lane whose feature row is beyond D: zero, except row 16
 // (lanes 16 and 48), which is all ones when D = 16.
 __device__ inline void ones_pv(PVOp<bf16>& o, int li, int D) {
-  (void)li; (void)D;  // bf16 tiles sum their weights with dot products instead
+  (void)li; (void)D;  // bf16 tiles get zero rows here (the forward's fast loops use pad_pv)
   const bf16 v = (bf16)0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) { o.a0[s] = v; o.a1[s] = v; }
@@ -276,6 +282,14 @@ __device__ inline void ones_pv(PVOp<float>& o, int li, int D) {
   const float v = D == 16 && li == 16 ? 1.f : 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) o.a[j] = v;
+}
+// The same for the unshifted bf16 loops of the forward: with D = 16 and
+// matrix-core sums, row 16 is all ones, so accumulator row 16 (register 8 of
+// the lower half) collects the column sums of the bf16 weights.
+__device__ inline void pad_pv(PVOp<bf16>& o, int li, int D) {
+  const bf16 v = (bf16)(FLARE_MFMA_SUM && D == 16 && li == 16 ? 1.f : 0.f);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) { o.a0[s] = v; o.a1[s] = v; }
 }
 
 // Maximum of the tile column held by this lane pair.
@@ -328,6 +342,44 @@ __device__ inline float pack_weights(const f32x16& s, bf16x8& b0, bf16x8& b1) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r]);
   return pack_exps(p, b0, b1);
+}
+
+// Unshifted weights exp2(s) packed to bf16, without their sum.
+__device__ inline void pack_only(const f32x16& s, bf16x8& b0, bf16x8& b1) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    b0[r] = (bf16)fast_exp2(s[r]);
+    b1[r] = (bf16)fast_exp2(s[8 + r]);
+  }
+}
+
+// Column sums of packed weight tiles on the matrix core.  A 16x16x32 product
+// whose B operand is the packed tile (b0 or b1) of every lane sees lane l as
+// column l % 16 and contraction group l / 16; lane l of the tile holds column
+// l % 32 of the 32x32 weight tile.  The A operand below is all ones on lanes
+// 0 and 32 (row 0, groups 0 and 2) and on lanes 17 and 49 (row 1, groups 1
+// and 3), zero elsewhere, so row 0 of the 16x16 result sums tile columns
+// 0..15 and row 1 tile columns 16..31, over both halves of the column.  The
+// pairing holds for any order of the contraction inside a group, because A
+// and B share it.  The sums are those of the bf16 weights the value product
+// uses, so the normalised weights sum to one exactly as multiplied.
+__device__ inline bf16x8 sum_selector(int lane) {
+  const bf16 v = (bf16)((lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 1.f : 0.f);
+  bf16x8 o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o[s] = v;
+  return o;
+}
+__device__ inline f32x4 sum_mma(const bf16x8& sel, const bf16x8& b0, const bf16x8& b1, f32x4 s) {
+  s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, b0, s, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, b1, s, 0, 0, 0);
+  return s;
+}
+// Sum of tile column li (on both lanes of the pair): row 0 / row 1 of the
+// 16x16 result, column li % 16, held by lane li % 16 in registers 0 / 1.
+__device__ inline float sum_col(const f32x4& s, int li) {
+  const float a = __shfl(s[0], li & 15), b = __shfl(s[1], li & 15);
+  return li < 16 ? a : b;
 }
 
 // Set rows at or beyond `from` (tile row index, acc_row order) to -inf.
@@ -480,6 +532,11 @@ template <int OFF> __device__ inline bf16x4 tr_read(unsigned addr) {
 __device__ inline void pv_wait(PVOp<bf16>& o, int lane, int D) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o.a0), "+v"(o.a1));
   if (16 * ((lane >> 4) & 1) >= D) ones_pv(o, lane & 31, D);  // feature rows beyond D
+}
+// The forward encode's: feature rows beyond D padded by pad_pv.
+__device__ inline void pv_wait_pad(PVOp<bf16>& o, int lane, int D) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o.a0), "+v"(o.a1));
+  if (16 * ((lane >> 4) & 1) >= D) pad_pv(o, lane & 31, D);
 }
 
 // ----------------------------------------------------------------------------
@@ -657,6 +714,37 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncArgs a) {
   }
 }
 
+// Running weight sum of the unshifted bf16 loops: the 16x16 matrix-core sums
+// and their selector operand, or a lane's partial sum of float32 weights.
+template <bool MMA, int D> struct WSum;
+template <> struct WSum<true, 32> {  // 16x16x32 sums of the packed weights
+  f32x4 s;
+  bf16x8 sel;
+  __device__ explicit WSum(int lane) : s{0.f, 0.f, 0.f, 0.f}, sel(sum_selector(lane)) {}
+  __device__ void add(const f32x16& sc, bf16x8& b0, bf16x8& b1) {
+    pack_only(sc, b0, b1);
+    s = sum_mma(sel, b0, b1, s);
+  }
+  __device__ float total(int li, const f32x16&) const { return sum_col(s, li); }
+};
+template <> struct WSum<true, 16> {  // accumulator row 16 (pad_pv)
+  __device__ explicit WSum(int) {}
+  __device__ void add(const f32x16& sc, bf16x8& b0, bf16x8& b1) { pack_only(sc, b0, b1); }
+  __device__ float total(int, const f32x16& acc) const { return col_sum<float, 16>(0.f, acc); }
+};
+template <int D> struct WSum<false, D> {
+  float s;
+  __device__ explicit WSum(int) : s(0.f) {}
+  __device__ void add(const f32x16& sc, bf16x8& b0, bf16x8& b1) {
+    s += pack_weights(sc, b0, b1);
+    // keep the block's sum here: sunk to the end of a tile, the adds would
+    // hold every block's weights in registers until then
+    asm volatile("" : "+v"(s));
+  }
+  __device__ float total(int, const f32x16&) const { return pair_sum(s); }
+};
+template <int D> using RowSum = WSum<FLARE_MFMA_SUM != 0, D>;
+
 // Scores S^T = K Q^T of token block NB of the tile in buffer BO (LDS byte
 // addresses ka + BO + NB * 64 * D) against one wave's 32 latents, unshifted.
 template <int D, int NB, int BO>
@@ -673,7 +761,7 @@ __device__ inline f32x16 enc_scores(const unsigned (&ka)[D / 16], const QKOp<bf1
 // (all of them for a block past the end) get no weight.
 template <int D, int NB, int BO>
 __device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0, int n_hi, int g, int lane,
-                                   float& lsum, f32x16& acc) {
+                                   RowSum<D>& lsum, f32x16& acc) {
   constexpr int OFF = BO + NB * 64 * D;
   PVOp<bf16> vop;
   {
@@ -684,11 +772,8 @@ __device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0,
   }
   if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
   bf16x8 b0, b1;
-  lsum += pack_weights(sc, b0, b1);
-  // keep the block's sum here: sunk to the end of the tile, the adds would
-  // hold every block's weights in registers until then
-  asm volatile("" : "+v"(lsum));
-  pv_wait(vop, lane, D);
+  lsum.add(sc, b0, b1);
+  pv_wait_pad(vop, lane, D);
   acc = pv_mma(vop, b0, b1, acc);
 }
 
@@ -700,7 +785,7 @@ __device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0,
 // the piece's last row): a branch per block costs more than the rare waste.
 template <int D, int WN, int BO, int J, int NBLK>
 __device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
-                                    int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc, const f32x16& cur) {
+                                    int lane, const QKOp<bf16, D>& qop, RowSum<D>& lsum, f32x16& acc, const f32x16& cur) {
   if constexpr (J + 1 < NBLK) {
     const f32x16 nxt = enc_scores<D, (J + 1) * WN, BO>(ka, qop);
     enc_consume<D, J * WN, BO>(va, cur, t0 + 32 * J * WN, n_hi, g, lane, lsum, acc);
@@ -715,7 +800,7 @@ __device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned
 // here is the wave's first row).
 template <int D, int NW, int WN, int BO>
 __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
-                                   int lane, const QKOp<bf16, D>& qop, float& lsum, f32x16& acc) {
+                                   int lane, const QKOp<bf16, D>& qop, RowSum<D>& lsum, f32x16& acc) {
   if (t0 >= n_hi) return;
   constexpr int NBLK = dma_rows<NW>() / 32 / WN;
   encode_chain<D, WN, BO, 0, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, enc_scores<D, 0, BO>(ka, qop));
@@ -826,7 +911,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    float lsum = 0.f;
+    RowSum<D> wsum(lane);
 
     const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
     const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + (size_t)bh * N * D;
@@ -846,7 +931,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, lsum, acc);
+      encode_tile<D, NW, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
@@ -860,7 +945,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, lsum, acc);
+      encode_tile<D, NW, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       wait_dma();
       __syncthreads();
       if constexpr (NK) {
@@ -871,8 +956,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       }
     }
     // unshifted partial (see fast_ok), or the careful recomputation's
-    float ltot = pair_sum(lsum), shift = 0.f;
+    float ltot = wsum.total(li, acc), shift = 0.f;
     if (fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
+      float lsum;
       shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane, qop, lsum,
                                     acc);
       ltot = pair_sum(lsum);
@@ -1197,18 +1283,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         // scores of latent block mb + 1 go to the MFMA unit before the
         // weights of block mb are exponentiated, so within the wave the
         // matrix products run under the exponentials.
+        RowSum<D> wsum(lane);
+        // This lane's LDS rows, recomputed for every token block from an
+        // index opaque to the compiler: held across the block loop they are
+        // spilled, and the reload's wait would also wait for the key prefetch.
+        int lid = threadIdx.x;
+        asm volatile("" : "+v"(lid));
+        const T* qrow = qs + (lid & 31) * L::QST;
+        const T* zrow = zt + (lid & 31) * zst;
         auto scores = [&](int mb) {
           QKOp<T, D> qop;
-          load_op<D>(qop, qs + (mb * 32 + li) * L::QST, g);
+          load_op<D>(qop, qrow + mb * 32 * L::QST, g);
           return qk_mma<D>(qop, kop, zero16);
         };
         auto consume = [&](f32x16 sc, int mb, const f32x16& from) {
           PVOp<T> zop;
-          if (li < D) load_pv(zop, zt + li * zst + mb * 32, g);
-          else ones_pv(zop, li, D);
+          if (li < D) load_pv(zop, zrow + mb * 32, g);
+          else pad_pv(zop, li, D);
           if (mask_tail && mb == MB - 1) mask_rows(sc, M - mb * 32, g);
           bf16x8 b0, b1;
-          lsum += pack_weights(sc, b0, b1);
+          wsum.add(sc, b0, b1);
           acc = pv_mma(zop, b0, b1, from);
         };
         f32x16 sa = scores(0), sb;
@@ -1228,7 +1322,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         } else if (mb < MB) {
           consume(sb, mb, acc);
         }
-        den = pair_sum(lsum);
+        den = wsum.total(li, acc);
         // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim
         if (__builtin_amdgcn_ballot_w64(!fast_ok(den) || den > zlim) != 0) {
           // careful redo of this token block: exact maximum of every latent block

@@ -16,6 +16,25 @@ def rel_l2(got, ref) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+def lse_err(got, ref) -> float:
+    """Error of a log-normaliser L = log l, measured on the normaliser l = e^L it encodes.
+
+    The bars of TOL are relative errors of values; for L that is the relative error of l,
+    e^(L - L_ref) - 1 at each entry, aggregated as a root mean square like the rel-L2 of the
+    other outputs.  A rel-L2 of L itself would not measure precision: L is near zero
+    whenever l is near one, and large L hides large errors.  Entries whose reference is
+    -inf (a latent that saw no token) must be -inf too.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), "empty rows must have L = -inf, and only they"
+    g, r = got[~empty], ref[~empty]
+    assert np.all(np.isfinite(g)), "non-finite values in the GPU result"
+    return float(np.sqrt(np.mean(np.expm1(g - r) ** 2))) if g.size else 0.0
+
+
 def dev(x, dtype: str, device="cuda:0"):
     """float32 numpy array (values exact in `dtype`) -> contiguous torch tensor on the GPU."""
     import torch
