@@ -877,9 +877,9 @@ int launch_stats_q(const DecArgs& a, size_t lds, int D, hipStream_t st) {
   const bool tail = a.M & 31;
   if (D == 16)
     return tail ? launch_decode_k<bf16, QT, 16, true, false, true>(a, lds, st)
-                : launch_decode_k<bf16, QT, 16, false, false, true>(a, lds, st);
+                : launch_decode_mb<bf16, QT, 16, false, true>(a, lds, st);
   return tail ? launch_decode_k<bf16, QT, 32, true, false, true>(a, lds, st)
-              : launch_decode_k<bf16, QT, 32, false, false, true>(a, lds, st);
+              : launch_decode_mb<bf16, QT, 32, false, true>(a, lds, st);
 }
 
 int launch_stats(const Dev& dev, const void* Q, bool qf32, int q_batched, const bf16* K, const float* Zc,

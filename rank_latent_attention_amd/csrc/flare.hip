@@ -1161,12 +1161,14 @@ template <typename T, int D> struct DecLds {
 // statistics mode for the backward (bf16): the log-normaliser of every
 // token's softmax over the latents (log2 units, the queries' scaling) and
 // the dot product of the token's output cotangent with its output.
-template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false>
+// MBT > 0 fixes the number of latent blocks at compile time (a.MB == MBT), so
+// the latent loop unrolls completely; 0 reads it from the arguments.
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
+  const int MB = MBT > 0 ? MBT : a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
   T* zt = qs + (size_t)Mp * L::QST;
   __shared__ float zred[kThreads / 64];
@@ -1309,6 +1311,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         if (MB > 1) sb = scores(1);
         consume(sa, 0, zero16);
         int mb = 1;
+#pragma unroll
         for (; mb + 2 < MB; mb += 2) {  // block mb is in sb
           sa = scores(mb + 1);
           consume(sb, mb, acc);
@@ -1595,15 +1598,30 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
 }
 
-template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false>
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
 int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK, ST>;
+  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK, ST, MBT>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK, ST>), dim3(a.nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK, ST, MBT>), dim3(a.nwg), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+// bf16 decode without a latent tail: 2, 4 or 8 latent blocks (M = 64, 128,
+// 256) get a fully unrolled latent loop.
+template <typename T, typename QT, int D, bool NK, bool ST = false>
+int launch_decode_mb(const DecArgs& a, size_t lds, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    switch (a.MB) {
+      case 2: return launch_decode_k<T, QT, D, false, NK, ST, 2>(a, lds, st);
+      case 4: return launch_decode_k<T, QT, D, false, NK, ST, 4>(a, lds, st);
+      case 8: return launch_decode_k<T, QT, D, false, NK, ST, 8>(a, lds, st);
+      default: break;
+    }
+  }
+  return launch_decode_k<T, QT, D, false, NK, ST>(a, lds, st);
 }
 
 template <typename T, typename QT, int D>
@@ -1611,12 +1629,12 @@ int launch_decode_t(const DecArgs& a, size_t lds, bool nk, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     if (nk)
       return (a.M & 31) ? launch_decode_k<T, QT, D, true, true>(a, lds, st)
-                        : launch_decode_k<T, QT, D, false, true>(a, lds, st);
+                        : launch_decode_mb<T, QT, D, true>(a, lds, st);
   } else {
     if (nk) return FLARE_ERR_UNSUPPORTED;
   }
   return (a.M & 31) ? launch_decode_k<T, QT, D, true, false>(a, lds, st)
-                    : launch_decode_k<T, QT, D, false, false>(a, lds, st);
+                    : launch_decode_mb<T, QT, D, false>(a, lds, st);
 }
 
 size_t decode_lds(int dtype, int D, int M) {
