@@ -1311,7 +1311,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         if (MB > 1) sb = scores(1);
         consume(sa, 0, zero16);
         int mb = 1;
-#pragma unroll
+        constexpr int kUnroll = MBT > 0 ? MBT : 1;
+#pragma unroll kUnroll
         for (; mb + 2 < MB; mb += 2) {  // block mb is in sb
           sa = scores(mb + 1);
           consume(sb, mb, acc);
