@@ -43,12 +43,17 @@ def log(*a):
 
 
 def kernel_source_sha256() -> str:
-    """sha256 over the kernel sources (csrc/*.hip and *.h, by name)."""
+    """sha256 over the code of the kernel sources (csrc/*.hip and *.h, by name), with
+    // comments, trailing blanks and empty lines left out: a comment edit does not
+    invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(KERNEL_SRC_DIR)):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
-            h.update(open(os.path.join(KERNEL_SRC_DIR, f), "rb").read())
+            for line in open(os.path.join(KERNEL_SRC_DIR, f), encoding="utf-8"):
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -9,28 +9,31 @@
 // with one more encode call and blends them onto fixed queries with a
 // per-head gate (Sec. 3.2, App. A.4).
 //
-// Kernels (all 256 threads = 4 waves of 64):
-//   encode_kernel  -- split-N encode partials.  The flattened (head, token)
-//                     range of a launch is cut into one contiguous piece per
-//                     workgroup; token tiles of 128 are staged in LDS (K
-//                     row-major, V transposed) and each wave owns up to 64
-//                     latents.  Scores S^T = K Q^T and the latent update
-//                     Z^T += V^T P^T run on 32x32 MFMA tiles; one lane owns
-//                     one latent column, so the softmax statistics over the
-//                     tokens are in-lane plus one permlane32 swap.  A split
-//                     emits the running (shift, sum, accumulator) triple.
+// Kernels (waves of 64; 32x32 MFMA tiles with the softmax axis on the
+// accumulator column, so a lane's statistics are in-lane plus one
+// permlane32 swap):
+//   encode_dma_kernel -- bf16 split-N encode partials.  The flattened (head,
+//                     token) range is cut into one contiguous piece per
+//                     workgroup of 8 waves; 128-token K / V tiles arrive by
+//                     LDS DMA one tile ahead, each wave owns 32 latents, and
+//                     S^T = K Q^T and Z^T += V^T P^T run on MFMA.  A split
+//                     emits (shift, sum, accumulator).
+//   encode_kernel  -- the same for float32 inputs, register-staged tiles.
 //   merge_kernel   -- log-sum-exp merge of the splits in a fixed order
 //                     (Sec. 3.3, App. B.3); optionally the FLARE++ blend.
 //   decode_kernel  -- per-token softmax over the latents: the scaled queries
 //                     and the latents stay in LDS for a head, every wave takes
-//                     64 tokens, S = Q K^T and Y^T += Z^T P run on MFMA with
-//                     one lane per token column.
+//                     32 tokens per step, S = Q K^T and Y^T += Z^T P run on
+//                     MFMA with one lane per token column.
+// backward.h holds the reverse-mode kernels and their entry points.
 // Scores are kept in log2 units: the queries are pre-multiplied by
-// s*log2(e) so every exponential is a single v_exp_f32.  The running shift
-// enters the score MFMA as its accumulator input, and it is only raised when
-// a tile's maximum exceeds it by more than kTheta (otherwise the stale shift
-// keeps every exponential below 2^kTheta), so the common tile costs one
-// exp, one add and one convert per score.
+// s*log2(e) so every exponential is a single v_exp_f32.  The bf16 loops use
+// no shift at all (weights exp2(score), checked for range afterwards, with an
+// exact-maximum recomputation as fallback) and sum the bf16 weights on the
+// matrix core, so a score costs one exponential and half a pack on the VALU.
+// float32 tiles keep an online softmax whose shift enters the score MFMA as
+// its accumulator input and is only raised when a tile's maximum exceeds it
+// by more than kTheta.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
