@@ -229,10 +229,13 @@ def main():
     # MFMA + transcendental load; 30 warmup steps (about 90 launches) reach it
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_backward", "flare_pp_backward"],
+    ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_pp_simplified", "flare_backward",
+                                           "flare_pp_backward"],
                     default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
                          "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels; "
+                         "flare_pp_simplified is simplified FLARE++ (N_a on the seeds and synthesis keys, separate "
+                         "synthesis values, no blend) through the same fused-norm entry point; "
                          "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward; "
                          "flare_pp_backward the FLARE++ backward likewise")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -252,7 +255,7 @@ def main():
 
     import torch
     import rank_latent_attention_amd as flare
-    from rank_latent_attention_amd.inputs import config5, config5_raw
+    from rank_latent_attention_amd.inputs import config5, config5_raw, config5_simplified
 
     if args.configs:
         time_configs(args.configs)
@@ -261,10 +264,13 @@ def main():
         bench_backward(args, pp=args.workload == "flare_pp_backward")
         return
 
-    pp = args.workload in ("flare_pp", "flare_pp_norm")
-    norm = args.workload == "flare_pp_norm"
+    pp = args.workload in ("flare_pp", "flare_pp_norm", "flare_pp_simplified")
+    norm = args.workload in ("flare_pp_norm", "flare_pp_simplified")
     t0 = time.perf_counter()
-    w = config5_raw() if norm else config5(pp=pp)
+    if args.workload == "flare_pp_simplified":
+        w = config5_simplified()
+    else:
+        w = config5_raw() if norm else config5(pp=pp)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
 
@@ -278,15 +284,18 @@ def main():
     L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
     if pp:
         Qs, Ks, Qf = up(w.Qs), up(w.Ks), up(w.Qf)
+        Vs = Ks if w.shared_vs else up(w.Vs)
         gate = torch.from_numpy(w.gate).to(dev)
         Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
         ws = flare.workspace(flare.flare.OP_PP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
 
         if norm:
-            aqs, ak = (torch.from_numpy(w.alpha_qs).to(dev), torch.from_numpy(w.alpha_k).to(dev))
+            def opt(a):
+                return None if a is None else torch.from_numpy(a).to(dev)
+            aqs, aks, ak = opt(w.alpha_qs), opt(w.alpha_ks), opt(w.alpha_k)
 
             def step():
-                flare.flare_pp_forward_norm(Qs, Ks, Ks, Qf, gate, K, V, w.norm_flags, aqs, None, ak, Y=Y, Q_out=Qo,
+                flare.flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, w.norm_flags, aqs, aks, ak, Y=Y, Q_out=Qo,
                                             Z=Z, L=L, ws=ws)
         else:
             def step():
@@ -366,12 +375,15 @@ def main():
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic("whole_step", args.workload),
                     "kernel": "whole step (5 launches)", "kernel_us": round(ms * 1e3, 2),
-                    "algorithmic_bytes": 4 * B * H * N * D * 2}
+                    # read Ks (and Vs when separate), K, V; write Y
+                    "algorithmic_bytes": (4 if w.shared_vs else 5) * B * H * N * D * 2}
     tok_s = B * N / (ms * 1e-3)
     out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": ("FLARE++" if pp else "FLARE") + " routing forward, million-point surface mesh"
+                      + (", simplified (no blend, separate synthesis values)"
+                         if args.workload == "flare_pp_simplified" else "")
                       + (", per-head RMS norms fused" if norm else ""),
                       "B": B, "H": H, "N": N, "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -408,6 +420,7 @@ def bench_backward(args, pp=False):
     L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
     if pp:
         Qs, Ks, Qf = up(w.Qs), up(w.Ks), up(w.Qf)
+        Vs = Ks if w.shared_vs else up(w.Vs)
         gate = torch.from_numpy(w.gate).to(dev)
         Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
         flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)

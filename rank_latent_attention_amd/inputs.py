@@ -318,6 +318,29 @@ def config5_raw(seed=5, N=1 << 20, H=8):
                     recipe="as c5pp before the norms: Ks=RFF Wks/sqrt 128 (=Vs), K, Qs, Qf raw; alpha=1+N(0,0.01)")
 
 
+def config5_simplified(seed=5, N=1 << 20, H=8):
+    """The million-point workload for simplified FLARE++ (Table 2, simplified
+    column): raw Qs and Ks as in config5_raw with N_a on both (flags 3), a
+    separate synthesis value Vs = RFF Wvs / sqrt(128), no blend (Qf = 0,
+    gate = 1), and the routing keys and values of config5 without norms."""
+    B, D, M, C = 1, 32, 256, 128
+    pts = sphere_points(seed, B, N).astype(np.float32)
+    omega = _gauss(seed, "omega", (C // 2, 3), 4.0).astype(np.float32)
+    X = _rff(pts, omega).astype(np.float32)
+    K = _heads(X, _gauss(seed, "wk", (C, H * D)).astype(np.float32), H, D)
+    V = _heads(X, _gauss(seed, "wv", (C, H * D)).astype(np.float32), H, D)
+    Ks = to_dtype(_heads(X, _gauss(seed, "wks", (C, H * D)).astype(np.float32), H, D), "bf16")
+    Vs = to_dtype(_heads(X, _gauss(seed, "wvs", (C, H * D)).astype(np.float32), H, D), "bf16")
+    Qs = _gauss(seed, "qs", (H, M, D), 1.0 / math.sqrt(D))
+    Qf = np.zeros((H, M, D), dtype=np.float32)
+    g = np.ones((H,), dtype=np.float32)
+    return Workload("c5_surface_mesh_pp_simplified_bf16", B, H, N, M, D, "bf16", Q=Qf, K=to_dtype(K, "bf16"),
+                    V=to_dtype(V, "bf16"), pp=True, Qs=to_dtype(Qs, "bf16"), Ks=Ks, Vs=Vs, Qf=Qf, gate=g,
+                    norm_flags=3, alpha_qs=channel_scales(seed, "alpha_qs", H, D),
+                    alpha_ks=channel_scales(seed, "alpha_ks", H, D),
+                    recipe="as c5pp before the norms, separate Vs=RFF Wvs/sqrt 128, N_a on Qs and Ks, Qf=0, g=1")
+
+
 def config5(pp=False, seed=5, N=1 << 20, H=8):
     """Million-point surface mesh, bf16: B1 H8 D32 N=2^20 M256.
 

@@ -197,3 +197,28 @@ def test_million_token_raw_workload_sampled(flare, orc):
         check_lse(f"head {h} L", L[:, sl], Lr, tol)
         Yr = orc.decode(Qb, K, Zr, idx=idx)
         check(f"head {h} Y[{idx.size} tokens]", Y[:, sl][:, :, idx], Yr, tol)
+
+
+def test_million_token_simplified_workload_sampled(flare, orc):
+    # the simplified FLARE++ bench workload (N_a on the seeds and synthesis
+    # keys, separate synthesis values, no blend), launched whole and checked
+    # on the routing queries, Z and L of two heads and on sampled rows of Y
+    from rank_latent_attention_amd.inputs import config5_simplified
+    w = config5_simplified()
+    say(f"[c5 simplified] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D} flags {w.norm_flags}")
+    Y, Q, Z, L = run_norm(flare, w, w.norm_flags)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Z)) and np.all(np.isfinite(L))
+    rng = np.random.default_rng(13)
+    idx = np.unique(np.concatenate([[0, 1, w.N // 2, w.N - 1], rng.choice(w.N, size=2048, replace=False)]))
+    tol = TOL["bf16"]
+    for h in (1, 6):
+        sl = slice(h, h + 1)
+        Qs = orc.rms_norm(w.Qs[sl], w.alpha_qs[sl], EPS)
+        Ks = orc.rms_norm(w.Ks[:, sl], w.alpha_ks[sl], EPS)
+        Qb = orc.pp_queries(Qs, Ks, w.Vs[:, sl], w.Qf[sl], w.gate[sl])
+        check(f"head {h} Q", Q[:, sl], Qb, tol)
+        Zr, Lr = orc.encode(Qb, w.K[:, sl], w.V[:, sl])
+        check(f"head {h} Z", Z[:, sl], Zr, tol)
+        check_lse(f"head {h} L", L[:, sl], Lr, tol)
+        Yr = orc.decode(Qb, w.K[:, sl], Zr, idx=idx)
+        check(f"head {h} Y[{idx.size} tokens]", Y[:, sl][:, :, idx], Yr, tol)
