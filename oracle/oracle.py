@@ -23,7 +23,8 @@ _lib = None
 
 __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
            "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed", "encode_backward",
-           "decode_backward", "flare_backward", "flare_pp_backward"]
+           "decode_backward", "flare_backward", "flare_pp_backward", "rms_norm_backward",
+           "flare_pp_backward_normed"]
 
 
 def build(force: bool = True) -> str:
@@ -297,3 +298,57 @@ def flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, dY, scale: float = 0.0, shared
     if shared:
         return dQs, dKs + dVs, None, dQf, dgate, dK, dV
     return dQs, dKs, dVs, dQf, dgate, dK, dV
+
+
+def rms_norm_backward(x, dy, alpha=None, eps: float = 1e-6):
+    """Reverse mode of rms_norm: given dy, the cotangent of N(x), returns
+    (dx, dalpha) (dalpha is None for N_0).  With r = (mean_d x^2 + eps)^(-1/2)
+    per row and xh = r x, the forward is N(x) = xh * alpha (App. A.3/A.4), so
+        dalpha[h, d] = sum over the rows of head h of dy * xh,
+        g = dy * alpha,   dx = r * (g - xh * mean_d(g * xh)),
+    the last from d r / d x_j = -r^3 x_j / D.  Written out in fp64."""
+    x, dy = _f64(x), _f64(dy)
+    if x.shape != dy.shape:
+        raise ValueError("x and dy must have one shape")
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh = x * r
+    dalpha = None
+    g = dy
+    if alpha is not None:
+        a = _f64(alpha)
+        g = dy * a[:, None, :]
+        t = dy * xh                                     # [..., H, rows, D]
+        dalpha = t.reshape((-1,) + t.shape[-3:]).sum(axis=(0, 2))
+    dx = r * (g - xh * np.mean(g * xh, axis=-1, keepdims=True))
+    return dx, dalpha
+
+
+def flare_pp_backward_normed(Qs, Ks, Vs, Qf, gate, K, V, dY, *, norm_qs=False, norm_ks=False, norm_qf=False,
+                             norm_k=False, alpha_qs=None, alpha_ks=None, alpha_k=None, eps: float = 1e-6,
+                             scale: float = 0.0):
+    """Reverse mode of flare_pp_forward_normed: the FLARE++ backward on the
+    normalised inputs (flare_pp_backward), then each norm's backward
+    (rms_norm_backward) on the cotangent of its output.  With shared synthesis
+    keys and values (Vs is Ks) the values are the normalised keys, so their
+    cotangent joins the keys' before the norm's backward.
+    Returns (dQs, dKs, dVs, dQf, dgate, dK, dV, dalpha_qs, dalpha_ks, dalpha_k);
+    dVs is None when shared, each dalpha is None when its norm has no scale
+    or is off."""
+    shared = Vs is Ks
+    Qs_n = rms_norm(Qs, alpha_qs, eps) if norm_qs else _f64(Qs)
+    Ks_n = rms_norm(Ks, alpha_ks, eps) if norm_ks else _f64(Ks)
+    Vs_n = Ks_n if shared else _f64(Vs)
+    Qf_n = rms_norm(Qf, None, eps) if norm_qf else _f64(Qf)
+    K_n = rms_norm(K, alpha_k, eps) if norm_k else _f64(K)
+    dQs, dKs, dVs, dQf, dgate, dK, dV = flare_pp_backward(Qs_n, Ks_n, Vs_n, Qf_n, gate, K_n, V, dY, scale,
+                                                          shared_vs=shared)
+    da_qs = da_ks = da_k = None
+    if norm_qs:
+        dQs, da_qs = rms_norm_backward(Qs, dQs, alpha_qs, eps)
+    if norm_ks:
+        dKs, da_ks = rms_norm_backward(Ks, dKs, alpha_ks, eps)
+    if norm_qf:
+        dQf, _ = rms_norm_backward(Qf, dQf, None, eps)
+    if norm_k:
+        dK, da_k = rms_norm_backward(K, dK, alpha_k, eps)
+    return dQs, dKs, dVs, dQf, dgate, dK, dV, da_qs, da_ks, da_k
