@@ -203,7 +203,17 @@ def cpu_baseline_backward(w, dY, target_s: float = 15.0):
 
     def run(n):
         t0 = time.perf_counter()
-        if w.pp:
+        if w.pp and w.norm_flags:
+            f = w.norm_flags
+            Ks = tok(w.Ks, n)
+
+            def a(x):
+                return None if x is None else x[:1]
+            oracle.flare_pp_backward_normed(
+                w.Qs[:1], Ks, Ks, w.Qf[:1], w.gate[:1], tok(w.K, n), tok(w.V, n), tok(dY, n),
+                norm_qs=bool(f & 1), norm_ks=bool(f & 2), norm_qf=bool(f & 4), norm_k=bool(f & 8),
+                alpha_qs=a(w.alpha_qs), alpha_ks=a(w.alpha_ks), alpha_k=a(w.alpha_k))
+        elif w.pp:
             Ks = tok(w.Ks, n)
             oracle.flare_pp_backward(w.Qs[:1], Ks, Ks, w.Qf[:1], w.gate[:1], tok(w.K, n), tok(w.V, n), tok(dY, n))
         else:
@@ -217,7 +227,8 @@ def cpu_baseline_backward(w, dY, target_s: float = 15.0):
     value = w.B * n / (t * w.H)   # a token of the whole pass needs all H heads
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle {'FLARE++' if w.pp else 'FLARE'} backward (forward recompute, decoder and "
-                      f"encoder backward{', blend and synthesis backward' if w.pp else ''}) on head 0 of "
+                      f"encoder backward{', blend and synthesis backward' if w.pp else ''}"
+                      f"{', through the per-head RMS norms' if w.norm_flags else ''}) on head 0 of "
                       f"{w.H}, first {n} of {w.N} tokens, M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; "
                       f"tokens/s scaled by 1/{w.H} heads (the work is linear in the token count)"}
 
@@ -230,14 +241,15 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_pp_simplified", "flare_backward",
-                                           "flare_pp_backward"],
+                                           "flare_pp_backward", "flare_pp_norm_backward"],
                     default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
                          "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels; "
                          "flare_pp_simplified is simplified FLARE++ (N_a on the seeds and synthesis keys, separate "
                          "synthesis values, no blend) through the same fused-norm entry point; "
                          "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward; "
-                         "flare_pp_backward the FLARE++ backward likewise")
+                         "flare_pp_backward the FLARE++ backward likewise, flare_pp_norm_backward the backward of flare_pp_norm "
+                         "(through the fused norms)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--configs", default="",
                     help="instead of the bench line, time the forward of these workloads (comma-separated names "
@@ -260,8 +272,8 @@ def main():
     if args.configs:
         time_configs(args.configs)
         return
-    if args.workload in ("flare_backward", "flare_pp_backward"):
-        bench_backward(args, pp=args.workload == "flare_pp_backward")
+    if args.workload in ("flare_backward", "flare_pp_backward", "flare_pp_norm_backward"):
+        bench_backward(args, pp=args.workload != "flare_backward", norm=args.workload == "flare_pp_norm_backward")
         return
 
     pp = args.workload in ("flare_pp", "flare_pp_norm", "flare_pp_simplified")
@@ -394,19 +406,21 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_backward(args, pp=False):
+def bench_backward(args, pp=False, norm=False):
     """One step = one flare_backward call (center, statistics, decode-side
     col pass, dZ sum, encoder-side col pass, dQ sum, row pass) over the
     million-point workload, given Z and L of one untimed forward; with pp,
     one flare_pp_backward call (synthesis recomputation, that routing
     backward with float32 queries, blend backward, synthesis encoder
     backward) given the routing queries, Z and L of one untimed FLARE++
-    forward."""
+    forward; with norm, one flare_pp_backward_norm call (the inputs normalised
+    again, that FLARE++ backward, the norms' backward) after one untimed
+    flare_pp_forward_norm."""
     import torch
     import rank_latent_attention_amd as flare
-    from rank_latent_attention_amd.inputs import config5, cotangent
+    from rank_latent_attention_amd.inputs import config5, config5_raw, cotangent
     t0 = time.perf_counter()
-    w = config5(pp=pp)
+    w = config5_raw() if norm else config5(pp=pp)
     dYh = cotangent(114 if pp else 101, "dy", w.K.shape)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
@@ -423,11 +437,20 @@ def bench_backward(args, pp=False):
         Vs = Ks if w.shared_vs else up(w.Vs)
         gate = torch.from_numpy(w.gate).to(dev)
         Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
-        flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)
-        ws = flare.workspace(flare.flare.OP_PP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
+        if norm:
+            aqs, ak = torch.from_numpy(w.alpha_qs).to(dev), torch.from_numpy(w.alpha_k).to(dev)
+            flare.flare_pp_forward_norm(Qs, Ks, Ks, Qf, gate, K, V, w.norm_flags, aqs, None, ak, Q_out=Qo, Z=Z, L=L)
+            ws = flare.workspace(flare.flare.OP_PP_BACKWARD_NORM, B, H, N, M, D, flare.flare.BF16, dev)
 
-        def step():
-            flare.flare_pp_backward(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dY, ws=ws)
+            def step():
+                flare.flare_pp_backward_norm(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dY, w.norm_flags, aqs, None, ak,
+                                             ws=ws)
+        else:
+            flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)
+            ws = flare.workspace(flare.flare.OP_PP_BACKWARD, B, H, N, M, D, flare.flare.BF16, dev)
+
+            def step():
+                flare.flare_pp_backward(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dY, ws=ws)
     else:
         Q = up(w.Q)
         flare.flare_forward(Q, K, V, Z=Z, L=L)
@@ -468,13 +491,16 @@ def bench_backward(args, pp=False):
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("whole_step", args.workload),
-                "kernel": "whole step (%d launches)" % (13 if pp else 7), "kernel_us": round(ms * 1e3, 2),
+                # launches per call, as in the committed kernel traces
+                "kernel": "whole step (%d launches)" % ((25 if norm else 16) if pp else 8),
+                "kernel_us": round(ms * 1e3, 2),
                 "algorithmic_bytes": kb, "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     what = "FLARE++" if pp else "FLARE"
     out = {"metric": METRIC_BWD, "value": B * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": f"{what} routing backward, million-point surface mesh", "B": B, "H": H, "N": N,
+           "config": {"workload": f"{what} routing backward, million-point surface mesh"
+                                  + (", through the per-head RMS norms" if norm else ""), "B": B, "H": H, "N": N,
                       "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
            "tflops": round(achieved, 2), "roofline": roofline}
     if not args.no_cpu:

@@ -76,6 +76,7 @@ extern "C" {
 #define FLARE_OP_BACKWARD 4
 #define FLARE_OP_ENCODE_BACKWARD 5
 #define FLARE_OP_PP_BACKWARD 6
+#define FLARE_OP_PP_BACKWARD_NORM 7
 
 /* Scratch bytes that `op` needs for this problem (0 when none); returns 0 for
  * arguments the op would reject.  Depends only on its arguments and on the
@@ -208,6 +209,35 @@ int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void
                       float* dQs, void* dKs, void* dVs, float* dQf, float* dgate, float* dQ_out, void* dK, void* dV,
                       int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* Backward of flare_pp_forward_norm: the FLARE++ backward through the
+ * per-head RMS norms of norm_flags (App. A.3, A.4 and Table 2 in A.7 for the
+ * norms; App. B.5 for the rest).  The normalised inputs are formed again
+ * (bf16, like the inputs), the FLARE++ backward runs on them as
+ * flare_pp_backward does, and then each norm's reverse mode: with
+ * r = (mean_d x^2 + eps)^(-1/2) per row, xh = r x and dy the cotangent of
+ * N(x) = xh * alpha,
+ *   dx = r (dy * alpha - xh mean_d(dy * alpha * xh)),
+ *   dalpha[h, :] = sum over the rows of head h of dy * xh.
+ * Arguments as flare_pp_backward (cotangents of the raw inputs in the same
+ * places; with Vs == Ks the values' cotangent is added to dKs before the
+ * norm's backward), plus those of flare_pp_forward_norm (norm_flags, alpha_*,
+ * eps) and:
+ *   dalpha_qs, dalpha_ks, dalpha_k  [H, D] float32 outputs, required exactly
+ *               when the matching alpha is given and its flag is set (else
+ *               not written; may be NULL).
+ * Q, Z, L are the routing queries, latents and log-normalisers that
+ * flare_pp_forward_norm returned for the same inputs.  norm_flags = 0 makes
+ * this call flare_pp_backward.  ws of
+ * flare_workspace_size(FLARE_OP_PP_BACKWARD_NORM, ...) bytes (it holds the
+ * normalised seeds and keys).  Deterministic, like the other entry points. */
+int flare_pp_backward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                           const void* K, const void* V, const float* Q, const float* Z, const float* L,
+                           const void* dY, float* dQs, void* dKs, void* dVs, float* dQf, float* dgate, float* dQ_out,
+                           void* dK, void* dV, float* dalpha_qs, float* dalpha_ks, float* dalpha_k, int B, int H,
+                           int N, int M, int D, int dtype, float scale, int norm_flags, const float* alpha_qs,
+                           const float* alpha_ks, const float* alpha_k, float eps, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* flare_status_string(int status);

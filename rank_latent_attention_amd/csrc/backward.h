@@ -1039,6 +1039,201 @@ PpBwdLayout pp_bwd_layout(const Dev& dev, int B, int H, int N, int M, int D) {
   return w;
 }
 
+// ----------------------------------------------------------------------------
+// Backward through the FLARE++ input norms (App. A.3, A.4, Table 2 in A.7).
+// With r = (mean_d x^2 + eps)^(-1/2) per row and xh = r x, a norm is
+// N(x) = xh * alpha (alpha = 1 for N_0).  Its reverse mode, given the
+// cotangent dy of N(x):
+//   g = dy * alpha,  dx = r (g - xh mean_d(g xh)),  dalpha = sum_rows dy xh.
+// Rows are [bh][R][D]; a row's D / 8 16-byte chunks sit in consecutive lanes.
+// ----------------------------------------------------------------------------
+constexpr int kNormRows = 4096;  // rows per workgroup of the norm backward (at most)
+
+// y = bf16(N(x)) for nrows rows; the head of row i is (i / R) % H.
+template <int D>
+__global__ void __launch_bounds__(kThreads) norm_rows_kernel(const bf16* x, bf16* y, const float* alpha,
+                                                             long long nrows, int R, int H, float eps) {
+  constexpr int CPR = D / 8;
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long row = t / CPR;
+  const int c = (int)(t % CPR);
+  const bool live = row < nrows;
+  const long long rr = live ? row : 0;  // dead lanes follow row 0 through the shuffles
+  const bf16x8 v = reinterpret_cast<const bf16x8*>(x + rr * D)[c];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += (float)v[i] * (float)v[i];
+#pragma unroll
+  for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+  const float r = norm_factor(ss, D, eps);
+  const int h = (int)((rr / R) % H);
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = alpha ? alpha[h * D + 8 * c + i] : 1.f;
+    o[i] = (bf16)((float)v[i] * r * a);
+  }
+  if (live) reinterpret_cast<bf16x8*>(y + rr * D)[c] = o;
+}
+
+template <typename G> __device__ inline void load8(const G* p, float (&f)[8]);
+template <> __device__ inline void load8(const float* p, float (&f)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
+}
+template <> __device__ inline void load8(const bf16* p, float (&f)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+}
+template <typename G> __device__ inline void store8(G* p, const float (&f)[8]);
+template <> __device__ inline void store8(float* p, const float (&f)[8]) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{f[0], f[1], f[2], f[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{f[4], f[5], f[6], f[7]};
+}
+template <> __device__ inline void store8(bf16* p, const float (&f)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)f[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+
+// In place: g holds the cotangent of N(x) on entry and that of x on exit.
+// Workgroup w covers rows [ch kNormRows, +kNormRows) of bh = w / nch (ch =
+// w % nch) and writes its partial dalpha to part[w][D] when alpha is given
+// (summed in a fixed order, so the result is deterministic).
+template <int D, typename G>
+__global__ void __launch_bounds__(kThreads) norm_rows_backward_kernel(const bf16* x, G* g, const float* alpha,
+                                                                      float* part, int R, int nch, int H,
+                                                                      float eps) {
+  constexpr int CPR = D / 8, RPP = kThreads / CPR;
+  __shared__ float red[kThreads][9];
+  const int bh = blockIdx.x / nch, ch = blockIdx.x % nch, h = bh % H;
+  const int lr = threadIdx.x / CPR, c = threadIdx.x % CPR;
+  const int r0 = ch * kNormRows, r1 = min(R, r0 + kNormRows);
+  const int span = (r1 - r0 + RPP - 1) / RPP * RPP;  // whole passes over the live rows
+  float a[8], acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = alpha ? alpha[h * D + 8 * c + i] : 1.f;
+    acc[i] = 0.f;
+  }
+  for (int r = r0 + lr; r < r0 + span; r += RPP) {  // the same trip count on every lane
+    const bool live = r < r1;
+    const size_t off = ((size_t)bh * R + (live ? r : r0)) * D + 8 * c;
+    float xv[8], gv[8];
+    load8(x + off, xv);
+    load8(g + off, gv);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += xv[i] * xv[i];
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const float rn = norm_factor(ss, D, eps);
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dot += gv[i] * a[i] * xv[i] * rn;
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) dot += __shfl_xor(dot, o);
+    const float mean = dot / (float)D;
+    float dx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xh = xv[i] * rn;
+      dx[i] = rn * (gv[i] * a[i] - xh * mean);
+      if (live) acc[i] += gv[i] * xh;
+    }
+    if (live) store8(g + off, dx);
+  }
+  if (!alpha) return;  // uniform over the workgroup
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x, cc = d / 8, i = d % 8;
+    float sum = 0.f;
+    for (int q = 0; q < RPP; ++q) sum += red[q * CPR + cc][i];
+    part[(size_t)blockIdx.x * D + d] = sum;
+  }
+}
+
+// dalpha[h][d] from the partials of head h's B nch workgroups: one
+// workgroup per head; thread (j, d) sums partials j, j + G, ... (G = kThreads
+// / D lanes per channel), then the G sums are added in order.
+__global__ void __launch_bounds__(kThreads) dalpha_sum_kernel(const float* part, float* dalpha, int B, int H,
+                                                              int nch, int D) {
+  __shared__ float red[kThreads];
+  const int h = blockIdx.x, d = threadIdx.x % D, j = threadIdx.x / D, G = kThreads / D;
+  const int np = B * nch;
+  float s = 0.f;
+  for (int q = j; q < np; q += G) {
+    const int b = q / nch, ch = q % nch;
+    s += part[((size_t)(b * H + h) * nch + ch) * D + d];
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+    for (int q = 0; q < G; ++q) t += red[q * D + threadIdx.x];
+    dalpha[(size_t)h * D + threadIdx.x] = t;
+  }
+}
+
+int launch_norm_rows(const bf16* x, bf16* y, const float* alpha, long long nrows, int R, int H, int D, float eps,
+                     hipStream_t st) {
+  if (nrows == 0) return FLARE_OK;
+  const dim3 grid((unsigned)cdiv(nrows * (D / 8), kThreads));
+  if (D == 16) hipLaunchKernelGGL((norm_rows_kernel<16>), grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
+  else hipLaunchKernelGGL((norm_rows_kernel<32>), grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
+  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+// Rows [BHr][R][D] of cotangent g (float or bf16) with raw inputs x; B is the
+// number of row blocks per head (the batch, or 1 for [H, M, D] tensors).
+template <typename G>
+int launch_norm_rows_backward(const bf16* x, G* g, const float* alpha, float* dalpha, float* part, int B, int H,
+                              int R, int D, float eps, hipStream_t st) {
+  if (R == 0) {
+    if (alpha) {
+      hipLaunchKernelGGL(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, 0, D);
+      return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+    }
+    return FLARE_OK;
+  }
+  const int nch = (int)cdiv(R, kNormRows);
+  const dim3 grid((unsigned)((long long)B * H * nch));
+  if (D == 16)
+    hipLaunchKernelGGL((norm_rows_backward_kernel<16, G>), grid, dim3(kThreads), 0, st, x, g, alpha, part, R, nch,
+                       H, eps);
+  else
+    hipLaunchKernelGGL((norm_rows_backward_kernel<32, G>), grid, dim3(kThreads), 0, st, x, g, alpha, part, R, nch,
+                       H, eps);
+  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  if (!alpha) return FLARE_OK;
+  hipLaunchKernelGGL(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, nch, D);
+  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+}
+
+struct PpBwdNormLayout {
+  size_t pp = 0, qs = 0, ks = 0, k = 0, part = 0, total = 0;
+};
+
+// The FLARE++ backward's workspace, then the normalised seeds and keys (bf16)
+// and the per-workgroup dalpha partials.
+PpBwdNormLayout pp_bwd_norm_layout(const Dev& dev, int B, int H, int N, int M, int D) {
+  PpBwdNormLayout w;
+  w.pp = 0;
+  w.qs = align256(pp_bwd_layout(dev, B, H, N, M, D).total);
+  w.ks = w.qs + align256((size_t)H * M * D * sizeof(bf16));
+  const size_t tok = align256((size_t)B * H * N * D * sizeof(bf16));
+  w.k = w.ks + tok;
+  w.part = w.k + tok;
+  const long long nch = cdiv(N > M ? N : M, kNormRows);
+  w.total = w.part + align256((size_t)B * H * (nch > 0 ? nch : 1) * D * sizeof(float));
+  return w;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -1137,6 +1332,77 @@ int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void
   const BwdLayout we = bwd_layout(dev, false, B, H, N, M, D);
   return backward(dev, false, true, Qs, false, 0, (const bf16*)Ks, (const bf16*)Vs, Zs, Ls, nullptr, dQd, nullptr,
                   dQs, (bf16*)dKs, (bf16*)dVs, alias, nullptr, B, H, N, M, D, s, wsc + w.region, we, st);
+}
+
+int flare_pp_backward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                           const void* K, const void* V, const float* Q, const float* Z, const float* L,
+                           const void* dY, float* dQs, void* dKs, void* dVs, float* dQf, float* dgate, float* dQ_out,
+                           void* dK, void* dV, float* dalpha_qs, float* dalpha_ks, float* dalpha_k, int B, int H,
+                           int N, int M, int D, int dtype, float scale, int norm_flags, const float* alpha_qs,
+                           const float* alpha_ks, const float* alpha_k, float eps, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (norm_flags & ~FLARE_NORM_ALL) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags == 0)
+    return flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, dQs, dKs, dVs, dQf, dgate, dQ_out, dK, dV, B, H,
+                             N, M, D, dtype, scale, ws, ws_bytes, stream);
+  int rc = check_common(B, H, N, M, D, dtype, 0);
+  if (rc) return rc;
+  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
+  if (!(eps > 0.f)) return FLARE_ERR_INVALID_ARG;
+  const bool nqs = norm_flags & FLARE_NORM_QS, nks = norm_flags & FLARE_NORM_KS;
+  const bool nqf = norm_flags & FLARE_NORM_QF, nk = norm_flags & FLARE_NORM_K;
+  const float* aqs = nqs ? alpha_qs : nullptr;
+  const float* aks = nks ? alpha_ks : nullptr;
+  const float* ak = nk ? alpha_k : nullptr;
+  if ((aqs && !dalpha_qs) || (aks && !dalpha_ks) || (ak && !dalpha_k)) return FLARE_ERR_INVALID_ARG;
+  if (!Qs || !Qf || (N > 0 && (!Ks || !K))) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {aqs, aks, ak, aqs ? dalpha_qs : nullptr, aks ? dalpha_ks : nullptr, ak ? dalpha_k : nullptr};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  const PpBwdNormLayout w = pp_bwd_norm_layout(dev, B, H, N, M, D);
+  if (ws_bytes < w.total || !ws || !aligned16(ws)) return FLARE_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  hipStream_t st = (hipStream_t)stream;
+  const bool alias = Ks == Vs;
+  // 1. the normalised inputs the forward used (bf16, like the inputs); Qf is
+  //    not needed: the FLARE++ backward takes the routing queries Q as given
+  const void* Qs_n = Qs;
+  const void* Ks_n = Ks;
+  const void* K_n = K;
+  if (nqs) {
+    rc = launch_norm_rows((const bf16*)Qs, (bf16*)(wsc + w.qs), aqs, (long long)H * M, M, H, D, eps, st);
+    if (rc) return rc;
+    Qs_n = wsc + w.qs;
+  }
+  if (nks) {
+    rc = launch_norm_rows((const bf16*)Ks, (bf16*)(wsc + w.ks), aks, (long long)B * H * N, N, H, D, eps, st);
+    if (rc) return rc;
+    Ks_n = wsc + w.ks;
+  }
+  if (nk) {
+    rc = launch_norm_rows((const bf16*)K, (bf16*)(wsc + w.k), ak, (long long)B * H * N, N, H, D, eps, st);
+    if (rc) return rc;
+    K_n = wsc + w.k;
+  }
+  // 2. the FLARE++ backward on them; shared synthesis values are the
+  //    normalised keys, so their cotangent joins the keys' before step 3
+  rc = flare_pp_backward(Qs_n, Ks_n, alias ? Ks_n : Vs, Qf, gate, K_n, V, Q, Z, L, dY, dQs, dKs, dVs, dQf, dgate,
+                         dQ_out, dK, dV, B, H, N, M, D, dtype, scale, ws, w.qs, stream);
+  if (rc) return rc;
+  // 3. each norm's backward, in place on the cotangents
+  float* part = (float*)(wsc + w.part);
+  if (nqs && (rc = launch_norm_rows_backward((const bf16*)Qs, dQs, aqs, dalpha_qs, part, 1, H, M, D, eps, st)))
+    return rc;
+  if (nqf && (rc = launch_norm_rows_backward((const bf16*)Qf, dQf, (const float*)nullptr, nullptr, part, 1, H, M, D,
+                                              eps, st)))
+    return rc;
+  if (nks && (rc = launch_norm_rows_backward((const bf16*)Ks, (bf16*)dKs, aks, dalpha_ks, part, B, H, N, D, eps, st)))
+    return rc;
+  if (nk && (rc = launch_norm_rows_backward((const bf16*)K, (bf16*)dK, ak, dalpha_k, part, B, H, N, D, eps, st)))
+    return rc;
+  return FLARE_OK;
 }
 
 }  // extern "C"

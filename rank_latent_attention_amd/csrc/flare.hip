@@ -1730,13 +1730,15 @@ const char* flare_status_string(int status) {
 
 size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype) {
   if (check_common(B, H, N, M, D, dtype, 0) != FLARE_OK) return 0;
-  if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_BACKWARD) return 0;
+  if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_BACKWARD_NORM) return 0;
   if (op == FLARE_OP_DECODE) return 0;
   Dev dev;
   if (query_dev(dev) != FLARE_OK) return 0;
-  if (op == FLARE_OP_BACKWARD || op == FLARE_OP_ENCODE_BACKWARD || op == FLARE_OP_PP_BACKWARD) {
+  if (op == FLARE_OP_BACKWARD || op == FLARE_OP_ENCODE_BACKWARD || op == FLARE_OP_PP_BACKWARD ||
+      op == FLARE_OP_PP_BACKWARD_NORM) {
     if (dtype != FLARE_BF16) return 0;
     if (op == FLARE_OP_PP_BACKWARD) return pp_bwd_layout(dev, B, H, N, M, D).total;
+    if (op == FLARE_OP_PP_BACKWARD_NORM) return pp_bwd_norm_layout(dev, B, H, N, M, D).total;
     return bwd_layout(dev, op == FLARE_OP_BACKWARD, B, H, N, M, D).total;
   }
   const bool need_z = op == FLARE_OP_FORWARD || op == FLARE_OP_PP_FORWARD;

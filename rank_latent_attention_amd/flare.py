@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libflare.so")
 
 F32, BF16 = 0, 1
 OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD, OP_BACKWARD, OP_ENCODE_BACKWARD, OP_PP_BACKWARD = 0, 1, 2, 3, 4, 5, 6
+OP_PP_BACKWARD_NORM = 7
 #: input normalisation flags of flare_pp_forward_norm (include/flare.h)
 NORM_QS, NORM_KS, NORM_QF, NORM_K = 1, 2, 4, 8
 NORM_FLAREPP = NORM_QS | NORM_KS | NORM_QF | NORM_K  # FLARE++ (Table 2)
@@ -33,7 +34,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
            "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_pp_backward",
-           "flare_status_string")
+           "flare_pp_backward_norm", "flare_status_string")
 
 _lib = None
 
@@ -64,8 +65,9 @@ def load(path: str = LIB_PATH):
     L.flare_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_encode_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_backward.argtypes = [vp] * 19 + [i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_pp_backward_norm.argtypes = [vp] * 22 + [i, i, i, i, i, i, f, i, vp, vp, vp, f, vp, sz, vp]
     for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm,
-               L.flare_backward, L.flare_encode_backward, L.flare_pp_backward):
+               L.flare_backward, L.flare_encode_backward, L.flare_pp_backward, L.flare_pp_backward_norm):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -320,3 +322,54 @@ def flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, scale: float = 0.
                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check("flare_pp_backward", rc)
     return dQs, dKs, dVs, dQf, dgate, dK, dV, dQ_out
+
+
+def flare_pp_backward_norm(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, norm_flags: int, alpha_qs=None, alpha_ks=None,
+                           alpha_k=None, eps: float = 1e-6, scale: float = 0.0, dQ_out=None, ws=None):
+    """Backward of flare_pp_forward_norm (flare_pp_backward_norm in include/flare.h):
+    cotangents of the raw inputs and of the norms' channel scales.  Q, Z, L are
+    that forward's routing queries, latents and log-normalisers.  Returns
+    (dQs, dKs, dVs, dQf, dgate, dK, dV, dalpha_qs, dalpha_ks, dalpha_k, dQ_out);
+    dVs is None when Vs is Ks, each dalpha None unless its scale is given and
+    its flag set."""
+    if K.dim() != 4:
+        raise ValueError("K must be [B,H,N,D]")
+    B, H, N, D = K.shape
+    if Qs.dim() != 3 or Qs.shape[0] != H or Qs.shape[2] != D or Qf.shape != Qs.shape:
+        raise ValueError("Qs and Qf must be [H,M,D]")
+    M = Qs.shape[1]
+    dt = _dtype_code(K)
+    for t in (Qs, Ks, Vs, Qf, V, dY):
+        if t.dtype != K.dtype:
+            raise ValueError("Qs, Ks, Vs, Qf, K, V, dY must share one dtype")
+    if Ks.shape != K.shape or Vs.shape != K.shape or V.shape != K.shape or dY.shape != K.shape:
+        raise ValueError("Ks, Vs, K, V, dY must all be [B,H,N,D]")
+    if gate.dtype != torch.float32 or gate.numel() != H:
+        raise ValueError("gate must be float32 [H]")
+    for t, shp in ((Q, (B, H, M, D)), (Z, (B, H, M, D)), (L, (B, H, M))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shp:
+            raise ValueError("Q, Z must be float32 [B,H,M,D] and L float32 [B,H,M]")
+    for a in (alpha_qs, alpha_ks, alpha_k):
+        if a is not None and (a.dtype != torch.float32 or tuple(a.shape) != (H, D)):
+            raise ValueError("alpha arrays must be float32 [H, D]")
+    alias = Vs.data_ptr() == Ks.data_ptr()
+    dev = K.device
+    dQs = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+    dQf = torch.empty((H, M, D), dtype=torch.float32, device=dev)
+    dgate = torch.empty((H,), dtype=torch.float32, device=dev)
+    dKs, dK, dV = torch.empty_like(K), torch.empty_like(K), torch.empty_like(K)
+    dVs = None if alias else torch.empty_like(K)
+
+    def da(a, bit):
+        return torch.empty((H, D), dtype=torch.float32, device=dev) if a is not None and norm_flags & bit else None
+    da_qs, da_ks, da_k = da(alpha_qs, NORM_QS), da(alpha_ks, NORM_KS), da(alpha_k, NORM_K)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out, alpha_qs, alpha_ks, alpha_k)
+    ws = workspace(OP_PP_BACKWARD_NORM, B, H, N, M, D, dt, dev) if ws is None else ws
+    rc = load().flare_pp_backward_norm(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Q),
+                                       _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQs), _ptr(dKs), _ptr(dVs), _ptr(dQf),
+                                       _ptr(dgate), _ptr(dQ_out), _ptr(dK), _ptr(dV), _ptr(da_qs), _ptr(da_ks),
+                                       _ptr(da_k), B, H, N, M, D, dt, float(scale), int(norm_flags), _ptr(alpha_qs),
+                                       _ptr(alpha_ks), _ptr(alpha_k), float(eps), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(dev))
+    _check("flare_pp_backward_norm", rc)
+    return dQs, dKs, dVs, dQf, dgate, dK, dV, da_qs, da_ks, da_k, dQ_out

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
                                            "flare_pp_forward", "flare_pp_forward_norm", "flare_backward",
-                                           "flare_encode_backward", "flare_pp_backward", "flare_status_string"])
+                                           "flare_encode_backward", "flare_pp_backward", "flare_pp_backward_norm",
+                                           "flare_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -131,3 +132,25 @@ def ppb(lib, dt=1, D=16, Vs=FAKE, dVs=FAKE, Q=FAKE, dgate=FAKE, dQo=None):
 ])
 def test_pp_backward_rejects_bad_arguments(lib, kw, status):
     assert ppb(lib, **kw) == status
+
+
+def ppbn(lib, dt=1, D=16, flags=15, eps=1e-6, aqs=FAKE, daqs=FAKE, ak=FAKE, dak=FAKE, Q=FAKE):
+    return lib.flare_pp_backward_norm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, Q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None, FAKE, FAKE, None, FAKE, FAKE, daqs, None, dak, 1, 1, 8, 8, D, dt, 0.0,
+                                      flags, aqs, None, ak, eps, FAKE, 1 << 30, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=16), 1), (dict(dt=0), 2), (dict(D=20), 2), (dict(eps=0.0), 1), (dict(eps=-1.0), 1),
+    (dict(daqs=None), 1),                 # a scale given with its flag set needs its cotangent
+    (dict(dak=None), 1), (dict(aqs=MISALIGNED), 1), (dict(dak=MISALIGNED), 1),
+    (dict(flags=0, Q=None), 1),           # no norms: the call is flare_pp_backward, with its checks
+])
+def test_pp_backward_norm_rejects_bad_arguments(lib, kw, status):
+    assert ppbn(lib, **kw) == status
+
+
+def test_pp_backward_norm_workspace_holds_the_normalised_inputs(lib):
+    # no device here: the size query fails closed (0) rather than guessing
+    assert lib.flare_workspace_size(7, 1, 1, 8, 8, 16, 0) == 0   # bf16 only
+    assert lib.flare_workspace_size(8, 1, 1, 8, 8, 16, 1) == 0   # unknown op

@@ -317,3 +317,91 @@ def test_backward_scores_beyond_the_unshifted_range(flare, orc):
     dY = cotangent(142, "dy", K.shape)
     say("[backward] log2 scores up to 160")
     compare(orc, flare, Q, K, V, dY, scale=1.0 / math.log2(math.e))
+
+
+# --------------------------------------------------------------------------
+# Backward through the fused input norms (flare_pp_backward_norm) against
+# oracle.flare_pp_backward_normed, pinned in test_oracle_norm_backward_pins.py
+# --------------------------------------------------------------------------
+
+NORM_EPS = 1e-6
+
+
+def gpu_pp_backward_norm(flare, w, dY, flags):
+    """GPU fused-norm FLARE++ forward, then its backward; host gradients in the
+    oracle's order (dQs, dKs, dVs or None, dQf, dgate, dK, dV, dalpha_qs,
+    dalpha_ks, dalpha_k)."""
+    import torch
+    d = "bf16"
+    Qs, Ks, Qf, K, V = dev(w.Qs, d), dev(w.Ks, d), dev(w.Qf, d), dev(w.K, d), dev(w.V, d)
+    Vs = Ks if w.Vs is w.Ks else dev(w.Vs, d)
+    gate = dev(w.gate, "f32")
+
+    def a(x, bit):
+        return dev(x, "f32") if x is not None and flags & bit else None
+    aqs, aks, ak = a(w.alpha_qs, 1), a(w.alpha_ks, 2), a(w.alpha_k, 8)
+    B, H, N, D = K.shape
+    M = Qs.shape[1]
+    Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    flare.flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, flags, aqs, aks, ak, eps=NORM_EPS, Q_out=Qo, Z=Z, L=L)
+    out = flare.flare_pp_backward_norm(Qs, Ks, Vs, Qf, gate, K, V, Qo, Z, L, dev(dY, d), flags, aqs, aks, ak,
+                                       eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return tuple(None if x is None else host(x) for x in out[:10])
+
+
+def oracle_pp_backward_norm(orc, w, dY, flags):
+    f = dict(norm_qs=bool(flags & 1), norm_ks=bool(flags & 2), norm_qf=bool(flags & 4), norm_k=bool(flags & 8),
+             alpha_qs=w.alpha_qs if flags & 1 else None, alpha_ks=w.alpha_ks if flags & 2 else None,
+             alpha_k=w.alpha_k if flags & 8 else None, eps=NORM_EPS)
+    return orc.flare_pp_backward_normed(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V, dY, **f)
+
+
+PPN_NAMES = PP_NAMES + ("dalpha_qs", "dalpha_ks", "dalpha_k")
+
+
+@pytest.mark.parametrize("variant,B,H,N,M,D", [
+    ("flarepp", 2, 2, 1500, 64, 32), ("flarepp", 1, 3, 777, 33, 16),
+    ("simplified", 2, 2, 1000, 64, 32), ("simplified", 1, 2, 700, 48, 16),
+])
+def test_pp_backward_norm(flare, orc, variant, B, H, N, M, D):
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian_pp_raw
+    w = make_gaussian_pp_raw(B, H, N, M, D, "bf16", seed=121, variant=variant)
+    dY = cotangent(122, "dy", w.K.shape)
+    flags = w.norm_flags
+    say(f"[pp backward, norms {flags}] {variant} B{B} H{H} N{N} M{M} D{D}")
+    got = gpu_pp_backward_norm(flare, w, dY, flags)
+    ref = oracle_pp_backward_norm(orc, w, dY, flags)
+    for n, g, r in zip(PPN_NAMES, got, ref):
+        if r is None:
+            assert g is None, n
+            continue
+        assert np.all(np.isfinite(g)), n
+        check(n, g, r)
+
+
+def test_pp_backward_norm_flags_zero_is_pp_backward(flare):
+    # norm_flags = 0 makes the call flare_pp_backward, bit for bit
+    import torch
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian_pp
+    w = make_gaussian_pp(1, 2, 900, 32, 32, "bf16", seed=123, share_vs=True)
+    dY = cotangent(124, "dy", w.K.shape)
+    d = "bf16"
+    Qs, Ks, Qf, K, V = dev(w.Qs, d), dev(w.Ks, d), dev(w.Qf, d), dev(w.K, d), dev(w.V, d)
+    gate = dev(w.gate, "f32")
+    B, H, N, D = K.shape
+    M = Qs.shape[1]
+    Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    flare.flare_pp_forward(Qs, Ks, Ks, Qf, gate, K, V, Q_out=Qo, Z=Z, L=L)
+    dy = dev(dY, d)
+    a = flare.flare_pp_backward(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dy)
+    b = flare.flare_pp_backward_norm(Qs, Ks, Ks, Qf, gate, K, V, Qo, Z, L, dy, 0)
+    torch.cuda.synchronize()
+    for x, y in zip(a[:7], b[:7]):
+        assert (x is None) == (y is None)
+        if x is not None:
+            assert torch.equal(x, y)
