@@ -405,3 +405,32 @@ def test_pp_backward_norm_flags_zero_is_pp_backward(flare):
         assert (x is None) == (y is None)
         if x is not None:
             assert torch.equal(x, y)
+
+
+def test_pp_norm_million_token_backward_one_head(flare, orc):
+    # the million-point FLARE++ workload before its norms (flags 15), forward
+    # and backward launched whole as the benchmark runs them; one head checked
+    # in full against the oracle (the channel-scale cotangents sum over all
+    # 2^20 tokens of that head)
+    from rank_latent_attention_amd.inputs import config5_raw, cotangent
+    w = config5_raw()
+    dY = cotangent(115, "dy", w.K.shape)
+    say(f"[c5pp norm backward] {w.name} B{w.B} H{w.H} N{w.N} M{w.M} D{w.D} flags {w.norm_flags}")
+    got = gpu_pp_backward_norm(flare, w, dY, w.norm_flags)
+    h = 3
+    sl = slice(h, h + 1)
+
+    def a(x):
+        return None if x is None else x[sl]
+    Ks = w.Ks[:, sl]
+    ref = orc.flare_pp_backward_normed(w.Qs[sl], Ks, Ks, w.Qf[sl], w.gate[sl], w.K[:, sl], w.V[:, sl], dY[:, sl],
+                                       norm_qs=True, norm_ks=True, norm_qf=True, norm_k=True, alpha_qs=a(w.alpha_qs),
+                                       alpha_ks=None, alpha_k=a(w.alpha_k), eps=NORM_EPS)
+    heads = (got[0][sl], got[1][:, sl], None, got[3][sl], got[4][sl], got[5][:, sl], got[6][:, sl], got[7][sl],
+             None, got[9][sl])
+    for n, g, r in zip(PPN_NAMES, heads, ref):
+        if r is None:
+            assert g is None, n
+            continue
+        assert np.all(np.isfinite(g)), n
+        check(f"head {h} {n}", g, r)
