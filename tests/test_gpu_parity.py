@@ -147,6 +147,8 @@ SHAPES = [  # B, H, N, M, D
     (1, 1, 1, 1, 16), (1, 1, 5, 3, 16), (1, 2, 31, 32, 32), (2, 3, 100, 33, 32), (1, 2, 300, 65, 16),
     (1, 1, 1000, 200, 32), (2, 2, 257, 256, 16), (1, 1, 129, 96, 32), (3, 1, 4099, 128, 16),
     (1, 1, 20000, 256, 32), (1, 1, 640, 17, 16),
+    # every compile-time latent block count of the bf16 decode (2, 4, 8) at both widths
+    (2, 1, 1500, 64, 32), (1, 2, 777, 128, 32), (1, 1, 2050, 64, 16),
 ]
 
 
