@@ -434,3 +434,19 @@ def test_pp_norm_million_token_backward_one_head(flare, orc):
             continue
         assert np.all(np.isfinite(g)), n
         check(f"head {h} {n}", g, r)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_random_shapes(flare, orc, seed):
+    # seeded random shapes: ragged token counts, latent counts off the 32-grid,
+    # both widths, shared and per-batch queries
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian
+    rng = np.random.default_rng(300 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    N, M, D = int(rng.integers(1, 2500)), int(rng.integers(1, 257)), int(rng.choice([16, 32]))
+    qb = bool(rng.integers(0, 2))
+    w = make_gaussian(B, H, N, M, D, "bf16", seed=310 + seed)
+    Q = np.broadcast_to(w.Q, (B,) + w.Q.shape).copy() if qb else w.Q
+    dY = cotangent(320 + seed, "dy", w.K.shape)
+    say(f"[backward random] B{B} H{H} N{N} M{M} D{D} q_batched {qb}")
+    compare(orc, flare, Q, w.K, w.V, dY)

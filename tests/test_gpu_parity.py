@@ -321,3 +321,30 @@ def test_workspace_too_small_is_rejected(flare):
     with pytest.raises(FlareError) as e:
         flare.flare_forward(Q, K, K, ws=ws)
     assert e.value.status == 3
+
+
+def _random_shapes(seed, count):
+    """Seeded random (B, H, N, M, D): ragged token counts (including fewer
+    tokens than a tile or a workgroup piece), latent counts off the 32-grid
+    and both widths."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 3000)),
+                    int(rng.integers(1, 257)), int(rng.choice([16, 32]))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(2024, 12), ids=lambda s: "B{}H{}N{}M{}D{}".format(*s))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_random_shapes(flare, orc, shape, dtype):
+    from rank_latent_attention_amd.inputs import make_gaussian
+    B, H, N, M, D = shape
+    w = make_gaussian(B, H, N, M, D, dtype, seed=7 * N + M)
+    say(f"[random shape] {shape} {dtype}")
+    Y, Z, L = run_flare(flare, w)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    tol = TOL[dtype]
+    check("Z", Z, Zr, tol)
+    check_lse("L", L, Lr, tol)
+    check("Y", Y, Yr, tol)
