@@ -42,6 +42,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def device_info() -> dict:
+    """Where the line was measured: device name, gfx architecture, HIP runtime."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def kernel_source_sha256() -> str:
     """sha256 over the code of the kernel sources (csrc/*.hip and *.h, by name), with
     // comments, trailing blanks and empty lines left out: a comment edit does not
@@ -108,7 +126,8 @@ def cpu_baseline(w, target_s: float = 15.0):
     what = "FLARE++ forward (synthesis encode, blend, encode + decode)" if w.pp else "FLARE forward (encode + decode)"
     if w.norm_flags:
         what = "FLARE++ forward with its per-head RMS norms (norms, synthesis encode, blend, encode + decode)"
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
+            "host_logical_cpus": os.cpu_count(),
             "sample": f"fp64 oracle {what} on heads 0..{k - 1} of {w.H}, all {w.N} tokens, "
                       f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
 
@@ -225,7 +244,8 @@ def cpu_baseline_backward(w, dY, target_s: float = 15.0):
     n = int(min(w.N, max(n1, n1 * target_s / max(t1, 1e-3))))
     t = run(n) if n > n1 else t1
     value = w.B * n / (t * w.H)   # a token of the whole pass needs all H heads
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
+            "host_logical_cpus": os.cpu_count(),
             "sample": f"fp64 oracle {'FLARE++' if w.pp else 'FLARE'} backward (forward recompute, decoder and "
                       f"encoder backward{', blend and synthesis backward' if w.pp else ''}"
                       f"{', through the per-head RMS norms' if w.norm_flags else ''}) on head 0 of "
@@ -400,7 +420,7 @@ def main():
                       "B": B, "H": H, "N": N, "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "step_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-           "roofline": roofline}
+           "roofline": roofline, "device": device_info()}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
@@ -502,7 +522,7 @@ def bench_backward(args, pp=False, norm=False):
            "config": {"workload": f"{what} routing backward, million-point surface mesh"
                                   + (", through the per-head RMS norms" if norm else ""), "B": B, "H": H, "N": N,
                       "M": M, "D": D, "inputs": "bf16", "accumulate": "f32"},
-           "tflops": round(achieved, 2), "roofline": roofline}
+           "tflops": round(achieved, 2), "roofline": roofline, "device": device_info()}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_backward(w, dYh)
     print(json.dumps(out), flush=True)
