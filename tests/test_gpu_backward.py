@@ -450,3 +450,29 @@ def test_backward_random_shapes(flare, orc, seed):
     dY = cotangent(320 + seed, "dy", w.K.shape)
     say(f"[backward random] B{B} H{H} N{N} M{M} D{D} q_batched {qb}")
     compare(orc, flare, Q, w.K, w.V, dY)
+
+
+def test_pp_backward_norm_without_tokens(flare):
+    # N = 0: the synthesised queries are 0, so the routing queries are N_0(Qf),
+    # Z = 0 and L = -inf; every cotangent, the channel scales' included, is 0
+    import torch
+    B, H, M, D = 2, 2, 40, 32
+    dev_ = "cuda:0"
+    Qs = torch.randn(H, M, D, device=dev_).to(torch.bfloat16)
+    Qf = torch.randn(H, M, D, device=dev_).to(torch.bfloat16)
+    K = torch.empty((B, H, 0, D), dtype=torch.bfloat16, device=dev_)
+    gate = torch.full((H,), 0.5, device=dev_)
+    aqs = 1.0 + 0.1 * torch.randn(H, D, device=dev_)
+    ak = 1.0 + 0.1 * torch.randn(H, D, device=dev_)
+    Qo = torch.empty((B, H, M, D), device=dev_)
+    Z = torch.empty((B, H, M, D), device=dev_)
+    L = torch.empty((B, H, M), device=dev_)
+    flare.flare_pp_forward_norm(Qs, K, K, Qf, gate, K, K, 15, aqs, None, ak, eps=NORM_EPS, Q_out=Qo, Z=Z, L=L)
+    out = flare.flare_pp_backward_norm(Qs, K, K, Qf, gate, K, K, Qo, Z, L, K, 15, aqs, None, ak, eps=NORM_EPS)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(L)) and torch.count_nonzero(Z).item() == 0
+    dQs, dKs, dVs, dQf, dgate, dK, dV, da_qs, da_ks, da_k, _ = out
+    assert dVs is None and da_ks is None
+    for t in (dQs, dQf, dgate, da_qs, da_k):
+        assert torch.all(torch.isfinite(t)) and torch.count_nonzero(t).item() == 0
+    assert dKs.numel() == 0 and dK.numel() == 0 and dV.numel() == 0
