@@ -1067,12 +1067,19 @@ __global__ void __launch_bounds__(kThreads) norm_rows_kernel(const bf16* x, bf16
   for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
   const float r = norm_factor(ss, D, eps);
   const int h = (int)((rr / R) % H);
+  float a[8];
+  if (alpha) {
+    const f32x4* ap = reinterpret_cast<const f32x4*>(alpha + h * D + 8 * c);
+    const f32x4 a0 = ap[0], a1 = ap[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = a0[i] * r; a[4 + i] = a1[i] * r; }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = r;
+  }
   bf16x8 o;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = alpha ? alpha[h * D + 8 * c + i] : 1.f;
-    o[i] = (bf16)((float)v[i] * r * a);
-  }
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[i] * a[i]);
   if (live) reinterpret_cast<bf16x8*>(y + rr * D)[c] = o;
 }
 
@@ -1114,11 +1121,17 @@ __global__ void __launch_bounds__(kThreads) norm_rows_backward_kernel(const bf16
   const int r0 = ch * kNormRows, r1 = min(R, r0 + kNormRows);
   const int span = (r1 - r0 + RPP - 1) / RPP * RPP;  // whole passes over the live rows
   float a[8], acc[8];
+  if (alpha) {
+    const f32x4* ap = reinterpret_cast<const f32x4*>(alpha + h * D + 8 * c);
+    const f32x4 a0 = ap[0], a1 = ap[1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = alpha ? alpha[h * D + 8 * c + i] : 1.f;
-    acc[i] = 0.f;
+    for (int i = 0; i < 4; ++i) { a[i] = a0[i]; a[4 + i] = a1[i]; }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 1.f;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int r = r0 + lr; r < r0 + span; r += RPP) {  // the same trip count on every lane
     const bool live = r < r1;
     const size_t off = ((size_t)bh * R + (live ? r : r0)) * D + 8 * c;

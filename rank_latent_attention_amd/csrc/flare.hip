@@ -1228,12 +1228,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         if (c < pq) {
           const int m = c * QE / D, d0 = c * QE % D;
           const QT* src = reinterpret_cast<const QT*>(&qv[j]);
-          const float* qm = a.qmul ? a.qmul + (size_t)h * D + d0 : nullptr;
+          float qm[QE];  // the channel scale of these QE features (16-byte aligned), or ones
+          if (a.qmul) {
+#pragma unroll
+            for (int k = 0; k < QE / 4; ++k) {
+              const f32x4 t = reinterpret_cast<const f32x4*>(a.qmul + (size_t)h * D + d0)[k];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) qm[4 * k + i] = t[i];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < QE; ++i) qm[i] = 1.f;
+          }
 #pragma unroll
           for (int i = 0; i < QE; ++i) {
-            float q = c < nq ? to_f(src[i]) * a.qscale : 0.f;
-            if (qm) q *= qm[i];
-            qs[m * L::QST + d0 + i] = from_f<T>(q);
+            const float q = c < nq ? to_f(src[i]) * a.qscale : 0.f;
+            qs[m * L::QST + d0 + i] = from_f<T>(q * qm[i]);
           }
         }
       }
