@@ -132,7 +132,30 @@ def cpu_baseline(w, target_s: float = 15.0):
                       f"M={w.M}, D={w.D}: {t:.1f} s on {cores} OpenMP threads; tokens/s scaled by {k}/{w.H} heads"}
 
 
-def time_configs(names: str) -> None:
+def oracle_times(w) -> dict:
+    """Wall time of the fp64 oracle of this workload's forward on the host,
+    on one thread and on all the threads the oracle uses by default."""
+    import oracle
+    oracle.build(force=False)
+    full = oracle.threads()
+
+    def run():
+        t0 = time.perf_counter()
+        if w.pp:
+            oracle.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+        else:
+            oracle.flare_forward(w.Q, w.K, w.V)
+        return time.perf_counter() - t0
+
+    oracle.threads(1)
+    t1 = run()
+    oracle.threads(full)
+    tn = run()
+    return {"oracle_s_1_thread": round(t1, 3), "oracle_s": round(tn, 3), "oracle_threads": full,
+            "oracle_tokens_per_s": w.B * w.N / tn}
+
+
+def time_configs(names: str, with_oracle: bool = False) -> None:
     """Per-workload forward timing (inputs resident, events on the library's
     stream): one JSON line per workload, not the bench line."""
     import torch
@@ -203,6 +226,8 @@ def time_configs(names: str) -> None:
             tc = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))
             rec["us_median_cold"] = round(tc[n // 2], 1)
             del flush
+        if with_oracle and w.N * w.B * w.H * w.M <= (1 << 30):  # the million-token runs stay with the bench line
+            rec.update(oracle_times(w))
         print(json.dumps(rec), flush=True)
         del K, V, Y, Z, L, ws
         torch.cuda.empty_cache()
@@ -276,6 +301,9 @@ def main():
                          "from rank_latent_attention_amd.inputs.CONFIGS, or 'all'): 10 warmup and 50 timed calls "
                          "each, one JSON line per workload with the median, min and max, plus a cold-cache "
                          "median (512 MB written before each call) where the working set is under 256 MB")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="with --configs: also time the fp64 oracle of each workload's forward on the host, on one "
+                         "thread and on all of them (skipped for the million-token workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB float32 scale kernel (read 256 MiB, write 256 MiB) before the steps, as a "
                          "known-size reference for HBM byte counters")
@@ -290,7 +318,7 @@ def main():
     from rank_latent_attention_amd.inputs import config5, config5_raw, config5_simplified
 
     if args.configs:
-        time_configs(args.configs)
+        time_configs(args.configs, args.oracle_times)
         return
     if args.workload in ("flare_backward", "flare_pp_backward", "flare_pp_norm_backward"):
         bench_backward(args, pp=args.workload != "flare_backward", norm=args.workload == "flare_pp_norm_backward")
