@@ -1007,15 +1007,16 @@ struct MergeArgs {
 // Running (A, den, num) of a set of splits: max shift, and sum of l_p and of
 // U_p scaled to 2^A.  Empty sets have A = -inf, den = num = 0.
 struct MergeState {
-  float A, den, num;
+  float A, den;
+  f32x4 num;  // four features of the latent
 };
 
-__device__ inline MergeState merge_fold(MergeState s, float a, float l, float u) {
+__device__ inline MergeState merge_fold(MergeState s, float a, float l, const f32x4& u) {
   if (l > 0.f) {
     if (a > s.A) {
       const float f = fast_exp2(s.A - a);  // 0 while A = -inf
       s.den *= f;
-      s.num *= f;
+      s.num = s.num * f;
       s.A = a;
     }
     const float w = fast_exp2(a - s.A);
@@ -1025,8 +1026,6 @@ __device__ inline MergeState merge_fold(MergeState s, float a, float l, float u)
   return s;
 }
 
-// Symmetric in its arguments (max and + commute exactly), so both lanes of a
-// butterfly pair obtain bitwise the same state.
 __device__ inline MergeState merge_pair(MergeState x, MergeState y) {
   const float A = fmaxf(x.A, y.A);
   if (!(A > -INFINITY)) return x;
@@ -1040,37 +1039,41 @@ __device__ inline MergeState merge_pair(MergeState x, MergeState y) {
 #endif
 constexpr int kMergeBatch = FLARE_MERGE_BATCH;
 
-// One wave per (head, latent): lane (pg, d) folds the splits p = pg, pg + PGW,
-// ... (PGW = 64 / D lane groups) in ascending order, and the PGW group states
-// are combined by a fixed xor butterfly over the group bits of the lane.
+// One wave per (head, latent).  Lane (pg, c) owns features 4c .. 4c + 3 and
+// folds the splits p = pg, pg + PGW, ... (PGW = 64 / (D / 4) lane groups) in
+// ascending order, all of a batch's loads issued before any is folded; the
+// PGW group states are then combined by a fixed xor butterfly over the group
+// bits of the lane, and group 0 writes the result.
 template <typename QT>
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   // B H M < 2^31 (checked on the host): 32-bit index arithmetic
   const unsigned pair = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (pair >= (unsigned)a.nbh * (unsigned)a.M) return;  // the whole wave
-  const int D = a.D, PGW = 64 / D;
-  const int pg = lane / D, d = lane % D;
+  const int D = a.D, CPS = D / 4, PGW = 64 / CPS;
+  const int pg = lane / CPS, c = lane % CPS;
   const int m = (int)(pair % (unsigned)a.M);
   const int bhl = (int)(pair / (unsigned)a.M);
   const int bh = a.bh0 + bhl;
-  MergeState st{-INFINITY, 0.f, 0.f};
+  MergeState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
   if (a.N > 0) {
     const long long hb = (long long)bhl * a.N;
     const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
-    // batches of kMergeBatch splits: all loads are issued before any is
-    // folded (slots past cnt re-read split pg and count as empty), so a batch
-    // costs one memory round trip instead of two dependent ones per split
+    // slots past cnt load nothing and count as empty
     for (int p0 = pg; p0 < cnt; p0 += kMergeBatch * PGW) {
       float2 v[kMergeBatch];
-      float u[kMergeBatch];
+      f32x4 u[kMergeBatch];
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
         const int p = p0 + j * PGW;
-        const size_t i = (base + (p < cnt ? p : pg)) * a.M + m;
-        v[j] = a.part_al[i];
-        u[j] = a.part_acc[i * D + d];
+        v[j] = make_float2(-INFINITY, 0.f);
+        u[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p < cnt) {
+          const size_t i = (base + p) * a.M + m;
+          v[j] = a.part_al[i];
+          u[j] = reinterpret_cast<const f32x4*>(a.part_acc + i * D)[c];
+        }
       }
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) asm volatile("" ::"v"(v[j]), "v"(u[j]));
@@ -1078,36 +1081,43 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
       for (int j = 0; j < kMergeBatch; ++j) st = merge_fold(st, v[j].x, p0 + j * PGW < cnt ? v[j].y : 0.f, u[j]);
     }
   }
-  for (int o = D; o < 64; o <<= 1) {
+  for (int o = CPS; o < 64; o <<= 1) {
     MergeState t;
     t.A = __shfl_xor(st.A, o);
     t.den = __shfl_xor(st.den, o);
-    t.num = __shfl_xor(st.num, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.num[i] = __shfl_xor(st.num[i], o);
     st = merge_pair(st, t);
   }
   const int h = bh % a.H;
-  float qf = 0.f;
-  if (a.Qout) {  // blend mode: the fixed query, N_0 over its D lanes while every lane group is active
-    qf = to_f(reinterpret_cast<const QT*>(a.Qf)[((size_t)h * a.M + m) * D + d]);
+  float qf[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.Qout) {  // blend mode: the fixed query, N_0 over its D features while every lane group is active
+    const QT* q = reinterpret_cast<const QT*>(a.Qf) + ((size_t)h * a.M + m) * D + 4 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = to_f(q[i]);
     if (a.norm_qf) {
-      float ss = qf * qf;
-      for (int o = 1; o < D; o <<= 1) ss += __shfl_xor(ss, o);
-      qf *= norm_factor(ss, D, a.eps);
+      float ss = qf[0] * qf[0] + qf[1] * qf[1] + qf[2] * qf[2] + qf[3] * qf[3];
+      for (int o = 1; o < CPS; o <<= 1) ss += __shfl_xor(ss, o);
+      const float r = norm_factor(ss, D, a.eps);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[i] *= r;
     }
   }
   if (pg != 0) return;
-  float z = 0.f, lse = -INFINITY;
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
   if (st.A > -INFINITY) {
     z = st.num / st.den;
     lse = kLn2 * (st.A + __builtin_amdgcn_logf(st.den));
   }
-  if (a.zmul) z *= a.zmul[(size_t)h * D + d];
-  const size_t o = ((size_t)bh * a.M + m) * D + d;
+  if (a.zmul) z = z * reinterpret_cast<const f32x4*>(a.zmul + (size_t)h * D)[c];
+  const size_t o = ((size_t)bh * a.M + m) * D + 4 * c;
   if (a.Qout) {
-    a.Qout[o] = qf + a.gate[h] * z;
+    const float g = a.gate[h];
+    *reinterpret_cast<f32x4*>(a.Qout + o) = f32x4{qf[0] + g * z[0], qf[1] + g * z[1], qf[2] + g * z[2], qf[3] + g * z[3]};
   } else {
-    a.Z[o] = z;
-    if (a.L && d == 0) a.L[(size_t)bh * a.M + m] = lse;
+    *reinterpret_cast<f32x4*>(a.Z + o) = z;
+    if (a.L && c == 0) a.L[(size_t)bh * a.M + m] = lse;
   }
 }
 
