@@ -178,7 +178,7 @@ def rms_norm(x, alpha=None, eps: float = 1e-6) -> np.ndarray:
         y[..., h, r, d] = x[..., h, r, d] / sqrt(mean_d x[..., h, r, :]^2 + eps) * alpha[h, d]
     ``x`` has the head axis third from last ([H, rows, D] or [B, H, rows, D]);
     ``alpha`` is [H, D], or None for N_0.  The pages do not state eps; the
-    default 1e-6 is this build's reading.
+    default 1e-6 is a reading of them, not a value they give.
     """
     x = _f64(x)
     y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
