@@ -309,8 +309,8 @@ def main():
                          "known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU path is a design, "
-              "not part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library runs on one GPU and its sharding "
+              "over several is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
