@@ -26,8 +26,15 @@
  *     Z               : [B, H, M, D] float32;  L : [B, H, M] float32
  *     Q_out           : [B, H, M, D] float32
  *     gate            : [H] float32, already g_h = sigmoid(gamma_h) (App. A.4)
- * - dtype: FLARE_F32 or FLARE_BF16.  Scores, softmax statistics and every
- *   accumulation are float32; bf16 inputs feed bf16 matrix-core products.
+ * - dtype: FLARE_F32 or FLARE_BF16.  Softmax statistics and every
+ *   accumulation are float32.  FLARE_F32 forms the scores with float32
+ *   matrix-core products.  FLARE_BF16 feeds bf16 matrix-core products: keys
+ *   and values as given; the queries scaled by s*log2(e) and rounded to bf16
+ *   wherever that rounding provably moves no score by more than 2^-5 (log2
+ *   units; checked per unit of work from the queries' rounding error and the
+ *   largest key norm), and otherwise split into a bf16 hi + lo pair so the
+ *   scores are exact to float32 accumulation; the softmax weights as bf16
+ *   (their sums are taken over the same bf16 weights).
  * - scale <= 0 selects s = 1/sqrt(D); any positive value overrides it.  The
  *   same s is used by the encode and by the decode (whose query, a token
  *   key, also has width D).
@@ -103,8 +110,7 @@ int flare_decode(const void* Q, int q_batched, const void* K, const float* Z, vo
 /* FLARE routing forward, encode then decode on one stream (App. A.1, Table 2):
  * Y = SDPA(K, Q, SDPA(Q, K, V)).  The N x M scores are never stored; the
  * decode recomputes them.  Z_out / L_out (may be NULL) receive the latents
- * and log-normalisers.  Heads are processed in groups so that a head's keys
- * are re-read by the decode while still cache resident. */
+ * and log-normalisers. */
 int flare_forward(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out,
                   float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* ws,
                   size_t ws_bytes, void* stream);

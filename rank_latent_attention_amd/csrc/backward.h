@@ -798,8 +798,7 @@ size_t row_lds(int D, int M) {
 
 template <typename QT, int D, int NW, int WN, bool DEC>
 int launch_col_k(const ColArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_col_kernel<QT, D, NW, WN, DEC>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  return launch(bwd_col_kernel<QT, D, NW, WN, DEC>, dim3(a.nwg), dim3(NW * 64), 0, st, a);
 }
 
 template <typename QT, int D, bool DEC>
@@ -822,10 +821,7 @@ int launch_col(const ColArgs& a, int D, bool dec, bool qf32, const EncPlan& p, h
   return qf32 ? launch_col_q<float>(a, D, dec, p, st) : launch_col_q<bf16>(a, D, dec, p, st);
 }
 
-#ifndef FLARE_ROW_WAVES
-#define FLARE_ROW_WAVES 8
-#endif
-constexpr int kRowWaves = FLARE_ROW_WAVES;
+constexpr int kRowWaves = 8;
 
 // The factored pass, then the exact-weight pass for the heads it flagged.
 template <typename QT, int D, bool TAIL, bool DEC, bool ENC>
@@ -838,12 +834,9 @@ int launch_row_k(const RowArgs& a, size_t lds, hipStream_t st) {
         hipFuncSetAttribute(fs, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((bwd_row_fast_kernel<QT, D, kRowWaves, TAIL, DEC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st,
-                     a);
-  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
-  hipLaunchKernelGGL((bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>), dim3(a.nwg), dim3(kRowWaves * 64), lds, st,
-                     a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  const int rc = launch(bwd_row_fast_kernel<QT, D, kRowWaves, TAIL, DEC>, dim3(a.nwg), dim3(kRowWaves * 64), lds, st, a);
+  if (rc) return rc;
+  return launch(bwd_row_kernel<QT, D, kRowWaves, TAIL, DEC, ENC>, dim3(a.nwg), dim3(kRowWaves * 64), lds, st, a);
 }
 
 template <typename QT, int D, bool DEC, bool ENC>
@@ -929,8 +922,8 @@ int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q
   uint4* srec = dec ? (uint4*)(ws + w.srec) : nullptr;
   if (N > 0) {
     if (dec) {
-      hipLaunchKernelGGL(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
-      if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+      rc = launch(center_kernel, dim3(BH), dim3(kThreads), 0, st, Z, zc, M, D);
+      if (rc) return rc;
       rc = launch_stats(dev, Q, qf32, q_batched, K, zc, dY, srec, BH, H, N, M, D, qs, st);
       if (rc) return rc;
       ColArgs cd = ca;
@@ -946,8 +939,8 @@ int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q
     sa.dz_in = dZ_in;  // no tokens: no partials (the split sums are empty)
   }
   if (dec || enc) {
-    hipLaunchKernelGGL(sum_dz_kernel, dim3(lat_grid), dim3(kThreads), 0, st, sa);
-    if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+    rc = launch(sum_dz_kernel, dim3(lat_grid), dim3(kThreads), 0, st, sa);
+    if (rc) return rc;
   }
   if (N > 0 && enc) {
     ColArgs ce = ca;
@@ -958,8 +951,8 @@ int backward(const Dev& dev, bool dec, bool enc, const void* Q, bool qf32, int q
   SumArgs sq = sa;
   sq.part = part_dq;
   const int QH = q_batched ? BH : H;
-  hipLaunchKernelGGL(sum_dq_kernel, dim3((unsigned)cdiv((long long)QH * M * D, kThreads)), dim3(kThreads), 0, st, sq);
-  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  rc = launch(sum_dq_kernel, dim3((unsigned)cdiv((long long)QH * M * D, kThreads)), dim3(kThreads), 0, st, sq);
+  if (rc) return rc;
   if (N == 0) return FLARE_OK;
   RowArgs ra{};
   ra.Q = Q; ra.K = K; ra.V = V; ra.dY = dY; ra.Zc = zc; ra.srec = srec; ra.dZ = dz; ra.L = L;
@@ -1197,9 +1190,8 @@ int launch_norm_rows(const bf16* x, bf16* y, const float* alpha, long long nrows
                      hipStream_t st) {
   if (nrows == 0) return FLARE_OK;
   const dim3 grid((unsigned)cdiv(nrows * (D / 8), kThreads));
-  if (D == 16) hipLaunchKernelGGL((norm_rows_kernel<16>), grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
-  else hipLaunchKernelGGL((norm_rows_kernel<32>), grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  if (D == 16) return launch(norm_rows_kernel<16>, grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
+  return launch(norm_rows_kernel<32>, grid, dim3(kThreads), 0, st, x, y, alpha, nrows, R, H, eps);
 }
 
 // Rows [BHr][R][D] of cotangent g (float or bf16) with raw inputs x; B is the
@@ -1209,23 +1201,18 @@ int launch_norm_rows_backward(const bf16* x, G* g, const float* alpha, float* da
                               int R, int D, float eps, hipStream_t st) {
   if (R == 0) {
     if (alpha) {
-      hipLaunchKernelGGL(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, 0, D);
-      return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+      return launch(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, 0, D);
     }
     return FLARE_OK;
   }
   const int nch = (int)cdiv(R, kNormRows);
   const dim3 grid((unsigned)((long long)B * H * nch));
-  if (D == 16)
-    hipLaunchKernelGGL((norm_rows_backward_kernel<16, G>), grid, dim3(kThreads), 0, st, x, g, alpha, part, R, nch,
-                       H, eps);
-  else
-    hipLaunchKernelGGL((norm_rows_backward_kernel<32, G>), grid, dim3(kThreads), 0, st, x, g, alpha, part, R, nch,
-                       H, eps);
-  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
-  if (!alpha) return FLARE_OK;
-  hipLaunchKernelGGL(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, nch, D);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  const int rc = D == 16 ? launch(norm_rows_backward_kernel<16, G>, grid, dim3(kThreads), 0, st, x, g, alpha, part, R,
+                                 nch, H, eps)
+                         : launch(norm_rows_backward_kernel<32, G>, grid, dim3(kThreads), 0, st, x, g, alpha, part, R,
+                                 nch, H, eps);
+  if (rc || !alpha) return rc;
+  return launch(dalpha_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, st, part, dalpha, B, H, nch, D);
 }
 
 struct PpBwdNormLayout {
@@ -1337,9 +1324,8 @@ int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void
                 dQb, (bf16*)dK, (bf16*)dV, false, nullptr, B, H, N, M, D, s, wsc + w.region, wr, st);
   if (rc) return rc;
   // 3. the blend
-  hipLaunchKernelGGL(blend_backward_kernel, dim3(H), dim3(kThreads), 0, st, dQb, Zs, gate, dQd, dQf, dgate, B, H, M,
-                     D);
-  if (hipGetLastError() != hipSuccess) return FLARE_ERR_HIP;
+  rc = launch(blend_backward_kernel, dim3(H), dim3(kThreads), 0, st, dQb, Zs, gate, dQd, dQf, dgate, B, H, M, D);
+  if (rc) return rc;
   // 4. the synthesis encoder's backward with dZ = dQd (dL = 0), the seeds
   //    shared over the batch
   const BwdLayout we = bwd_layout(dev, false, B, H, N, M, D);

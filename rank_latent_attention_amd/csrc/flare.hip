@@ -39,6 +39,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "flare.h"
 #include "pieces.h"
 
@@ -50,21 +53,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Softmax sums of the unshifted bf16 loops on the matrix core (see sum_mma and
-// pad_pv) rather than with float adds.
-#ifndef FLARE_MFMA_SUM
-#define FLARE_MFMA_SUM 1
-#endif
-
 constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kTile = 128;         // tokens per float32 encode LDS tile (4 blocks of 32)
-#ifndef FLARE_DMA_TILE
-#define FLARE_DMA_TILE 128
-#endif
 // Tokens per bf16 encode LDS tile (DMA-filled, double-buffered) for a
-// workgroup of NW waves: 32 per wave up to FLARE_DMA_TILE, so two tiles of K
-// and V stay within 64 KB and four waves per SIMD still fit.
-template <int NW> constexpr int dma_rows() { return FLARE_DMA_TILE < 32 * NW ? FLARE_DMA_TILE : 32 * NW; }
+// workgroup of NW waves: 32 per wave up to 128, so two tiles of K and V stay
+// within 64 KB and four waves per SIMD still fit.
+template <int NW> constexpr int dma_rows() { return 128 < 32 * NW ? 128 : 32 * NW; }
 constexpr int kDecGroup = 128;     // tokens per decode step of a workgroup (32 per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -156,10 +150,13 @@ __device__ inline float norm_factor(float sumsq, int D, float eps) { return rsqr
 // QK operand (bf16) from a query row of type QT: optionally N_0 over the
 // whole row (its other half is held by lane +-32, so all 64 lanes must call
 // this), then multiplied channel by channel by the [D] rows mul0 and mul1
-// (either may be null) and by `scale`, and rounded.
+// (either may be null) and by `scale`, and rounded to bf16.  With lo given,
+// lo receives the bf16 rounding of what that rounding left, so hi + lo is
+// the scaled row to about 2^-17 of each element.  Returns the squared
+// Euclidean norm of the rounding error of the whole row, |bf16(v) - v|^2.
 template <int D, typename QT>
-__device__ inline void load_q_row(QKOp<bf16, D>& o, const QT* row, int g, float scale, bool norm, float eps,
-                                  const float* mul0, const float* mul1) {
+__device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT* row, int g, float scale, bool norm,
+                                   float eps, const float* mul0, const float* mul1) {
   float x[D / 2];
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
@@ -172,16 +169,60 @@ __device__ inline void load_q_row(QKOp<bf16, D>& o, const QT* row, int g, float 
     for (int j = 0; j < D / 2; ++j) ss += x[j] * x[j];
     f *= norm_factor(pair_sum(ss), D, eps);
   }
+  float v[D / 2];  // x * f, then times the channel scales of this lane's features
+#pragma unroll
+  for (int j = 0; j < D / 2; ++j) v[j] = x[j] * f;
+  if (mul0) {
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) v[j] *= mul0[16 * (j >> 3) + 8 * g + (j & 7)];
+  }
+  if (mul1) {
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) v[j] *= mul1[16 * (j >> 3) + 8 * g + (j & 7)];
+  }
+  float e2 = 0.f;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int d = 16 * st + 8 * g + s;
-      float v = x[8 * st + s] * f;
-      if (mul0) v *= mul0[d];
-      if (mul1) v *= mul1[d];
-      o.v[st][s] = (bf16)v;
+      const float vs = v[8 * st + s];
+      const bf16 h = (bf16)vs;
+      const float r = vs - (float)h;
+      o.v[st][s] = h;
+      if (lo) lo->v[st][s] = (bf16)r;
+      e2 += r * r;
     }
+  return pair_sum(e2);
+}
+
+// Scores from queries rounded to bf16 (the fast loops) differ from the exact
+// ones by (bf16(q) - q) . k, at most |bf16(q) - q| |k| in absolute value (log2
+// units).  A unit of work whose largest query rounding error times largest
+// key norm stays within kScoreErr keeps the fast loop's result: every
+// exponent is then within 2^-5 of the exact one.  Otherwise the work is redone
+// with exact scores (queries as bf16 hi + lo).  Squared, as compared.
+constexpr float kScoreErr2 = 0x1p-10f;
+
+// Largest value over the 64 lanes of a wave.
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Squared Euclidean norm of a bf16 QK operand row (half in this lane, half in
+// lane +-32; all 64 lanes must call this).
+template <int D> __device__ inline float row_norm2(const QKOp<bf16, D>& o) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float s = 0.f;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bf16x2 v = {o.v[st][2 * p], o.v[st][2 * p + 1]};
+      s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+    }
+  return pair_sum(s);
 }
 
 // N_0 of a bf16 QK operand in registers (a key row, half in this lane and
@@ -290,7 +331,7 @@ __device__ inline void ones_pv(PVOp<float>& o, int li, int D) {
 // matrix-core sums, row 16 is all ones, so accumulator row 16 (register 8 of
 // the lower half) collects the column sums of the bf16 weights.
 __device__ inline void pad_pv(PVOp<bf16>& o, int li, int D) {
-  const bf16 v = (bf16)(FLARE_MFMA_SUM && D == 16 && li == 16 ? 1.f : 0.f);
+  const bf16 v = (bf16)(D == 16 && li == 16 ? 1.f : 0.f);
 #pragma unroll
   for (int s = 0; s < 8; ++s) { o.a0[s] = v; o.a1[s] = v; }
 }
@@ -337,14 +378,6 @@ __device__ inline float pack_exps(const f32x16& p, bf16x8& b0, bf16x8& b1) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) t[r] = p[2 * r] + p[2 * r + 1];
   return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-}
-
-// Scores minus the running shift -> packed weights and their lane sum.
-__device__ inline float pack_weights(const f32x16& s, bf16x8& b0, bf16x8& b1) {
-  f32x16 p;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r]);
-  return pack_exps(p, b0, b1);
 }
 
 // Unshifted weights exp2(s) packed to bf16, without their sum.
@@ -486,6 +519,32 @@ template <int D, int NW> __device__ inline void norm_tile(bf16* tile, int wave, 
       *ptr = v;
     }
   }
+}
+
+// Running maximum of the squared key norms of a swizzled bf16 tile in LDS,
+// once its DMA (and normalisation) is complete and visible: the NW waves
+// split the tile's 16-byte chunks, and the D / 8 chunks of a row, held by
+// consecutive lanes, add their partial sums by quad permutes.  Rows past the
+// piece repeat its last row, so they add no key from outside it.
+template <int D, int NW> __device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float m) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  constexpr int CPR = D / 8;
+  constexpr int CH = dma_rows<NW>() * CPR;  // a multiple of 64
+  for (int P0 = wave * 64; P0 < CH; P0 += NW * 64) {
+    const int P = P0 + lane;
+    const bf16x8 v = reinterpret_cast<const bf16x8*>(tile)[chunk_pos<D>(P / CPR, P % CPR)];
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bf16x2 w = {v[2 * p], v[2 * p + 1]};
+      s = __builtin_amdgcn_fdot2_f32_bf16(w, w, s, false);
+    }
+    // lanes 4r .. 4r + 3 (D = 32) or 2r, 2r + 1 (D = 16) hold one row
+    s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, false));  // xor 1
+    if constexpr (CPR == 4) s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, false));
+    m = fmaxf(m, s);
+  }
+  return m;
 }
 
 // Per-lane byte offsets into a swizzled tile for token block 0.  The XOR
@@ -735,27 +794,26 @@ template <> struct WSum<true, 16> {  // accumulator row 16 (pad_pv)
   __device__ void add(const f32x16& sc, bf16x8& b0, bf16x8& b1) { pack_only(sc, b0, b1); }
   __device__ float total(int, const f32x16& acc) const { return col_sum<float, 16>(0.f, acc); }
 };
-template <int D> struct WSum<false, D> {
-  float s;
-  __device__ explicit WSum(int) : s(0.f) {}
-  __device__ void add(const f32x16& sc, bf16x8& b0, bf16x8& b1) {
-    s += pack_weights(sc, b0, b1);
-    // keep the block's sum here: sunk to the end of a tile, the adds would
-    // hold every block's weights in registers until then
-    asm volatile("" : "+v"(s));
-  }
-  __device__ float total(int, const f32x16&) const { return pair_sum(s); }
-};
-template <int D> using RowSum = WSum<FLARE_MFMA_SUM != 0, D>;
+template <int D> using RowSum = WSum<true, D>;
 
 // Scores S^T = K Q^T of token block NB of the tile in buffer BO (LDS byte
 // addresses ka + BO + NB * 64 * D) against one wave's 32 latents, unshifted.
+// The key reads are inline assembly, like the transposing reads: as ordinary
+// loads the compiler cannot tell them from the DMA filling the other buffer
+// and would make them wait for it.
+template <int OFF> __device__ inline bf16x8 k_read(unsigned addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
 template <int D, int NB, int BO>
 __device__ inline f32x16 enc_scores(const unsigned (&ka)[D / 16], const QKOp<bf16, D>& qop) {
   constexpr int OFF = BO + NB * 64 * D;
   QKOp<bf16, D> kop;
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) kop.v[st] = lds_load<bf16x8>(ka[st] + OFF);
+  for (int st = 0; st < D / 16; ++st) kop.v[st] = k_read<OFF>(ka[st]);
+  if constexpr (D == 32) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kop.v[0]), "+v"(kop.v[1]));
+  else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kop.v[0]));
   return qk_mma<D>(kop, qop, f32x16{});
 }
 
@@ -811,16 +869,18 @@ __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned 
 
 // Careful recomputation of one wave's share of a piece (the token blocks
 // t0 + 32 (ng + k WN) of every `rows`-token tile), straight from global memory
-// with the exact maximum of every block (online softmax with a shift raised
+// with exact scores (the scaled queries as bf16 hi + lo, two products) and
+// the exact maximum of every block (online softmax with a shift raised
 // whenever the block maximum exceeds it by more than kTheta).  Used only when
-// the fast loop reported weights too large to accumulate safely.
+// the fast loop's rounded queries could shift a score by more than its bound,
+// or its weights left the float range.
 // With NK the key rows are N_0-normalised as they are loaded, and so are the
 // values when they alias the keys.  Returns the final shift of this lane's
 // latent.
 template <int D, bool NK>
 __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alias, float eps, int n_lo, int n_hi,
-                                       int ng, int WN, int rows, int lane, const QKOp<bf16, D>& qop, float& lsum,
-                                       f32x16& acc) {
+                                       int ng, int WN, int rows, int lane, const QKOp<bf16, D>& qhi,
+                                       const QKOp<bf16, D>& qlo, float& lsum, f32x16& acc) {
   const int li = lane & 31, g = lane >> 5;
   f32x16 negs;
 #pragma unroll
@@ -848,7 +908,7 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
         if (j < 8) vop.a0[j] = (bf16)v;
         else vop.a1[j - 8] = (bf16)v;
       }
-      f32x16 sc = qk_mma<D>(kop, qop, negs);
+      f32x16 sc = qk_mma<D>(kop, qlo, qk_mma<D>(kop, qhi, negs));
       if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
       online_step(sc, negs, started, lsum, acc);
       bf16x8 b0, b1;
@@ -869,6 +929,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
   constexpr int TE = ROWS * D;  // elements per tile
   constexpr int G = NW / WN;
   __shared__ __align__(16) bf16 tiles[4 * TE];  // [buffer][K, V][TE]
+  __shared__ float kred[NW];                     // per-wave largest squared key norm of a piece
   bf16* const k0 = tiles;
   bf16* const v0 = tiles + TE;
   bf16* const k1 = tiles + 2 * TE;
@@ -905,16 +966,24 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const int h = bh % a.H;
     const int slot = (blockIdx.x - piece_of(hb, a.total, a.nwg)) * WN + ng;
 
-    const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
+    // this lane's latent query row (rows past M repeat row M - 1 and are zeroed)
+    auto qrow = [&]() {
+      const int m = mg * 32 + li;
+      return reinterpret_cast<const QT*>(a.Q) + ((size_t)(a.q_batched ? bh : h) * M + (m < M ? m : M - 1)) * D;
+    };
+    const float* qm0 = a.qmul0 ? a.qmul0 + (size_t)h * D : nullptr;
+    const float* qm1 = a.qmul1 ? a.qmul1 + (size_t)h * D : nullptr;
     const int m = mg * 32 + li;
     QKOp<bf16, D> qop;
-    load_q_row<D>(qop, Qh + (size_t)(m < M ? m : M - 1) * D, g, a.qscale, a.norm_q != 0, a.eps,
-                  a.qmul0 ? a.qmul0 + (size_t)h * D : nullptr, a.qmul1 ? a.qmul1 + (size_t)h * D : nullptr);
+    // the wave's largest query rounding error (uniform: a scalar register)
+    const float qerr2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
+        wave_max(load_q_row<D>(qop, nullptr, qrow(), g, a.qscale, a.norm_q != 0, a.eps, qm0, qm1)))));
     if (m >= M) zero_op<D>(qop);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     RowSum<D> wsum(lane);
+    float kmax2 = 0.f;  // largest squared key norm of the tiles this wave scanned
 
     const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
     const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + (size_t)bh * N * D;
@@ -930,6 +999,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * ROWS) {
       // tile t0 from buffer 0 while tile t0 + ROWS streams into buffer 1
       const int tn = t0 + ROWS;
+      kmax2 = tile_key_max<D, NW>(k0, wave, lane, kmax2);
       if (tn < n_hi) {
         dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
@@ -944,6 +1014,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       }
       // tile tn from buffer 1 while tn + ROWS streams into buffer 0
       const int tn2 = tn + ROWS;
+      kmax2 = tile_key_max<D, NW>(k1, wave, lane, kmax2);
       if (tn2 < n_hi) {
         dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
@@ -958,13 +1029,32 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         }
       }
     }
-    // unshifted partial (see fast_ok), or the careful recomputation's
+    // The piece's largest key norm (every wave scanned part of every tile).
+    // kred is free: its last readers passed the barriers of this piece's tiles.
+    kmax2 = wave_max(kmax2);
+    if (lane == 0) kred[wave] = kmax2;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) kmax2 = fmaxf(kmax2, kred[w]);
+    // unshifted partial (see fast_ok), renormalised to a power-of-two shift
+    // so that the merge never adds sums beyond the float range; or the exact
+    // recomputation when the rounded queries could move a score too far
     float ltot = wsum.total(li, acc), shift = 0.f;
-    if (fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
+    const bool inexact = qerr2 * kmax2 > kScoreErr2;
+    if (inexact || fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
+      QKOp<bf16, D> qhi, qlo;
+      load_q_row<D>(qhi, &qlo, qrow(), g, a.qscale, a.norm_q != 0, a.eps, qm0, qm1);
+      if (m >= M) { zero_op<D>(qhi); zero_op<D>(qlo); }
       float lsum;
-      shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane, qop, lsum,
-                                    acc);
+      shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane, qhi, qlo,
+                                    lsum, acc);
       ltot = pair_sum(lsum);
+    } else {
+      const int e = __builtin_amdgcn_frexp_expf(ltot);  // ltot = f 2^e, f in [1/2, 1); 0 for an empty split
+      const float sc = __builtin_amdgcn_ldexpf(1.f, -e);
+      acc = acc * sc;
+      ltot *= sc;
+      shift = (float)e;
     }
     if (m < M) {
       const size_t p = (size_t)bhl * a.pmax + slot;
@@ -1034,10 +1124,7 @@ __device__ inline MergeState merge_pair(MergeState x, MergeState y) {
   return MergeState{A, x.den * fx + y.den * fy, x.num * fx + y.num * fy};
 }
 
-#ifndef FLARE_MERGE_BATCH
-#define FLARE_MERGE_BATCH 8
-#endif
-constexpr int kMergeBatch = FLARE_MERGE_BATCH;
+constexpr int kMergeBatch = 8;  // splits loaded per lane group before any is folded
 
 // One wave per (head, latent).  Lane (pg, c) owns features 4c .. 4c + 3 and
 // folds the splits p = pg, pg + PGW, ... (PGW = 64 / (D / 4) lane groups) in
@@ -1184,7 +1271,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const int MB = MBT > 0 ? MBT : a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
   T* zt = qs + (size_t)Mp * L::QST;
-  __shared__ float zred[kThreads / 64];
+  __shared__ float zred[kThreads / 64], qred[kThreads / 64];
   const int zst = (int)L::zst(MB);
   // the wave index is uniform: kept in a scalar register, block guards derived
   // from it become scalar branches
@@ -1211,6 +1298,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
     const float* Zh = a.Z + (size_t)bh * M * D;
     float zmax = 0.f;
+    float qerr2 = 0.f;  // largest squared rounding error of a staged query row
     {
       constexpr int QE = 16 / sizeof(QT);          // elements per 16-byte chunk
       constexpr int QJ = 256 * D / QE / kThreads;  // chunks per thread at M = 256
@@ -1235,6 +1323,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
         const int c = tid + j * kThreads;
+        float ce2 = 0.f;  // squared rounding error of these QE staged values
         if (c < pq) {
           const int m = c * QE / D, d0 = c * QE % D;
           const QT* src = reinterpret_cast<const QT*>(&qv[j]);
@@ -1252,10 +1341,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           }
 #pragma unroll
           for (int i = 0; i < QE; ++i) {
-            const float q = c < nq ? to_f(src[i]) * a.qscale : 0.f;
-            qs[m * L::QST + d0 + i] = from_f<T>(q * qm[i]);
+            const float q = (c < nq ? to_f(src[i]) * a.qscale : 0.f) * qm[i];
+            const T r = from_f<T>(q);
+            qs[m * L::QST + d0 + i] = r;
+            ce2 += (q - to_f(r)) * (q - to_f(r));
           }
         }
+        // the D / QE chunks of a row sit in consecutive, aligned lanes
+#pragma unroll
+        for (int o = 1; o < D / QE; o <<= 1) ce2 += __shfl_xor(ce2, o);
+        qerr2 = fmaxf(qerr2, ce2);
       }
 #pragma unroll
       for (int j = 0; j < ZJ; ++j) {
@@ -1274,11 +1369,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     }
     // |Y accumulator| <= (sum of weights) * max |z|: a token block whose
     // weight sum stays below zlim cannot have overflowed (see fast_failed)
-    for (int o = 32; o > 0; o >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, o));
-    if (lane == 0) zred[wave] = zmax;
+    zmax = wave_max(zmax);
+    qerr2 = wave_max(qerr2);
+    if (lane == 0) { zred[wave] = zmax; qred[wave] = qerr2; }
     __syncthreads();
     zmax = fmaxf(fmaxf(zred[0], zred[1]), fmaxf(zred[2], zred[3]));
+    qerr2 = fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]));
     const float zlim = 1.329228e36f / fmaxf(zmax * 1.01f, 1.f);  // 2^120 / max|z|
+    // a token block keeps the fast loop's result only if every score it
+    // forms is within kScoreErr of the exact one: |k_n|^2 <= klim2
+    const float klim2 = qerr2 > 0.f ? kScoreErr2 / qerr2 : INFINITY;
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
@@ -1350,21 +1450,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
           consume(sb, mb, acc);
         }
         den = wsum.total(li, acc);
-        // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim
-        if (__builtin_amdgcn_ballot_w64(!fast_ok(den) || den > zlim) != 0) {
-          // careful redo of this token block: exact maximum of every latent block
+        // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim;
+        // the staged queries' rounding moves no score of a key with
+        // |k|^2 <= klim2 by more than kScoreErr
+        const bool redo = !fast_ok(den) || den > zlim || row_norm2<D>(kop) > klim2;
+        if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+          // careful redo of this token block: exact scores (the queries read
+          // again and split into bf16 hi + lo) and the exact maximum of
+          // every latent block
           f32x16 negs = zero16;
           bool started = false;
           acc = zero16;
           lsum = 0.f;
+          const float* qm = a.qmul ? a.qmul + (size_t)h * D : nullptr;
           int mc = 0;
           do {
-            QKOp<T, D> qop;
-            load_op<D>(qop, qs + (mc * 32 + li) * L::QST, g);
+            const int m = mc * 32 + li;
+            QKOp<T, D> qhi, qlo;
+            load_q_row<D>(qhi, &qlo, Qh + (size_t)(m < M ? m : M - 1) * D, g, a.qscale, false, 0.f, qm, nullptr);
+            if (m >= M) { zero_op<D>(qhi); zero_op<D>(qlo); }
             PVOp<T> zop;
             if (li < D) load_pv(zop, zt + li * zst + mc * 32, g);
             else ones_pv(zop, li, D);
-            f32x16 sc = qk_mma<D>(qop, kop, negs);
+            f32x16 sc = qk_mma<D>(qlo, kop, qk_mma<D>(qhi, kop, negs));
             if (mask_tail && mc == MB - 1) mask_rows(sc, M - mc * 32, g);
             online_step(sc, negs, started, lsum, acc);
             bf16x8 b0, b1;
@@ -1460,6 +1568,22 @@ int query_dev(Dev& d) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+// Launch a kernel and return that launch's own status.  (hipGetLastError
+// after a launch would also return, and clear, an error left pending by an
+// earlier, unrelated call on this thread.)
+template <typename... P, typename... A, size_t... I>
+int launch_impl(void (*fn)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, std::index_sequence<I...>,
+                A&&... args) {
+  std::tuple<P...> vals(std::forward<A>(args)...);
+  void* argv[] = {(void*)&std::get<I>(vals)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, argv, lds, st) == hipSuccess ? FLARE_OK
+                                                                                                      : FLARE_ERR_HIP;
+}
+template <typename... P, typename... A>
+int launch(void (*fn)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A&&... args) {
+  return launch_impl(fn, grid, block, lds, st, std::index_sequence_for<P...>{}, std::forward<A>(args)...);
+}
+
 // Latent blocks of 32: padded to 1, 2, 4 or 8 so that waves split them evenly.
 inline int latent_blocks(int M) {
   int mb = (int)cdiv(M, 32);
@@ -1475,14 +1599,8 @@ struct EncPlan {
 
 // Resident waves per compute unit the encode grid is sized for, and the
 // decode's workgroups per compute unit.
-#ifndef FLARE_ENC_WAVES_PER_CU
-#define FLARE_ENC_WAVES_PER_CU 16
-#endif
-#ifndef FLARE_DEC_WG_PER_CU
-#define FLARE_DEC_WG_PER_CU 4
-#endif
-constexpr int kEncWavesPerCu = FLARE_ENC_WAVES_PER_CU;
-constexpr int kDecWgPerCu = FLARE_DEC_WG_PER_CU;
+constexpr int kEncWavesPerCu = 16;
+constexpr int kDecWgPerCu = 4;
 
 // bf16: one 32-latent block per wave, max(4, blocks) waves per workgroup.
 // f32: up to two latent blocks per wave, 4 waves per workgroup.
@@ -1514,23 +1632,6 @@ EncPlan plan_encode(const Dev& dev, int nbh, int N, int M, int dtype) {
   return p;
 }
 
-// Heads per fused encode -> merge -> decode round.  With a nonzero budget a
-// group's keys and values are meant to stay resident in the last-level cache
-// until its decode re-reads the keys; 0 runs all heads in one round.
-#ifndef FLARE_HEAD_GROUP_MB
-#define FLARE_HEAD_GROUP_MB 0
-#endif
-constexpr size_t kHeadGroupBytes = (size_t)FLARE_HEAD_GROUP_MB << 20;
-
-int heads_per_group(int BH, int N, int D, int dtype) {
-  const size_t per = (size_t)N * D * (dtype == FLARE_BF16 ? 2 : 4) * 2;
-  if (kHeadGroupBytes == 0 || per == 0) return BH;
-  size_t g = kHeadGroupBytes / per;
-  if (g < 1) g = 1;
-  if (g > (size_t)BH) g = BH;
-  return (int)g;
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int check_common(int B, int H, int N, int M, int D, int dtype, int q_batched) {
@@ -1546,8 +1647,7 @@ int check_common(int B, int H, int N, int M, int D, int dtype, int q_batched) {
 
 template <typename QT, int D, int NW, int WN, bool NK>
 int launch_encode_dma(const EncArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((encode_dma_kernel<QT, D, NW, WN, NK>), dim3(a.nwg), dim3(NW * 64), 0, st, a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  return launch(encode_dma_kernel<QT, D, NW, WN, NK>, dim3(a.nwg), dim3(NW * 64), 0, st, a);
 }
 
 template <typename QT, int D, bool NK>
@@ -1581,8 +1681,7 @@ struct Norms {
 template <int D, int MBW>
 int launch_encode_f32(const EncArgs& a, hipStream_t st) {
   const size_t lds = EncLds<float, D>::bytes;
-  hipLaunchKernelGGL((encode_kernel<float, float, D, MBW>), dim3(a.nwg), dim3(kThreads), lds, st, a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  return launch(encode_kernel<float, float, D, MBW>, dim3(a.nwg), dim3(kThreads), lds, st, a);
 }
 
 // qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
@@ -1617,9 +1716,8 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   a.total = p.total;
   a.N = N; a.M = M; a.D = D; a.H = H; a.WN = p.WN; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0; a.nbh = nbh;
   const dim3 grid((unsigned)cdiv((long long)nbh * M, kThreads / 64));
-  if (qftype == FLARE_BF16) hipLaunchKernelGGL((merge_kernel<bf16>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((merge_kernel<float>), grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  if (qftype == FLARE_BF16) return launch(merge_kernel<bf16>, grid, dim3(kThreads), 0, st, a);
+  return launch(merge_kernel<float>, grid, dim3(kThreads), 0, st, a);
 }
 
 template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
@@ -1629,8 +1727,7 @@ int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  hipLaunchKernelGGL((decode_kernel<T, QT, D, TAIL, NK, ST, MBT>), dim3(a.nwg), dim3(kThreads), lds, st, a);
-  return hipGetLastError() == hipSuccess ? FLARE_OK : FLARE_ERR_HIP;
+  return launch(decode_kernel<T, QT, D, TAIL, NK, ST, MBT>, dim3(a.nwg), dim3(kThreads), lds, st, a);
 }
 
 // bf16 decode without a latent tail: 2, 4 or 8 latent blocks (M = 64, 128,
@@ -1695,8 +1792,8 @@ int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const
 
 float pick_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf((float)D); }
 
-// Workspace carve-up: partials of the largest head group, then float32
-// buffers the call needs internally.
+// Workspace carve-up: the encode's split partials, then float32 buffers the
+// call needs internally.
 struct WsLayout {
   size_t part_acc = 0, part_al = 0, z = 0, l = 0, q = 0, total = 0;
 };
@@ -1704,23 +1801,15 @@ struct WsLayout {
 WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, int dtype, bool need_z, bool need_q) {
   WsLayout w;
   const int BH = B * H;
-  const int grp = (op == FLARE_OP_ENCODE) ? BH : heads_per_group(BH, N, D, dtype);
   size_t off = 0;
   if (op != FLARE_OP_DECODE && N > 0) {
-    // every head-group size that is launched: full groups, the remainder
-    // group, and all heads at once for the FLARE++ synthesis encode
-    const int groups[3] = {grp, BH % grp ? BH % grp : grp, op == FLARE_OP_PP_FORWARD ? BH : grp};
-    size_t max_acc = 0, max_al = 0;
-    for (int gi = 0; gi < 3; ++gi) {
-      const EncPlan p = plan_encode(dev, groups[gi], N, M, dtype);
-      const size_t acc = align256((size_t)groups[gi] * p.pmax * M * D * sizeof(float));
-      const size_t al = align256((size_t)groups[gi] * p.pmax * M * sizeof(float2));
-      if (acc > max_acc) max_acc = acc;
-      if (al > max_al) max_al = al;
-    }
+    // the split partials of one encode over all heads
+    const EncPlan p = plan_encode(dev, BH, N, M, dtype);
+    const size_t acc = align256((size_t)BH * p.pmax * M * D * sizeof(float));
+    const size_t al = align256((size_t)BH * p.pmax * M * sizeof(float2));
     w.part_acc = 0;
-    w.part_al = max_acc;
-    off = max_acc + max_al;
+    w.part_al = acc;
+    off = acc + al;
   }
   if (need_z) { w.z = off; off += align256((size_t)BH * M * D * sizeof(float)); w.l = off; off += align256((size_t)BH * M * sizeof(float)); }
   if (need_q) { w.q = off; off += align256((size_t)BH * M * D * sizeof(float)); }
@@ -1806,30 +1895,23 @@ int flare_decode(const void* Q, int q_batched, const void* K, const float* Z, vo
 }
 
 // Shared by flare_forward and the routing half of flare_pp_forward: encode ->
-// merge -> decode per head group.  Q has element type qtype; nm carries the
+// merge -> decode over all heads.  Q has element type qtype; nm carries the
 // routing keys' normalisation (N_0 rows, and their scale moved onto Q).
 static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const void* V, void* Y,
                    float* Z, float* L, int B, int H, int N, int M, int D, int dtype, float qs, char* ws,
                    const WsLayout& w, const Norms& nm, hipStream_t st) {
   const int BH = B * H;
-  const int grp = heads_per_group(BH, N, D, dtype);
   float* pacc = (float*)(ws + w.part_acc);
   float2* pal = (float2*)(ws + w.part_al);
+  const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   int rc;
-  for (int bh0 = 0; bh0 < BH; bh0 += grp) {
-    const int nbh = BH - bh0 < grp ? BH - bh0 : grp;
-    const EncPlan p = plan_encode(dev, nbh, N, M, dtype);
-    if (N > 0) {
-      rc = launch_encode(Q, qtype, q_batched, K, V, bh0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st);
-      if (rc) return rc;
-    }
-    rc = launch_merge(p, pacc, pal, bh0, nbh, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr,
-                      0.f, st);
-    if (rc) return rc;
-    rc = launch_decode(dev, Q, qtype, q_batched, K, Z, Y, bh0, nbh, H, N, M, D, dtype, qs, nm, st);
+  if (N > 0) {
+    rc = launch_encode(Q, qtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st);
     if (rc) return rc;
   }
-  return FLARE_OK;
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+  if (rc) return rc;
+  return launch_decode(dev, Q, qtype, q_batched, K, Z, Y, 0, BH, H, N, M, D, dtype, qs, nm, st);
 }
 
 int flare_forward(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out, float* L_out,

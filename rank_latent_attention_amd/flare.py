@@ -108,13 +108,48 @@ def _dims(Q: torch.Tensor, K: torch.Tensor) -> Tuple[int, int, int, int, int, in
 
 
 def _same(ref: torch.Tensor, *ts):
-    for t in ts:
+    """Every given tensor is a contiguous GPU tensor on ref's device (the
+    kernels take raw device pointers: a host or foreign-device pointer would
+    be dereferenced on the GPU)."""
+    for t in (ref,) + ts:
         if t is None:
             continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"expected a torch.Tensor, got {type(t).__name__}")
         if t.device != ref.device:
             raise ValueError("all tensors must be on the same device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {ref.device}")
+
+
+def _out(name: str, t: Optional[torch.Tensor], shape, dtype: torch.dtype):
+    """A caller-supplied output must have exactly the shape and dtype the
+    kernels write (they get no sizes and would write past a smaller one)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _ws_bytes(ws: Optional[torch.Tensor]) -> int:
+    """Byte size of a caller-supplied workspace (any dtype, contiguous)."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"ws must be a torch.Tensor, got {type(ws).__name__}")
+    return ws.numel() * ws.element_size()
+
+
+def _pp_outs(K: torch.Tensor, M: int, Y, Q_out, Z, L):
+    B, H, N, D = K.shape
+    _out("Y", Y, K.shape, K.dtype)
+    _out("Q_out", Q_out, (B, H, M, D), torch.float32)
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
 
 
 def workspace_size(op: int, B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
@@ -132,12 +167,14 @@ def flare_encode(Q, K, V, scale: float = 0.0, Z=None, L=None, ws=None):
     dt = _dtype_code(K)
     if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
         raise ValueError("Q, K, V must share dtype and K, V shape")
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
+    _same(K, Q, V, Z, L, ws)
     Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device) if Z is None else Z
     L = torch.empty((B, H, M), dtype=torch.float32, device=K.device) if L is None else L
-    _same(K, Q, V, Z, L)
     ws = workspace(OP_ENCODE, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_encode(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale),
-                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(K.device))
+                             _ptr(ws), _ws_bytes(ws), _stream(K.device))
     _check("flare_encode", rc)
     return Z, L
 
@@ -148,8 +185,9 @@ def flare_decode(Q, K, Z, scale: float = 0.0, Y=None):
     dt = _dtype_code(K)
     if Q.dtype != K.dtype or Z.dtype != torch.float32 or tuple(Z.shape) != (B, H, M, D):
         raise ValueError("Q must match K's dtype and Z must be float32 [B,H,M,D]")
-    Y = torch.empty_like(K) if Y is None else Y
+    _out("Y", Y, K.shape, K.dtype)
     _same(K, Q, Z, Y)
+    Y = torch.empty_like(K) if Y is None else Y
     rc = load().flare_decode(_ptr(Q), qb, _ptr(K), _ptr(Z), _ptr(Y), B, H, N, M, D, dt, float(scale), None, 0,
                              _stream(K.device))
     _check("flare_decode", rc)
@@ -166,11 +204,14 @@ def flare_forward(Q, K, V, scale: float = 0.0, Y=None, Z=None, L=None, ws=None):
     dt = _dtype_code(K)
     if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
         raise ValueError("Q, K, V must share dtype and K, V shape")
+    _out("Y", Y, K.shape, K.dtype)
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
+    _same(K, Q, V, Y, Z, L, ws)
     Y = torch.empty_like(K) if Y is None else Y
-    _same(K, Q, V, Y, Z, L)
     ws = workspace(OP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_forward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Y), _ptr(Z), _ptr(L), B, H, N, M, D, dt,
-                              float(scale), _ptr(ws), 0 if ws is None else ws.numel(), _stream(K.device))
+                              float(scale), _ptr(ws), _ws_bytes(ws), _stream(K.device))
     _check("flare_forward", rc)
     return Y, Z, L
 
@@ -191,12 +232,13 @@ def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0, Y=None, Q_o
         raise ValueError("Ks, Vs, K, V must all be [B,H,N,D]")
     if gate.dtype != torch.float32 or gate.numel() != H:
         raise ValueError("gate must be float32 [H]")
+    _pp_outs(K, M, Y, Q_out, Z, L)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L, ws)
     Y = torch.empty_like(K) if Y is None else Y
-    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L)
     ws = workspace(OP_PP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_pp_forward(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Y),
                                  _ptr(Q_out), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(K.device))
+                                 _ws_bytes(ws), _stream(K.device))
     _check("flare_pp_forward", rc)
     return Y, Q_out, Z, L
 
@@ -223,18 +265,22 @@ def flare_pp_forward_norm(Qs, Ks, Vs, Qf, gate, K, V, norm_flags: int, alpha_qs=
     for a in (alpha_qs, alpha_ks, alpha_k):
         if a is not None and (a.dtype != torch.float32 or tuple(a.shape) != (H, D)):
             raise ValueError("alpha arrays must be float32 [H, D]")
+    _pp_outs(K, M, Y, Q_out, Z, L)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L, alpha_qs, alpha_ks, alpha_k, ws)
     Y = torch.empty_like(K) if Y is None else Y
-    _same(K, Qs, Ks, Vs, Qf, gate, V, Y, Q_out, Z, L, alpha_qs, alpha_ks, alpha_k)
     ws = workspace(OP_PP_FORWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_pp_forward_norm(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Y),
                                       _ptr(Q_out), _ptr(Z), _ptr(L), B, H, N, M, D, dt, float(scale), int(norm_flags),
                                       _ptr(alpha_qs), _ptr(alpha_ks), _ptr(alpha_k), float(eps), _ptr(ws),
-                                      0 if ws is None else ws.numel(), _stream(K.device))
+                                      _ws_bytes(ws), _stream(K.device))
     _check("flare_pp_forward_norm", rc)
     return Y, Q_out, Z, L
 
 
 def _grads(Q, K, dQ, dK, dV):
+    _out("dQ", dQ, Q.shape, torch.float32)
+    _out("dK", dK, K.shape, K.dtype)
+    _out("dV", dV, K.shape, K.dtype)
     dQ = torch.empty(Q.shape, dtype=torch.float32, device=K.device) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
     dV = torch.empty_like(K) if dV is None else dV
@@ -253,12 +299,13 @@ def flare_backward(Q, K, V, Z, L, dY, scale: float = 0.0, dQ=None, dK=None, dV=N
     if Z.dtype != torch.float32 or tuple(Z.shape) != (B, H, M, D) or L.dtype != torch.float32 or \
             tuple(L.shape) != (B, H, M):
         raise ValueError("Z must be float32 [B,H,M,D] and L float32 [B,H,M]")
+    _out("dZ", dZ, (B, H, M, D), torch.float32)
+    _same(K, Q, V, Z, L, dY, dQ, dK, dV, dZ, ws)
     dQ, dK, dV = _grads(Q, K, dQ, dK, dV)
-    _same(K, Q, V, Z, L, dY, dQ, dK, dV, dZ)
     ws = workspace(OP_BACKWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_backward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQ), _ptr(dK),
                                _ptr(dV), _ptr(dZ), B, H, N, M, D, dt, float(scale), _ptr(ws),
-                               0 if ws is None else ws.numel(), _stream(K.device))
+                               _ws_bytes(ws), _stream(K.device))
     _check("flare_backward", rc)
     return dQ, dK, dV, dZ
 
@@ -274,12 +321,12 @@ def flare_encode_backward(Q, K, V, Z, L, dZ, dL=None, scale: float = 0.0, dQ=Non
     for t, shp in ((Z, (B, H, M, D)), (L, (B, H, M)), (dZ, (B, H, M, D)), (dL, (B, H, M))):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shp):
             raise ValueError("Z, dZ must be float32 [B,H,M,D]; L, dL float32 [B,H,M]")
+    _same(K, Q, V, Z, L, dZ, dL, dQ, dK, dV, ws)
     dQ, dK, dV = _grads(Q, K, dQ, dK, dV)
-    _same(K, Q, V, Z, L, dZ, dL, dQ, dK, dV)
     ws = workspace(OP_ENCODE_BACKWARD, B, H, N, M, D, dt, K.device) if ws is None else ws
     rc = load().flare_encode_backward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Z), _ptr(L), _ptr(dZ), _ptr(dL),
                                       _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, M, D, dt, float(scale), _ptr(ws),
-                                      0 if ws is None else ws.numel(), _stream(K.device))
+                                      _ws_bytes(ws), _stream(K.device))
     _check("flare_encode_backward", rc)
     return dQ, dK, dV
 
@@ -314,12 +361,13 @@ def flare_pp_backward(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, scale: float = 0.
     dgate = torch.empty((H,), dtype=torch.float32, device=dev)
     dKs, dK, dV = torch.empty_like(K), torch.empty_like(K), torch.empty_like(K)
     dVs = None if alias else torch.empty_like(K)
-    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out)
+    _out("dQ_out", dQ_out, (B, H, M, D), torch.float32)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out, ws)
     ws = workspace(OP_PP_BACKWARD, B, H, N, M, D, dt, dev) if ws is None else ws
     rc = load().flare_pp_backward(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Q),
                                   _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQs), _ptr(dKs), _ptr(dVs), _ptr(dQf),
                                   _ptr(dgate), _ptr(dQ_out), _ptr(dK), _ptr(dV), B, H, N, M, D, dt, float(scale),
-                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+                                  _ptr(ws), _ws_bytes(ws), _stream(dev))
     _check("flare_pp_backward", rc)
     return dQs, dKs, dVs, dQf, dgate, dK, dV, dQ_out
 
@@ -363,13 +411,14 @@ def flare_pp_backward_norm(Qs, Ks, Vs, Qf, gate, K, V, Q, Z, L, dY, norm_flags: 
     def da(a, bit):
         return torch.empty((H, D), dtype=torch.float32, device=dev) if a is not None and norm_flags & bit else None
     da_qs, da_ks, da_k = da(alpha_qs, NORM_QS), da(alpha_ks, NORM_KS), da(alpha_k, NORM_K)
-    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out, alpha_qs, alpha_ks, alpha_k)
+    _out("dQ_out", dQ_out, (B, H, M, D), torch.float32)
+    _same(K, Qs, Ks, Vs, Qf, gate, V, Q, Z, L, dY, dQ_out, alpha_qs, alpha_ks, alpha_k, ws)
     ws = workspace(OP_PP_BACKWARD_NORM, B, H, N, M, D, dt, dev) if ws is None else ws
     rc = load().flare_pp_backward_norm(_ptr(Qs), _ptr(Ks), _ptr(Vs), _ptr(Qf), _ptr(gate), _ptr(K), _ptr(V), _ptr(Q),
                                        _ptr(Z), _ptr(L), _ptr(dY), _ptr(dQs), _ptr(dKs), _ptr(dVs), _ptr(dQf),
                                        _ptr(dgate), _ptr(dQ_out), _ptr(dK), _ptr(dV), _ptr(da_qs), _ptr(da_ks),
                                        _ptr(da_k), B, H, N, M, D, dt, float(scale), int(norm_flags), _ptr(alpha_qs),
                                        _ptr(alpha_ks), _ptr(alpha_k), float(eps), _ptr(ws),
-                                       0 if ws is None else ws.numel(), _stream(dev))
+                                       _ws_bytes(ws), _stream(dev))
     _check("flare_pp_backward_norm", rc)
     return dQs, dKs, dVs, dQf, dgate, dK, dV, da_qs, da_ks, da_k, dQ_out

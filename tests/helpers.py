@@ -16,6 +16,30 @@ def rel_l2(got, ref) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+#: per-row bar, as a multiple of the rel-L2 bar: the largest error of a single row
+#: (a token of Y, a latent of Z or Q), relative to that row's norm floored at the
+#: root-mean-square row norm of the reference.  A row that is wholly wrong has a
+#: row error of order one and fails it however many rows are right.
+ROW_FACTOR = 5.0
+
+
+def row_err(got, ref) -> float:
+    """Largest relative error of one row (the last axis) of got against ref."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in the GPU result"
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    if r.size == 0:
+        return 0.0
+    rn = np.linalg.norm(r, axis=1)
+    floor = np.sqrt(np.mean(rn ** 2))
+    if floor == 0:
+        return float(np.max(np.linalg.norm(g - r, axis=1)))
+    return float(np.max(np.linalg.norm(g - r, axis=1) / np.maximum(rn, floor)))
+
+
 def lse_err(got, ref) -> float:
     """Error of a log-normaliser L = log l, measured on the normaliser l = e^L it encodes.
 

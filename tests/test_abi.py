@@ -154,3 +154,75 @@ def test_pp_backward_norm_workspace_holds_the_normalised_inputs(lib):
     # no device here: the size query fails closed (0) rather than guessing
     assert lib.flare_workspace_size(7, 1, 1, 8, 8, 16, 0) == 0   # bf16 only
     assert lib.flare_workspace_size(8, 1, 1, 8, 8, 16, 1) == 0   # unknown op
+
+
+# --------------------------------------------------------------------------
+# The Python binding validates caller-supplied outputs and the device before
+# any library call (CPU tensors here: the checks fire before anything runs).
+# --------------------------------------------------------------------------
+
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("bad", ["Z_shape", "Z_dtype", "L_shape", "Y_shape", "Y_dtype", "ws_type"])
+def test_binding_rejects_wrong_outputs(bad):
+    import torch
+    from rank_latent_attention_amd import flare
+    B, H, N, M, D = 1, 2, 100, 32, 16
+    Q, K, V = _cpu((H, M, D)), _cpu((B, H, N, D)), _cpu((B, H, N, D))
+    kw = {"Z": torch.zeros((B, H, M, D)), "L": torch.zeros((B, H, M)), "Y": _cpu((B, H, N, D))}
+    if bad == "Z_shape":
+        kw["Z"] = torch.zeros((B, H, M - 1, D))
+    elif bad == "Z_dtype":
+        kw["Z"] = _cpu((B, H, M, D))
+    elif bad == "L_shape":
+        kw["L"] = torch.zeros((B, H, M, 1))
+    elif bad == "Y_shape":
+        kw["Y"] = _cpu((B, H, N - 1, D))
+    elif bad == "Y_dtype":
+        kw["Y"] = torch.zeros((B, H, N, D))
+    with pytest.raises((ValueError, TypeError)):
+        if bad == "ws_type":
+            flare.flare_forward(Q, K, V, ws=bytearray(16), **kw)
+        else:
+            flare.flare_forward(Q, K, V, **kw)
+
+
+def test_binding_rejects_wrong_outputs_of_every_entry_point():
+    import torch
+    from rank_latent_attention_amd import flare
+    B, H, N, M, D = 2, 2, 64, 16, 16
+    Q, K, V = _cpu((H, M, D)), _cpu((B, H, N, D)), _cpu((B, H, N, D))
+    gate = torch.zeros(H)
+    small = torch.zeros((B, H, M - 1, D))
+    with pytest.raises(ValueError):
+        flare.flare_encode(Q, K, V, Z=small)
+    with pytest.raises(ValueError):
+        flare.flare_decode(Q, K, torch.zeros((B, H, M, D)), Y=_cpu((B, H, N, D // 2)))
+    with pytest.raises(ValueError):
+        flare.flare_pp_forward(Q, K, K, Q, gate, K, V, Q_out=small)
+    with pytest.raises(ValueError):
+        flare.flare_pp_forward_norm(Q, K, K, Q, gate, K, V, flare.NORM_FLAREPP, Z=small)
+    Z, L = torch.zeros((B, H, M, D)), torch.zeros((B, H, M))
+    with pytest.raises(ValueError):
+        flare.flare_backward(Q, K, V, Z, L, K, dK=_cpu((B, H, N - 1, D)))
+    with pytest.raises(ValueError):
+        flare.flare_backward(Q, K, V, Z, L, K, dQ=_cpu((H, M, D)))
+    with pytest.raises(ValueError):
+        flare.flare_encode_backward(Q, K, V, Z, L, Z, dV=torch.zeros((B, H, N, D)))
+    Qb = torch.zeros((B, H, M, D))
+    with pytest.raises(ValueError):
+        flare.flare_pp_backward(Q, K, K, Q, gate, K, V, Qb, Z, L, K, dQ_out=small)
+
+
+def test_binding_rejects_host_tensors():
+    """Well-formed arguments that live in host memory are refused: the
+    kernels would dereference their addresses on the GPU."""
+    from rank_latent_attention_amd import flare
+    Q, K, V = _cpu((2, 32, 16)), _cpu((1, 2, 100, 16)), _cpu((1, 2, 100, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        flare.flare_forward(Q, K, V)
+    with pytest.raises(ValueError, match="GPU"):
+        flare.flare_decode(Q, K, _cpu((1, 2, 32, 16)).float())
