@@ -115,6 +115,23 @@ int flare_forward(const void* Q, int q_batched, const void* K, const void* V, vo
                   float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* flare_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments as flare_forward minus ws / ws_bytes.
+ * The scratch it needs (the encode's split partials, and Z / L when Z_out /
+ * L_out are NULL) lives in a file-scope device array of
+ * FLARE_NOALLOC_SCRATCH_BYTES, one per GPU, held from the library's load
+ * until the process ends; this call allocates nothing.  A problem whose
+ * scratch, flare_workspace_size(FLARE_OP_FORWARD, ...), exceeds that size
+ * returns FLARE_ERR_WORKSPACE before anything is enqueued (the million-token
+ * shape B1 H8 N2^20 M256 D32 needs about 18 MB).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs clearing between calls. */
+#define FLARE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int flare_forward_noalloc(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out,
+                          float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* stream);
+
 /* FLARE++ routing forward (Sec. 3.2; App. A.1, A.4, A.6):
  *   Qd[b,h] = SDPA(Qs[h], Ks[b,h], Vs[b,h])            (synthesis encode)
  *   Q[b,h]  = Qf[h] + gate[h] * Qd[b,h]                 (float32 blend)

@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -1822,6 +1823,35 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
 #include "backward.h"
 
 // ----------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: a file-scope device array, one
+// copy per GPU, resolved to a device address once per device.  Host code
+// never uses the array's name as an address (on the host it is a stand-in,
+// not device memory); kernels get the resolved pointer.
+// ----------------------------------------------------------------------------
+constexpr size_t kScratchBytes = FLARE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLARE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FLARE_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return FLARE_OK;
+}
+}  // namespace
+
+// ----------------------------------------------------------------------------
 // C ABI
 // ----------------------------------------------------------------------------
 extern "C" {
@@ -1914,9 +1944,12 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
   return launch_decode(dev, Q, qtype, q_batched, K, Z, Y, 0, BH, H, N, M, D, dtype, qs, nm, st);
 }
 
-int flare_forward(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out, float* L_out,
-                  int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
-                  void* stream) {
+// flare_forward with the workspace at ws (ws_bytes long), or, when ws_bytes
+// is 0 and scratch is set, in the file-scope scratch array of the current
+// device (checked against its size before anything is enqueued).
+static int forward_impl(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out,
+                        float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* ws,
+                        size_t ws_bytes, bool scratch, void* stream) {
   int rc = check_common(B, H, N, M, D, dtype, q_batched);
   if (rc) return rc;
   if (!Q || (N > 0 && (!K || !V || !Y))) return FLARE_ERR_INVALID_ARG;
@@ -1927,6 +1960,11 @@ int flare_forward(const void* Q, int q_batched, const void* K, const void* V, vo
   if ((rc = query_dev(dev))) return rc;
   if (decode_lds(dtype, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const WsLayout w = ws_layout(dev, FLARE_OP_FORWARD, B, H, N, M, D, dtype, true, false);
+  if (scratch) {
+    if (w.total > kScratchBytes) return FLARE_ERR_WORKSPACE;
+    if ((rc = scratch_address(&ws))) return rc;
+    ws_bytes = kScratchBytes;
+  }
   if (ws_bytes < w.total || (w.total > 0 && !ws)) return FLARE_ERR_WORKSPACE;
   char* wsc = (char*)ws;
   float* Z = Z_out ? Z_out : (float*)(wsc + w.z);
@@ -1934,6 +1972,18 @@ int flare_forward(const void* Q, int q_batched, const void* K, const void* V, vo
   const float qs = pick_scale(scale, D) * kLog2e;
   return routing(dev, Q, dtype, q_batched, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, Norms{},
                  (hipStream_t)stream);
+}
+
+int flare_forward(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out, float* L_out,
+                  int B, int H, int N, int M, int D, int dtype, float scale, void* ws, size_t ws_bytes,
+                  void* stream) {
+  return forward_impl(Q, q_batched, K, V, Y, Z_out, L_out, B, H, N, M, D, dtype, scale, ws, ws_bytes, false,
+                      stream);
+}
+
+int flare_forward_noalloc(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z_out,
+                          float* L_out, int B, int H, int N, int M, int D, int dtype, float scale, void* stream) {
+  return forward_impl(Q, q_batched, K, V, Y, Z_out, L_out, B, H, N, M, D, dtype, scale, nullptr, 0, true, stream);
 }
 
 int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,

@@ -34,7 +34,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
            "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_pp_backward",
-           "flare_pp_backward_norm", "flare_status_string")
+           "flare_pp_backward_norm", "flare_status_string", "flare_forward_noalloc")
 
 _lib = None
 
@@ -59,6 +59,7 @@ def load(path: str = LIB_PATH):
     L.flare_encode.argtypes = [vp, i, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_decode.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_forward_noalloc.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.flare_pp_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_forward_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, vp, f,
                                         vp, sz, vp]
@@ -66,7 +67,8 @@ def load(path: str = LIB_PATH):
     L.flare_encode_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_backward.argtypes = [vp] * 19 + [i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_backward_norm.argtypes = [vp] * 22 + [i, i, i, i, i, i, f, i, vp, vp, vp, f, vp, sz, vp]
-    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_pp_forward, L.flare_pp_forward_norm,
+    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_forward_noalloc, L.flare_pp_forward,
+               L.flare_pp_forward_norm,
                L.flare_backward, L.flare_encode_backward, L.flare_pp_backward, L.flare_pp_backward_norm):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
@@ -213,6 +215,26 @@ def flare_forward(Q, K, V, scale: float = 0.0, Y=None, Z=None, L=None, ws=None):
     rc = load().flare_forward(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Y), _ptr(Z), _ptr(L), B, H, N, M, D, dt,
                               float(scale), _ptr(ws), _ws_bytes(ws), _stream(K.device))
     _check("flare_forward", rc)
+    return Y, Z, L
+
+
+def flare_forward_noalloc(Q, K, V, scale: float = 0.0, Y=None, Z=None, L=None):
+    """flare_forward with the library's per-GPU scratch array instead of a
+    workspace (flare_forward_noalloc in include/flare.h): the C call allocates
+    nothing.  Pass Y (and Z, L) to keep this wrapper allocation-free too.
+    Calls that overlap on one GPU race.  Returns (Y, Z, L)."""
+    B, H, N, M, D, qb = _dims(Q, K)
+    dt = _dtype_code(K)
+    if Q.dtype != K.dtype or V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("Q, K, V must share dtype and K, V shape")
+    _out("Y", Y, K.shape, K.dtype)
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
+    _same(K, Q, V, Y, Z, L)
+    Y = torch.empty_like(K) if Y is None else Y
+    rc = load().flare_forward_noalloc(_ptr(Q), qb, _ptr(K), _ptr(V), _ptr(Y), _ptr(Z), _ptr(L), B, H, N, M, D, dt,
+                                      float(scale), _stream(K.device))
+    _check("flare_forward_noalloc", rc)
     return Y, Z, L
 
 

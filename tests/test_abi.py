@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
                                            "flare_pp_forward", "flare_pp_forward_norm", "flare_backward",
                                            "flare_encode_backward", "flare_pp_backward", "flare_pp_backward_norm",
-                                           "flare_status_string"])
+                                           "flare_status_string", "flare_forward_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
