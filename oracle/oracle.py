@@ -24,7 +24,7 @@ _lib = None
 __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_queries",
            "flare_pp_forward", "materialize", "rms_norm", "flare_pp_forward_normed", "encode_backward",
            "decode_backward", "flare_backward", "flare_pp_backward", "rms_norm_backward",
-           "flare_pp_backward_normed"]
+           "flare_pp_backward_normed", "project", "flare_forward_proj", "flare_pp_forward_proj"]
 
 
 def build(force: bool = True) -> str:
@@ -210,6 +210,35 @@ def flare_pp_forward_normed(Qs, Ks, Vs, Qf, gate, K, V, *, norm_qs=False, norm_k
     Qf_n = rms_norm(Qf, None, eps) if norm_qf else Qf
     K_n = rms_norm(K, alpha_k, eps) if norm_k else K
     return flare_pp_forward(Qs_n, Ks_n, Vs_n, Qf_n, gate, K_n, V, scale)
+
+
+def project(X, W) -> np.ndarray:
+    """Per-head input projection of FLARE (FLARE++ paper, Sec. 3.1: K_h = X W_K,h
+    and V_h = X W_V,h), in fp64.  X [B, N, C] (the block's input tokens,
+    shared by every head), W [H, C, D]; returns [B, H, N, D] with
+    out[b, h, n, :] = X[b, n, :] @ W[h]."""
+    X, W = _f64(X), _f64(W)
+    if X.ndim != 3 or W.ndim != 3 or W.shape[1] != X.shape[2]:
+        raise ValueError(f"X must be [B,N,C] and W [H,C,D], got {X.shape}, {W.shape}")
+    return np.ascontiguousarray(np.matmul(X[:, None], W[None]))
+
+
+def flare_forward_proj(X, WK, WV, Q, scale: float = 0.0):
+    """FLARE routing forward from the block input: K = X W_K, V = X W_V per head
+    (Sec. 3.1), then the FLARE pair.  Returns (Y, Z, L)."""
+    return flare_forward(Q, project(X, WK), project(X, WV), scale)
+
+
+def flare_pp_forward_proj(X, WKs, WK, WV, Qs, Qf, gate, *, norm_qs=False, norm_ks=False, norm_qf=False,
+                          norm_k=False, alpha_qs=None, alpha_k=None, eps: float = 1e-6, scale: float = 0.0):
+    """FLARE++ routing forward from the block input: the synthesis keys
+    K~ = X W~_K (also the synthesis values, App. A.6), the routing keys
+    K = X W_K and values V = X W_V per head, then the per-head norms of the
+    flags and the FLARE++ forward (flare_pp_forward_normed).  Returns (Y, Q, Z, L)."""
+    Ks = project(X, WKs)
+    return flare_pp_forward_normed(Qs, Ks, Ks, Qf, gate, project(X, WK), project(X, WV), norm_qs=norm_qs,
+                                   norm_ks=norm_ks, norm_qf=norm_qf, norm_k=norm_k, alpha_qs=alpha_qs,
+                                   alpha_k=alpha_k, eps=eps, scale=scale)
 
 
 def materialize(Q, K, scale: float = 0.0):

@@ -112,6 +112,12 @@ class Workload:
     alpha_qs: Optional[np.ndarray] = None
     alpha_ks: Optional[np.ndarray] = None
     alpha_k: Optional[np.ndarray] = None
+    # block input and per-head projections (the fused-projection forwards):
+    # X [B,N,C]; WK, WV, WKs [H,C,D]; K, V (and Ks) are then X @ W per head
+    X: Optional[np.ndarray] = None
+    WK: Optional[np.ndarray] = None
+    WV: Optional[np.ndarray] = None
+    WKs: Optional[np.ndarray] = None
 
     @property
     def shared_vs(self) -> bool:
@@ -370,6 +376,68 @@ def config5(pp=False, seed=5, N=1 << 20, H=8):
     return Workload(name, B, H, N, M, D, "bf16", Q=to_dtype(Qf, "bf16"), K=K, V=to_dtype(V, "bf16"),
                     pp=True, Qs=to_dtype(Qs, "bf16"), Ks=Ks, Vs=Ks, Qf=to_dtype(Qf, "bf16"), gate=g,
                     recipe="as c5 plus Ks=N0(RFF Wks/sqrt 128)=Vs, K=N0(K), Qs,Qf=N0(N(0,1/D)), g=sigmoid(0.25)")
+
+
+def _per_head(W: np.ndarray, H: int, D: int) -> np.ndarray:
+    """[C, H*D] / sqrt(C) -> [H, C, D]: the per-head projection matrices of _heads."""
+    C = W.shape[0]
+    return np.ascontiguousarray((W / math.sqrt(C)).reshape(C, H, D).transpose(1, 0, 2))
+
+
+def make_gaussian_proj(B, H, N, M, D, C=128, seed=0, pp=False, name="gaussian_proj"):
+    """Fused-projection inputs, bf16: X ~ N(0,1) [B,N,C], W_K, W_V (and for
+    FLARE++ W~_K) ~ N(0, 1/C) [H,C,D], Q ~ N(0, 1/D); FLARE++ adds raw seeds
+    Qs and fixed queries Qf, channel scales as make_gaussian_pp_raw, gate
+    sigmoid(0.25) and the norms of Table 2 (flags 15)."""
+    X = to_dtype(_gauss(seed, "x", (B, N, C)), "bf16")
+    WK = to_dtype(_gauss(seed, "wk", (H, C, D), 1.0 / math.sqrt(C)), "bf16")
+    WV = to_dtype(_gauss(seed, "wv", (H, C, D), 1.0 / math.sqrt(C)), "bf16")
+    Q = to_dtype(_gauss(seed, "q", (H, M, D), 1.0 / math.sqrt(D)), "bf16")
+    w = Workload(name, B, H, N, M, D, "bf16", Q=Q, K=None, V=None, X=X, WK=WK, WV=WV,
+                 recipe=f"X~N(0,1) [B,N,{C}], W~N(0,1/{C}), Q~N(0,1/D); seed {seed}")
+    if pp:
+        w.pp = True
+        w.WKs = to_dtype(_gauss(seed, "wks", (H, C, D), 1.0 / math.sqrt(C)), "bf16")
+        w.Qs = to_dtype(_gauss(seed, "qs", (H, M, D), 0.6), "bf16")
+        w.Qf = to_dtype(_gauss(seed, "qf", (H, M, D), 0.5), "bf16")
+        w.Q = w.Qf
+        w.gate = np.full((H,), 1.0 / (1.0 + math.exp(-GATE_LOGIT)), dtype=np.float32)
+        w.norm_flags = 15
+        w.alpha_qs = channel_scales(seed, "alpha_qs", H, D)
+        w.alpha_k = channel_scales(seed, "alpha_k", H, D)
+    return w
+
+
+def config5_proj(pp=False, seed=5, N=1 << 20, H=8):
+    """The million-point surface mesh from its block input: X = the 128 RFF
+    channels of the points (bf16 [1, N, 128]) and the per-head projections
+    W / sqrt(128) of config5 as [H, 128, 32] bf16 matrices, so that K = X W_K
+    and V = X W_V are formed inside the forward.  FLARE++ adds the synthesis
+    projection W~_K, raw Qs and Qf and the Table 2 norms (flags 15) with the
+    channel scales of config5_raw."""
+    B, D, M, C = 1, 32, 256, 128
+    pts = sphere_points(seed, B, N).astype(np.float32)
+    omega = _gauss(seed, "omega", (C // 2, 3), 4.0).astype(np.float32)
+    X = to_dtype(_rff(pts, omega).astype(np.float32), "bf16")
+    WK = to_dtype(_per_head(_gauss(seed, "wk", (C, H * D)), H, D), "bf16")
+    WV = to_dtype(_per_head(_gauss(seed, "wv", (C, H * D)), H, D), "bf16")
+    Q = to_dtype(_gauss(seed, "q", (H, M, D), 1.0 / math.sqrt(D)), "bf16")
+    name = "c5_surface_mesh_proj_pp_bf16" if pp else "c5_surface_mesh_proj_bf16"
+    w = Workload(name, B, H, N, M, D, "bf16", Q=Q, K=None, V=None, X=X, WK=WK, WV=WV,
+                 recipe="unit-sphere points, X = RFF(64 w~N(0,16I)) of xyz [1,N,128], W_K, W_V = W/sqrt(128) "
+                        "per head, Q~N(0,1/D)")
+    if pp:
+        w.pp = True
+        w.WKs = to_dtype(_per_head(_gauss(seed, "wks", (C, H * D)), H, D), "bf16")
+        w.Qs = to_dtype(_gauss(seed, "qs", (H, M, D), 1.0 / math.sqrt(D)), "bf16")
+        w.Qf = to_dtype(_gauss(seed, "qf", (H, M, D), 1.0 / math.sqrt(D)), "bf16")
+        w.Q = w.Qf
+        w.gate = np.full((H,), 1.0 / (1.0 + math.exp(-GATE_LOGIT)), dtype=np.float32)
+        w.norm_flags = 15
+        w.alpha_qs = channel_scales(seed, "alpha_qs", H, D)
+        w.alpha_k = channel_scales(seed, "alpha_k", H, D)
+        w.recipe += "; FLARE++: W~_K = Wks/sqrt(128), raw Qs, Qf, Table 2 norms (flags 15)"
+    return w
 
 
 def _rms_norm_f32(x: np.ndarray) -> np.ndarray:
