@@ -281,12 +281,11 @@ def cpu_baseline_backward(w, dY, target_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU clock settles over the first ~40 launches of this sustained
-    # MFMA + transcendental load; 30 warmup steps (about 90 launches) reach it
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["flare", "flare_pp", "flare_pp_norm", "flare_pp_simplified", "flare_backward",
-                                           "flare_pp_backward", "flare_pp_norm_backward"],
+                                           "flare_pp_backward", "flare_pp_norm_backward", "flare_proj",
+                                           "flare_proj_unfused"],
                     default="flare",
                     help="FLARE or FLARE++ routing forward on the million-point surface mesh; flare_pp_norm feeds "
                          "the FLARE++ inputs before their per-head RMS norms and normalises inside the kernels; "
@@ -294,8 +293,14 @@ def main():
                          "synthesis values, no blend) through the same fused-norm entry point; "
                          "flare_backward times the FLARE backward (dQ, dK, dV from dY) after one untimed forward; "
                          "flare_pp_backward the FLARE++ backward likewise, flare_pp_norm_backward the backward of flare_pp_norm "
-                         "(through the fused norms)")
+                         "(through the fused norms); flare_proj starts from the block input X [B,N,128] with the "
+                         "per-head projections K = X W_K, V = X W_V fused into the encode (flare_forward_proj), "
+                         "flare_proj_unfused runs the same from X with the projections as torch.mm calls writing K "
+                         "and V, then flare_forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps, so the GPU clock has ramped up "
+                         "(0 to skip)")
     ap.add_argument("--configs", default="",
                     help="instead of the bench line, time the forward of these workloads (comma-separated names "
                          "from rank_latent_attention_amd.inputs.CONFIGS, or 'all'): 10 warmup and 50 timed calls "
@@ -322,6 +327,9 @@ def main():
         return
     if args.workload in ("flare_backward", "flare_pp_backward", "flare_pp_norm_backward"):
         bench_backward(args, pp=args.workload != "flare_backward", norm=args.workload == "flare_pp_norm_backward")
+        return
+    if args.workload in ("flare_proj", "flare_proj_unfused"):
+        bench_proj(args, fused=args.workload == "flare_proj")
         return
 
     pp = args.workload in ("flare_pp", "flare_pp_norm", "flare_pp_simplified")
@@ -373,6 +381,7 @@ def main():
         dst = src * 1.0
         torch.cuda.synchronize()
         del src, dst
+    settle(step, args.settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -439,7 +448,7 @@ def main():
                     "algorithmic_bytes": (4 if w.shared_vs else 5) * B * H * N * D * 2}
     tok_s = B * N / (ms * 1e-3)
     out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": ("FLARE++" if pp else "FLARE") + " routing forward, million-point surface mesh"
                       + (", simplified (no blend, separate synthesis values)"
@@ -452,6 +461,99 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def bench_proj(args, fused: bool):
+    """One step = the FLARE routing forward from the block input X of the
+    million-point workload (config5_proj): fused, one flare_forward_proj call
+    (the encode forms K and V per tile from X, writes K for the decode);
+    unfused, one torch.mm per batch element for all heads' K and V (hipBLASLt),
+    a copy into the [B,H,N,D] layout and then flare_forward.  FLOPs: 8 BHNMD for the routing plus 4 BNCHD for the two
+    projections."""
+    import torch
+    import rank_latent_attention_amd as flare
+    from rank_latent_attention_amd.inputs import config5_proj
+    t0 = time.perf_counter()
+    w = config5_proj()
+    log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    B, H, N, M, D = w.B, w.H, w.N, w.M, w.D
+    C = w.X.shape[-1]
+    X, WK, WV, Q = up(w.X), up(w.WK), up(w.WV), up(w.Q)
+    Y = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    if fused:
+        ws = flare.workspace(flare.flare.OP_FORWARD_PROJ, B, H, N, M, D, flare.flare.BF16, dev)
+
+        def step():
+            flare.flare_forward_proj(X, WK, WV, Q, Y=Y, Z=Z, L=L, ws=ws)
+    else:
+        K = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        V = torch.empty_like(K)
+        ws = flare.workspace(flare.flare.OP_FORWARD, B, H, N, M, D, flare.flare.BF16, dev)
+        # one GEMM per batch element for every head's K and V ([C, 2 H D]
+        # weights: X is read once), then a copy into the [H, N, D] layout
+        Wcat = torch.cat([WK.permute(1, 0, 2).reshape(C, H * D), WV.permute(1, 0, 2).reshape(C, H * D)],
+                         dim=1).contiguous()
+        KV = torch.empty((N, 2 * H * D), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            for b in range(B):
+                torch.mm(X[b], Wcat, out=KV)
+                K[b].copy_(KV[:, :H * D].view(N, H, D).permute(1, 0, 2))
+                V[b].copy_(KV[:, H * D:].view(N, H, D).permute(1, 0, 2))
+            flare.flare_forward(Q, K, V, Y=Y, Z=Z, L=L, ws=ws)
+    stream = torch.cuda.current_stream(dev)
+    settle(step, args.settle)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps: {ms:.3f} ms/step ({'fused' if fused else 'unfused'} projections)")
+    flops = 8.0 * B * H * N * M * D + 4.0 * B * N * C * H * D
+    achieved = flops / (ms * 1e-3) / 1e12
+    # algorithmic bytes: read X once and write Y
+    kb = B * N * C * 2 + B * H * N * D * 2
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "whole step (%s)" % ("3 launches" if fused else f"{B} GEMMs, {2 * B} copies + 3 launches"),
+                "kernel_us": round(ms * 1e3, 2), "algorithmic_bytes": kb,
+                "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out = {"metric": METRIC + " (from the block input X)", "value": B * N / (ms * 1e-3), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "FLARE routing forward from the block input, million-point surface mesh, "
+                                  + ("projections fused into the encode" if fused
+                                     else "projections as one torch.mm, copied to [B,H,N,D], then flare_forward"),
+                      "B": B, "H": H, "N": N, "M": M, "D": D, "C": C, "inputs": "bf16", "accumulate": "f32"},
+           "tflops": round(achieved, 2), "routing_tflops": round(8.0 * B * H * N * M * D / (ms * 1e-3) / 1e12, 2),
+           "roofline": roofline, "device": device_info()}
+    print(json.dumps(out), flush=True)
+
+
+def settle(step, seconds: float) -> None:
+    """Run the step untimed for at least `seconds` of wall time (then sync):
+    the GPU's clock ramps up over the first tens of milliseconds of this
+    sustained load, and the first launches after idle run up to 1.5 times
+    slower.  Nothing of it is timed."""
+    import torch
+    if seconds <= 0:
+        return
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
 
 
 def bench_backward(args, pp=False, norm=False):
@@ -515,6 +617,7 @@ def bench_backward(args, pp=False, norm=False):
         dst = src * 1.0
         torch.cuda.synchronize()
         del src, dst
+    settle(step, args.settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -545,7 +648,7 @@ def bench_backward(args, pp=False, norm=False):
                 "algorithmic_bytes": kb, "hbm_frac": round(kb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     what = "FLARE++" if pp else "FLARE"
     out = {"metric": METRIC_BWD, "value": B * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"{what} routing backward, million-point surface mesh"
                                   + (", through the per-head RMS norms" if norm else ""), "B": B, "H": H, "N": N,

@@ -84,6 +84,8 @@ extern "C" {
 #define FLARE_OP_ENCODE_BACKWARD 5
 #define FLARE_OP_PP_BACKWARD 6
 #define FLARE_OP_PP_BACKWARD_NORM 7
+#define FLARE_OP_FORWARD_PROJ 8
+#define FLARE_OP_PP_FORWARD_PROJ 9
 
 /* Scratch bytes that `op` needs for this problem (0 when none); returns 0 for
  * arguments the op would reject.  Depends only on its arguments and on the
@@ -176,6 +178,37 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
                           int B, int H, int N, int M, int D, int dtype, float scale, int norm_flags,
                           const float* alpha_qs, const float* alpha_ks, const float* alpha_k, float eps,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* FLARE routing forward from the block input (FLARE++ paper, Sec. 3.1 "FLARE:
+ * fixed-query latent routing": K_h = X W_K,h, V_h = X W_V,h; then App. A.1):
+ *   K[b,h] = X[b] WK[h],  V[b,h] = X[b] WV[h],  Y = SDPA(K, Q, SDPA(Q, K, V)).
+ * The projections run on the matrix cores inside the encode, per tile of
+ * tokens, from X tiles in LDS: V is never stored; K is written once (to K_out,
+ * or to the workspace) and read by the decode.  The projected keys and values
+ * are rounded to bf16 before the attention products, as stored inputs are.
+ * X: [B, N, C] bf16 (shared by the heads); WK, WV: [H, C, D] bf16; Q, Y, Z_out,
+ * L_out as flare_forward; K_out: [B, H, N, D] bf16 or NULL.
+ * Supported: dtype FLARE_BF16, D = 32, C = 128 (else FLARE_ERR_UNSUPPORTED).
+ * ws of flare_workspace_size(FLARE_OP_FORWARD_PROJ, ...) bytes (it includes
+ * room for the projected keys). */
+int flare_forward_proj(const void* X, const void* WK, const void* WV, const void* Q, int q_batched, void* Y,
+                       void* K_out, float* Z_out, float* L_out, int B, int H, int N, int M, int D, int C, int dtype,
+                       float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* FLARE++ routing forward from the block input (Sec. 3.1, 3.2; App. A.1, A.4,
+ * A.6; Table 2 for the norms): synthesis keys X WKs[h] (also the synthesis
+ * values), routing keys X WK[h] and values X WV[h], formed inside the two
+ * encodes as in flare_forward_proj, then the per-head norms of norm_flags
+ * (FLARE_NORM_QS with alpha_qs, FLARE_NORM_KS as N_0, FLARE_NORM_QF,
+ * FLARE_NORM_K with alpha_k) and the FLARE++ forward as flare_pp_forward_norm.
+ * K_out (NULL or [B, H, N, D] bf16) receives the routing keys, normalised when
+ * FLARE_NORM_K is set.  Same support and workspace rules as flare_forward_proj
+ * (op FLARE_OP_PP_FORWARD_PROJ). */
+int flare_pp_forward_proj(const void* X, const void* WKs, const void* WK, const void* WV, const void* Qs,
+                          const void* Qf, const float* gate, void* Y, float* Q_out, void* K_out, float* Z_out,
+                          float* L_out, int B, int H, int N, int M, int D, int C, int dtype, float scale,
+                          int norm_flags, const float* alpha_qs, const float* alpha_k, float eps, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* Backward of the FLARE pair Y = SDPA(K, Q, SDPA(Q, K, V)) (reverse mode;
  * FLARE++ paper, App. B.5 "Local backward" for the encoder with one shard,

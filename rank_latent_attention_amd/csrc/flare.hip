@@ -157,7 +157,7 @@ __device__ inline float norm_factor(float sumsq, int D, float eps) { return rsqr
 // Euclidean norm of the rounding error of the whole row, |bf16(v) - v|^2.
 template <int D, typename QT>
 __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT* row, int g, float scale, bool norm,
-                                   float eps, const float* mul0, const float* mul1) {
+                                   float eps, const float* mul0, const float* mul1, float* norm2 = nullptr) {
   float x[D / 2];
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
@@ -181,7 +181,7 @@ __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT
 #pragma unroll
     for (int j = 0; j < D / 2; ++j) v[j] *= mul1[16 * (j >> 3) + 8 * g + (j & 7)];
   }
-  float e2 = 0.f;
+  float e2 = 0.f, n2 = 0.f;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
 #pragma unroll
@@ -192,7 +192,9 @@ __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT
       o.v[st][s] = h;
       if (lo) lo->v[st][s] = (bf16)r;
       e2 += r * r;
+      n2 += vs * vs;
     }
+  if (norm2) *norm2 = pair_sum(n2);  // the squared norm of the scaled row (before rounding)
   return pair_sum(e2);
 }
 
@@ -527,13 +529,18 @@ template <int D, int NW> __device__ inline void norm_tile(bf16* tile, int wave, 
 // split the tile's 16-byte chunks, and the D / 8 chunks of a row, held by
 // consecutive lanes, add their partial sums by quad permutes.  Rows past the
 // piece repeat its last row, so they add no key from outside it.
-template <int D, int NW> __device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float m) {
+// With dst given, the tile's rows below nvalid are also copied to dst (row
+// n at dst + n D, 16-byte chunks, coalesced).
+template <int D, int NW>
+__device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float m, bf16* dst = nullptr,
+                                     int nvalid = 0) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   constexpr int CPR = D / 8;
   constexpr int CH = dma_rows<NW>() * CPR;  // a multiple of 64
   for (int P0 = wave * 64; P0 < CH; P0 += NW * 64) {
     const int P = P0 + lane;
     const bf16x8 v = reinterpret_cast<const bf16x8*>(tile)[chunk_pos<D>(P / CPR, P % CPR)];
+    if (dst && P / CPR < nvalid) *reinterpret_cast<bf16x8*>(dst + (size_t)(P / CPR) * D + (P % CPR) * 8) = v;
     float s = 0.f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -1796,7 +1803,7 @@ float pick_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf
 // Workspace carve-up: the encode's split partials, then float32 buffers the
 // call needs internally.
 struct WsLayout {
-  size_t part_acc = 0, part_al = 0, z = 0, l = 0, q = 0, total = 0;
+  size_t part_acc = 0, part_al = 0, z = 0, l = 0, q = 0, k = 0, total = 0;
 };
 
 WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, int dtype, bool need_z, bool need_q) {
@@ -1814,6 +1821,10 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
   }
   if (need_z) { w.z = off; off += align256((size_t)BH * M * D * sizeof(float)); w.l = off; off += align256((size_t)BH * M * sizeof(float)); }
   if (need_q) { w.q = off; off += align256((size_t)BH * M * D * sizeof(float)); }
+  if (op == FLARE_OP_FORWARD_PROJ || op == FLARE_OP_PP_FORWARD_PROJ) {  // the projected keys, bf16 [B,H,N,D]
+    w.k = off;
+    off += align256((size_t)BH * N * D * 2);
+  }
   w.total = off;
   return w;
 }
@@ -1821,6 +1832,7 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
 }  // namespace
 
 #include "backward.h"
+#include "proj.h"
 
 // ----------------------------------------------------------------------------
 // Scratch of the allocation-free entry point: a file-scope device array, one
@@ -1869,7 +1881,7 @@ const char* flare_status_string(int status) {
 
 size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype) {
   if (check_common(B, H, N, M, D, dtype, 0) != FLARE_OK) return 0;
-  if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_BACKWARD_NORM) return 0;
+  if (op < FLARE_OP_ENCODE || op > FLARE_OP_PP_FORWARD_PROJ) return 0;
   if (op == FLARE_OP_DECODE) return 0;
   Dev dev;
   if (query_dev(dev) != FLARE_OK) return 0;
@@ -1880,8 +1892,12 @@ size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype
     if (op == FLARE_OP_PP_BACKWARD_NORM) return pp_bwd_norm_layout(dev, B, H, N, M, D).total;
     return bwd_layout(dev, op == FLARE_OP_BACKWARD, B, H, N, M, D).total;
   }
-  const bool need_z = op == FLARE_OP_FORWARD || op == FLARE_OP_PP_FORWARD;
-  const bool need_q = op == FLARE_OP_PP_FORWARD;
+  if (op == FLARE_OP_FORWARD_PROJ || op == FLARE_OP_PP_FORWARD_PROJ) {
+    if (dtype != FLARE_BF16 || D != 32) return 0;
+  }
+  const bool need_z = op == FLARE_OP_FORWARD || op == FLARE_OP_PP_FORWARD || op == FLARE_OP_FORWARD_PROJ ||
+                      op == FLARE_OP_PP_FORWARD_PROJ;
+  const bool need_q = op == FLARE_OP_PP_FORWARD || op == FLARE_OP_PP_FORWARD_PROJ;
   return ws_layout(dev, op, B, H, N, M, D, dtype, need_z, need_q).total;
 }
 
@@ -2041,6 +2057,110 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
   if (rc) return rc;
   // Routing with the per-batch float32 queries.
   return routing(dev, Qb, FLARE_F32, 1, K, V, Y, Z, L, B, H, N, M, D, dtype, qs, wsc, w, rt, st);
+}
+
+// Routing from the block input: the encode projects K and V per tile and
+// writes the keys to Kbuf, the merge forms Z and L, the decode reads Kbuf.
+static int routing_proj(const Dev& dev, const void* X, const void* WK, const void* WV, bf16* Kbuf, const void* Q,
+                        int qtype, int q_batched, void* Y, float* Z, float* L, int B, int H, int N, int M, int D,
+                        float qs, char* ws, const WsLayout& w, const Norms& nm, hipStream_t st) {
+  const int BH = B * H;
+  float* pacc = (float*)(ws + w.part_acc);
+  float2* pal = (float2*)(ws + w.part_al);
+  const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  int rc;
+  if (N > 0) {
+    rc = launch_encode_proj(X, WK, WV, Kbuf, Q, qtype, q_batched, H, N, M, qs, pacc, pal, p, nm, st);
+    if (rc) return rc;
+  }
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+  if (rc) return rc;
+  // the keys in Kbuf are already normalised: the decode only moves their scale onto the queries
+  Norms dn;
+  dn.qmul1 = nm.qmul1;
+  return launch_decode(dev, Q, qtype, q_batched, Kbuf, Z, Y, 0, BH, H, N, M, D, FLARE_BF16, qs, dn, st);
+}
+
+static int check_proj(int B, int H, int N, int M, int D, int C, int dtype) {
+  int rc = check_common(B, H, N, M, D, dtype, 0);
+  if (rc) return rc;
+  if (dtype != FLARE_BF16 || D != 32 || C != kProjC) return FLARE_ERR_UNSUPPORTED;
+  if ((long long)B * N * C >= (1LL << 31)) return FLARE_ERR_UNSUPPORTED;
+  return FLARE_OK;
+}
+
+int flare_forward_proj(const void* X, const void* WK, const void* WV, const void* Q, int q_batched, void* Y,
+                       void* K_out, float* Z_out, float* L_out, int B, int H, int N, int M, int D, int C, int dtype,
+                       float scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_proj(B, H, N, M, D, C, dtype);
+  if (rc) return rc;
+  if (q_batched != 0 && q_batched != 1) return FLARE_ERR_INVALID_ARG;
+  if (!Q || !WK || !WV || (N > 0 && (!X || !Y))) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {X, WK, WV, Q, Y, K_out, Z_out, L_out, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  if (decode_lds(dtype, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const WsLayout w = ws_layout(dev, FLARE_OP_FORWARD_PROJ, B, H, N, M, D, dtype, true, false);
+  if (ws_bytes < w.total || (w.total > 0 && !ws)) return FLARE_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  float* Z = Z_out ? Z_out : (float*)(wsc + w.z);
+  float* L = L_out ? L_out : (float*)(wsc + w.l);
+  bf16* Kb = K_out ? (bf16*)K_out : (bf16*)(wsc + w.k);
+  const float qs = pick_scale(scale, D) * kLog2e;
+  return routing_proj(dev, X, WK, WV, Kb, Q, FLARE_BF16, q_batched, Y, Z, L, B, H, N, M, D, qs, wsc, w, Norms{},
+                      (hipStream_t)stream);
+}
+
+int flare_pp_forward_proj(const void* X, const void* WKs, const void* WK, const void* WV, const void* Qs,
+                          const void* Qf, const float* gate, void* Y, float* Q_out, void* K_out, float* Z_out,
+                          float* L_out, int B, int H, int N, int M, int D, int C, int dtype, float scale,
+                          int norm_flags, const float* alpha_qs, const float* alpha_k, float eps, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int rc = check_proj(B, H, N, M, D, C, dtype);
+  if (rc) return rc;
+  if (!Qs || !Qf || !gate || !WKs || !WK || !WV || (N > 0 && (!X || !Y))) return FLARE_ERR_INVALID_ARG;
+  const void* ptrs[] = {X, WKs, WK, WV, Qs, Qf, gate, Y, Q_out, K_out, Z_out, L_out, ws, alpha_qs, alpha_k};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags & ~FLARE_NORM_ALL) return FLARE_ERR_INVALID_ARG;
+  if (norm_flags && !(eps > 0.f)) return FLARE_ERR_INVALID_ARG;
+  Dev dev;
+  if ((rc = query_dev(dev))) return rc;
+  if (decode_lds(dtype, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  const WsLayout w = ws_layout(dev, FLARE_OP_PP_FORWARD_PROJ, B, H, N, M, D, dtype, true, true);
+  if (ws_bytes < w.total || (w.total > 0 && !ws)) return FLARE_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  hipStream_t st = (hipStream_t)stream;
+  float* Qb = Q_out ? Q_out : (float*)(wsc + w.q);
+  float* Z = Z_out ? Z_out : (float*)(wsc + w.z);
+  float* L = L_out ? L_out : (float*)(wsc + w.l);
+  bf16* Kb = K_out ? (bf16*)K_out : (bf16*)(wsc + w.k);
+  const float qs = pick_scale(scale, D) * kLog2e;
+  const int BH = B * H;
+  // Synthesis from X W~_K, the values being the (normalised) keys (App. A.6).
+  Norms syn;
+  syn.norm_q = (norm_flags & FLARE_NORM_QS) ? 1 : 0;
+  syn.qmul0 = syn.norm_q ? alpha_qs : nullptr;
+  syn.norm_k = norm_flags & FLARE_NORM_KS;
+  syn.eps = eps;
+  const EncPlan p = plan_encode(dev, BH, N, M, dtype);
+  float* pacc = (float*)(wsc + w.part_acc);
+  float2* pal = (float2*)(wsc + w.part_al);
+  if (N > 0) {
+    rc = launch_encode_proj(X, WKs, WKs, nullptr, Qs, FLARE_BF16, 0, H, N, M, qs, pacc, pal, p, syn, st);
+    if (rc) return rc;
+  }
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, nullptr, nullptr, Qf, FLARE_BF16, gate, Qb,
+                    (norm_flags & FLARE_NORM_QF) ? 1 : 0, nullptr, eps, st);
+  if (rc) return rc;
+  // Routing from X W_K (N_0 rows, the scale alpha_k moved onto the queries) and X W_V.
+  Norms rt;
+  rt.norm_k = norm_flags & FLARE_NORM_K;
+  rt.qmul1 = rt.norm_k ? alpha_k : nullptr;
+  rt.eps = eps;
+  return routing_proj(dev, X, WK, WV, Kb, Qb, FLARE_F32, 1, Y, Z, L, B, H, N, M, D, qs, wsc, w, rt, st);
 }
 
 int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libflare.so")
 F32, BF16 = 0, 1
 OP_ENCODE, OP_DECODE, OP_FORWARD, OP_PP_FORWARD, OP_BACKWARD, OP_ENCODE_BACKWARD, OP_PP_BACKWARD = 0, 1, 2, 3, 4, 5, 6
 OP_PP_BACKWARD_NORM = 7
+OP_FORWARD_PROJ, OP_PP_FORWARD_PROJ = 8, 9
 #: input normalisation flags of flare_pp_forward_norm (include/flare.h)
 NORM_QS, NORM_KS, NORM_QF, NORM_K = 1, 2, 4, 8
 NORM_FLAREPP = NORM_QS | NORM_KS | NORM_QF | NORM_K  # FLARE++ (Table 2)
@@ -34,7 +35,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 #: every C entry point declared in include/flare.h
 SYMBOLS = ("flare_workspace_size", "flare_encode", "flare_decode", "flare_forward", "flare_pp_forward",
            "flare_pp_forward_norm", "flare_backward", "flare_encode_backward", "flare_pp_backward",
-           "flare_pp_backward_norm", "flare_status_string", "flare_forward_noalloc")
+           "flare_pp_backward_norm", "flare_status_string", "flare_forward_noalloc", "flare_forward_proj",
+           "flare_pp_forward_proj")
 
 _lib = None
 
@@ -60,6 +62,8 @@ def load(path: str = LIB_PATH):
     L.flare_decode.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_forward_noalloc.argtypes = [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.flare_forward_proj.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.flare_pp_forward_proj.argtypes = [vp] * 12 + [i] * 7 + [f, i, vp, vp, f, vp, sz, vp]
     L.flare_pp_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_forward_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, vp, f,
                                         vp, sz, vp]
@@ -67,8 +71,8 @@ def load(path: str = LIB_PATH):
     L.flare_encode_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_backward.argtypes = [vp] * 19 + [i, i, i, i, i, i, f, vp, sz, vp]
     L.flare_pp_backward_norm.argtypes = [vp] * 22 + [i, i, i, i, i, i, f, i, vp, vp, vp, f, vp, sz, vp]
-    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_forward_noalloc, L.flare_pp_forward,
-               L.flare_pp_forward_norm,
+    for fn in (L.flare_encode, L.flare_decode, L.flare_forward, L.flare_forward_noalloc, L.flare_forward_proj,
+               L.flare_pp_forward_proj, L.flare_pp_forward, L.flare_pp_forward_norm,
                L.flare_backward, L.flare_encode_backward, L.flare_pp_backward, L.flare_pp_backward_norm):
         fn.restype = i
     L.flare_status_string.argtypes = [i]
@@ -236,6 +240,83 @@ def flare_forward_noalloc(Q, K, V, scale: float = 0.0, Y=None, Z=None, L=None):
                                       float(scale), _stream(K.device))
     _check("flare_forward_noalloc", rc)
     return Y, Z, L
+
+
+def _proj_dims(X, W, name="WK"):
+    if X.dim() != 3:
+        raise ValueError(f"X must be [B,N,C], got {tuple(X.shape)}")
+    if W.dim() != 3 or W.shape[1] != X.shape[2]:
+        raise ValueError(f"{name} must be [H,C,D] with C = {X.shape[2]}, got {tuple(W.shape)}")
+    B, N, C = X.shape
+    H, _, D = W.shape
+    return B, H, N, D, C
+
+
+def flare_forward_proj(X, WK, WV, Q, scale: float = 0.0, Y=None, K_out=None, Z=None, L=None, ws=None):
+    """FLARE routing forward from the block input (flare_forward_proj in
+    include/flare.h): K = X WK, V = X WV per head inside the encode, then the
+    FLARE pair.  X [B,N,C], WK, WV [H,C,D], Q [H,M,D] or [B,H,M,D], all bf16.
+    Returns (Y, K_out, Z, L); the last three only when passed in."""
+    B, H, N, D, C = _proj_dims(X, WK)
+    if WV.shape != WK.shape:
+        raise ValueError("WV must have WK's shape")
+    if Q.dim() == 3 and Q.shape[0] == H and Q.shape[2] == D:
+        M, qb = Q.shape[1], 0
+    elif Q.dim() == 4 and Q.shape[0] == B and Q.shape[1] == H and Q.shape[3] == D:
+        M, qb = Q.shape[2], 1
+    else:
+        raise ValueError(f"Q must be [H,M,D] or [B,H,M,D] with H={H}, D={D}, got {tuple(Q.shape)}")
+    for t in (X, WK, WV, Q):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("X, WK, WV and Q must be bfloat16")
+    _out("Y", Y, (B, H, N, D), torch.bfloat16)
+    _out("K_out", K_out, (B, H, N, D), torch.bfloat16)
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
+    _same(X, WK, WV, Q, Y, K_out, Z, L, ws)
+    Y = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=X.device) if Y is None else Y
+    ws = workspace(OP_FORWARD_PROJ, B, H, N, M, D, BF16, X.device) if ws is None else ws
+    rc = load().flare_forward_proj(_ptr(X), _ptr(WK), _ptr(WV), _ptr(Q), qb, _ptr(Y), _ptr(K_out), _ptr(Z), _ptr(L),
+                                   B, H, N, M, D, C, BF16, float(scale), _ptr(ws), _ws_bytes(ws), _stream(X.device))
+    _check("flare_forward_proj", rc)
+    return Y, K_out, Z, L
+
+
+def flare_pp_forward_proj(X, WKs, WK, WV, Qs, Qf, gate, norm_flags: int, alpha_qs=None, alpha_k=None,
+                          eps: float = 1e-6, scale: float = 0.0, Y=None, Q_out=None, K_out=None, Z=None, L=None,
+                          ws=None):
+    """FLARE++ routing forward from the block input (flare_pp_forward_proj in
+    include/flare.h): synthesis keys (= values) X WKs, routing keys X WK and
+    values X WV per head, the Table 2 norms of norm_flags (alpha_qs, alpha_k
+    float32 [H,D] or None), then FLARE++.  Returns (Y, Q_out, K_out, Z, L)."""
+    B, H, N, D, C = _proj_dims(X, WK)
+    if WV.shape != WK.shape or WKs.shape != WK.shape:
+        raise ValueError("WKs, WK, WV must share one shape [H,C,D]")
+    if Qs.dim() != 3 or Qs.shape[0] != H or Qs.shape[2] != D or Qf.shape != Qs.shape:
+        raise ValueError("Qs and Qf must be [H,M,D]")
+    M = Qs.shape[1]
+    for t in (X, WKs, WK, WV, Qs, Qf):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("X, WKs, WK, WV, Qs and Qf must be bfloat16")
+    if gate.dtype != torch.float32 or gate.numel() != H:
+        raise ValueError("gate must be float32 [H]")
+    for a in (alpha_qs, alpha_k):
+        if a is not None and (a.dtype != torch.float32 or tuple(a.shape) != (H, D)):
+            raise ValueError("alpha arrays must be float32 [H, D]")
+    _out("Y", Y, (B, H, N, D), torch.bfloat16)
+    _out("Q_out", Q_out, (B, H, M, D), torch.float32)
+    _out("K_out", K_out, (B, H, N, D), torch.bfloat16)
+    _out("Z", Z, (B, H, M, D), torch.float32)
+    _out("L", L, (B, H, M), torch.float32)
+    _same(X, WKs, WK, WV, Qs, Qf, gate, Y, Q_out, K_out, Z, L, alpha_qs, alpha_k, ws)
+    Y = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=X.device) if Y is None else Y
+    ws = workspace(OP_PP_FORWARD_PROJ, B, H, N, M, D, BF16, X.device) if ws is None else ws
+    rc = load().flare_pp_forward_proj(_ptr(X), _ptr(WKs), _ptr(WK), _ptr(WV), _ptr(Qs), _ptr(Qf), _ptr(gate), _ptr(Y),
+                                      _ptr(Q_out), _ptr(K_out), _ptr(Z), _ptr(L), B, H, N, M, D, C, BF16,
+                                      float(scale), int(norm_flags), _ptr(alpha_qs), _ptr(alpha_k), float(eps),
+                                      _ptr(ws), _ws_bytes(ws), _stream(X.device))
+    _check("flare_pp_forward_proj", rc)
+    return Y, Q_out, K_out, Z, L
 
 
 def flare_pp_forward(Qs, Ks, Vs, Qf, gate, K, V, scale: float = 0.0, Y=None, Q_out=None, Z=None, L=None, ws=None):

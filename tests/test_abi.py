@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["flare_workspace_size", "flare_encode", "flare_decode", "flare_forward",
                                            "flare_pp_forward", "flare_pp_forward_norm", "flare_backward",
                                            "flare_encode_backward", "flare_pp_backward", "flare_pp_backward_norm",
-                                           "flare_status_string", "flare_forward_noalloc"])
+                                           "flare_status_string", "flare_forward_noalloc", "flare_forward_proj",
+                                           "flare_pp_forward_proj"])
 
 
 def test_library_exports_every_declared_symbol(lib):
