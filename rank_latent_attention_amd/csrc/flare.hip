@@ -206,11 +206,24 @@ __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT
 // with exact scores (queries as bf16 hi + lo).  Squared, as compared.
 constexpr float kScoreErr2 = 0x1p-10f;
 
-// Largest value over the 64 lanes of a wave.
+// Largest value over the 64 lanes of a wave, on every lane: within rows of
+// 16 lanes by DPP quad and mirror moves, then across rows by the permlane
+// swaps (no LDS traffic).
+__device__ inline float dpp_max(float x, int ctrl) {
+  float y;
+  switch (ctrl) {  // the DPP control must be a constant
+    case 0: y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)); break;  // xor 1
+    case 1: y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)); break;  // xor 2
+    case 2: y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)); break;  // half mirror
+    default: y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)); break;  // mirror
+  }
+  return fmaxf(x, y);
+}
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = dpp_max(dpp_max(dpp_max(dpp_max(x, 0), 1), 2), 3);  // the row's maximum on all 16 lanes
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));  // rows 2k and 2k + 1
+  return pair_max(x);                                       // and the other half of the wave
 }
 
 // Squared Euclidean norm of a bf16 QK operand row (half in this lane, half in
@@ -427,6 +440,24 @@ __device__ inline void mask_rows(f32x16& s, int from, int g) {
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+}
+
+// One online-softmax step of the exact recomputations with the running shift
+// held as one float per lane (the shift of this lane's column): on entry s is
+// the raw score tile, on exit the weights exp2(s - shift).  The shift is
+// raised to the tile maximum when that exceeds it by more than kTheta, or on
+// the first non-empty tile; acc and lsum are rescaled with it.
+__device__ inline void online_step_s(f32x16& s, float& shift, bool& started, float& lsum, f32x16& acc) {
+  const float t = col_max(s);
+  if ((t > shift + kTheta) || (!started && t > -INFINITY)) {
+    const float f = started ? fast_exp2(shift - t) : 0.f;
+    acc = acc * f;
+    lsum *= f;
+    shift = t;
+    started = true;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r] - shift);
 }
 
 // bf16 fast path.  Softmax is invariant to the shift, and floating point is
@@ -890,9 +921,9 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
                                        int ng, int WN, int rows, int lane, const QKOp<bf16, D>& qhi,
                                        const QKOp<bf16, D>& qlo, float& lsum, f32x16& acc) {
   const int li = lane & 31, g = lane >> 5;
-  f32x16 negs;
+  float shift = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { negs[r] = 0.f; acc[r] = 0.f; }
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   lsum = 0.f;
   bool started = false;
   for (int t0 = n_lo; t0 < n_hi; t0 += rows) {
@@ -916,15 +947,15 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
         if (j < 8) vop.a0[j] = (bf16)v;
         else vop.a1[j - 8] = (bf16)v;
       }
-      f32x16 sc = qk_mma<D>(kop, qlo, qk_mma<D>(kop, qhi, negs));
+      f32x16 sc = qk_mma<D>(kop, qlo, qk_mma<D>(kop, qhi, f32x16{}));
       if (row0 + 32 > n_hi) mask_rows(sc, n_hi - row0, g);
-      online_step(sc, negs, started, lsum, acc);
+      online_step_s(sc, shift, started, lsum, acc);
       bf16x8 b0, b1;
       lsum += pack_exps(sc, b0, b1);
       acc = pv_mma(vop, b0, b1, acc);
     }
   }
-  return -negs[0];
+  return shift;
 }
 
 // bf16 encode: NW waves in WN token lanes of G = NW / WN latent groups; wave w
@@ -1046,15 +1077,21 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     for (int w = 0; w < NW; ++w) kmax2 = fmaxf(kmax2, kred[w]);
     // unshifted partial (see fast_ok), renormalised to a power-of-two shift
     // so that the merge never adds sums beyond the float range; or the exact
-    // recomputation when the rounded queries could move a score too far
-    float ltot = wsum.total(li, acc), shift = 0.f;
+    // recomputation when the rounded queries could move a score too far.
+    // Lane indices are taken again from an index opaque to the compiler, so
+    // that none is held in a register across the tile loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane2 = tid & 63, li2 = lane2 & 31, g2 = lane2 >> 5, m2 = mg * 32 + li2;
+    float ltot = wsum.total(li2, acc), shift = 0.f;
     const bool inexact = qerr2 * kmax2 > kScoreErr2;
     if (inexact || fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
+      const QT* qr = reinterpret_cast<const QT*>(a.Q) + ((size_t)(a.q_batched ? bh : h) * M + (m2 < M ? m2 : M - 1)) * D;
       QKOp<bf16, D> qhi, qlo;
-      load_q_row<D>(qhi, &qlo, qrow(), g, a.qscale, a.norm_q != 0, a.eps, qm0, qm1);
-      if (m >= M) { zero_op<D>(qhi); zero_op<D>(qlo); }
+      load_q_row<D>(qhi, &qlo, qr, g2, a.qscale, a.norm_q != 0, a.eps, qm0, qm1);
+      if (m2 >= M) { zero_op<D>(qhi); zero_op<D>(qlo); }
       float lsum;
-      shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane, qhi, qlo,
+      shift = encode_careful<D, NK>(Kh, alias ? Kh : Vh, alias, a.eps, n_lo, n_hi, ng, WN, ROWS, lane2, qhi, qlo,
                                     lsum, acc);
       ltot = pair_sum(lsum);
     } else {
@@ -1064,17 +1101,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       ltot *= sc;
       shift = (float)e;
     }
-    if (m < M) {
+    if (m2 < M) {
       const size_t p = (size_t)bhl * a.pmax + slot;
-      float* dst = a.part_acc + (p * M + m) * D;
+      float* dst = a.part_acc + (p * M + m2) * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if (8 * c + 4 * g < D) {
+        if (8 * c + 4 * g2 < D) {
           f32x4 v = {acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
-          *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g) = v;
+          *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g2) = v;
         }
       }
-      if (g == 0) a.part_al[p * M + m] = make_float2(shift, ltot);
+      if (g2 == 0) a.part_al[p * M + m2] = make_float2(shift, ltot);
     }
     x = hb + n_hi;
   }
