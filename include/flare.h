@@ -219,12 +219,15 @@ int flare_pp_forward_proj(const void* X, const void* WKs, const void* WK, const 
  *   encoder  P = softmax over tokens,  c_m = dZ_m . Z_m,
  *            dS_enc = P o (dZ V^T - c),  dV = P^T dZ
  *   dK = s (dS_dec + dS_enc)^T Q,  dQ = s (dS_dec + dS_enc) K.
- * Inputs: Q, K, V as for flare_forward (dtype FLARE_BF16 only, else
- * FLARE_ERR_UNSUPPORTED); Z [B,H,M,D] f32 and L [B,H,M] f32 are the
- * latents and log-normalisers flare_forward returned for the same Q, K, V
- * (the scores are recomputed, never stored); dY [B,H,N,D] bf16.
+ * Inputs: Q, K, V as for flare_forward, dtype FLARE_BF16 or FLARE_F32;
+ * Z [B,H,M,D] f32 and L [B,H,M] f32 are the latents and log-normalisers
+ * flare_forward returned for the same Q, K, V (the scores are recomputed,
+ * never stored); dY [B,H,N,D] in the input dtype.
  * Outputs: dQ f32 in Q's layout ([H,M,D] shared queries receive the sum
- * over the batch); dK, dV [B,H,N,D] bf16; dZ_out [B,H,M,D] f32 or NULL.
+ * over the batch); dK, dV [B,H,N,D] in the input dtype; dZ_out [B,H,M,D]
+ * f32 or NULL.  bf16 inputs use bf16 matrix-core operands with float32
+ * accumulation; float32 inputs are computed in float32 throughout (every
+ * exponential with its exact shift).
  * All device pointers 16-byte aligned; ws of
  * flare_workspace_size(FLARE_OP_BACKWARD, ...) bytes is required.  The result
  * is deterministic (fixed split plan, fixed summation order). */
@@ -252,11 +255,11 @@ int flare_encode_backward(const void* Q, int q_batched, const void* K, const voi
  * and dQd is handed once to the synthesis encoder's backward (as
  * flare_encode_backward with dL = 0), which gives dQs (summed over the
  * batch), dKs and dVs.  The synthesis latents Qd are recomputed.
- * Inputs: those of flare_pp_forward (dtype FLARE_BF16 only, inputs already
- * normalised) plus what it returned for them: Q [B,H,M,D] f32 (its Q_out),
- * Z [B,H,M,D] f32 and L [B,H,M] f32; dY [B,H,N,D] bf16.
+ * Inputs: those of flare_pp_forward (dtype FLARE_BF16 or FLARE_F32, inputs
+ * already normalised) plus what it returned for them: Q [B,H,M,D] f32 (its
+ * Q_out), Z [B,H,M,D] f32 and L [B,H,M] f32; dY [B,H,N,D] in the input dtype.
  * Outputs: dQs, dQf [H,M,D] f32; dgate [H] f32; dKs, dVs, dK, dV [B,H,N,D]
- * bf16; dQ_out [B,H,M,D] f32 or NULL.  When Vs == Ks (shared synthesis keys
+ * in the input dtype; dQ_out [B,H,M,D] f32 or NULL.  When Vs == Ks (shared synthesis keys
  * and values, App. A.6) dKs receives the sum of the key and value
  * cotangents and dVs is not written (it may be NULL).
  * ws of flare_workspace_size(FLARE_OP_PP_BACKWARD, ...) bytes. */

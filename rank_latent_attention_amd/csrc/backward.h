@@ -1236,6 +1236,8 @@ PpBwdNormLayout pp_bwd_norm_layout(const Dev& dev, int B, int H, int N, int M, i
 
 }  // namespace
 
+#include "backward32.h"
+
 // ----------------------------------------------------------------------------
 // C ABI of the backward
 // ----------------------------------------------------------------------------
@@ -1246,13 +1248,20 @@ int flare_backward(const void* Q, int q_batched, const void* K, const void* V, c
                    int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(B, H, N, M, D, dtype, q_batched);
   if (rc) return rc;
-  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
   if (!Q || !Z || !L || !dQ || (N > 0 && (!K || !V || !dY || !dK || !dV))) return FLARE_ERR_INVALID_ARG;
   const void* ptrs[] = {Q, K, V, Z, L, dY, dQ, dK, dV, dZ_out, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
   Dev dev;
   if ((rc = query_dev(dev))) return rc;
+  if (dtype == FLARE_F32) {
+    if (!bwd32_fits(dev, true, D, M)) return FLARE_ERR_UNSUPPORTED;
+    const Bwd32Layout w = bwd32_layout(dev, true, B, H, N, M, D);
+    if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+    return backward32(dev, true, (const float*)Q, q_batched, (const float*)K, (const float*)V, Z, L,
+                      (const float*)dY, nullptr, nullptr, dQ, (float*)dK, (float*)dV, false, dZ_out, B, H, N, M, D,
+                      pick_scale(scale, D), (char*)ws, w, (hipStream_t)stream);
+  }
   if (row_lds(D, M) > dev.lds_max || decode_lds(FLARE_BF16, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const BwdLayout w = bwd_layout(dev, true, B, H, N, M, D);
   if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
@@ -1266,13 +1275,20 @@ int flare_encode_backward(const void* Q, int q_batched, const void* K, const voi
                           int D, int dtype, float scale, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(B, H, N, M, D, dtype, q_batched);
   if (rc) return rc;
-  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
   if (!Q || !Z || !L || !dZ || !dQ || (N > 0 && (!K || !V || !dK || !dV))) return FLARE_ERR_INVALID_ARG;
   const void* ptrs[] = {Q, K, V, Z, L, dZ, dL, dQ, dK, dV, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
   Dev dev;
   if ((rc = query_dev(dev))) return rc;
+  if (dtype == FLARE_F32) {
+    if (!bwd32_fits(dev, false, D, M)) return FLARE_ERR_UNSUPPORTED;
+    const Bwd32Layout w = bwd32_layout(dev, false, B, H, N, M, D);
+    if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+    return backward32(dev, false, (const float*)Q, q_batched, (const float*)K, (const float*)V, Z, L, nullptr, dZ, dL,
+                      dQ, (float*)dK, (float*)dV, false, nullptr, B, H, N, M, D, pick_scale(scale, D), (char*)ws, w,
+                      (hipStream_t)stream);
+  }
   if (row_lds(D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const BwdLayout w = bwd_layout(dev, false, B, H, N, M, D);
   if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
@@ -1288,7 +1304,6 @@ int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void
                       void* stream) {
   int rc = check_common(B, H, N, M, D, dtype, 0);
   if (rc) return rc;
-  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
   const bool alias = Ks == Vs;
   if (!Qs || !Qf || !gate || !Q || !Z || !L || !dQs || !dQf || !dgate) return FLARE_ERR_INVALID_ARG;
   if (N > 0 && (!Ks || !Vs || !K || !V || !dY || !dKs || (!alias && !dVs) || !dK || !dV)) return FLARE_ERR_INVALID_ARG;
@@ -1297,6 +1312,43 @@ int flare_pp_backward(const void* Qs, const void* Ks, const void* Vs, const void
     if (!aligned16(p)) return FLARE_ERR_INVALID_ARG;
   Dev dev;
   if ((rc = query_dev(dev))) return rc;
+  if (dtype == FLARE_F32) {
+    if (!bwd32_fits(dev, true, D, M)) return FLARE_ERR_UNSUPPORTED;
+    const PpBwd32Layout w = pp_bwd32_layout(dev, B, H, N, M, D);
+    if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;
+    char* wsc = (char*)ws;
+    hipStream_t st = (hipStream_t)stream;
+    const float s = pick_scale(scale, D);
+    const int BH = B * H;
+    float* Zs = (float*)(wsc + w.zs);
+    float* Ls = (float*)(wsc + w.ls);
+    float* dQb = dQ_out ? dQ_out : (float*)(wsc + w.dq);
+    float* dQd = (float*)(wsc + w.dqd);
+    // 1. the synthesis latents Qd = SDPA(Qs, Ks, Vs) and their log-normalisers
+    const EncPlan p = plan_encode(dev, BH, N, M, FLARE_F32);
+    if (N > 0) {
+      rc = launch_encode(Qs, FLARE_F32, 0, Ks, Vs, 0, H, N, M, D, FLARE_F32, s * kLog2e, (float*)(wsc + w.part_acc),
+                         (float2*)(wsc + w.part_al), p, Norms{}, st);
+      if (rc) return rc;
+    }
+    rc = launch_merge(p, (float*)(wsc + w.part_acc), (float2*)(wsc + w.part_al), 0, BH, H, N, M, D, Zs, Ls, nullptr,
+                      FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+    if (rc) return rc;
+    // 2. the routing pair's backward with the per-batch queries
+    rc = backward32(dev, true, Q, 1, (const float*)K, (const float*)V, Z, L, (const float*)dY, nullptr, nullptr, dQb,
+                    (float*)dK, (float*)dV, false, nullptr, B, H, N, M, D, s, wsc + w.region,
+                    bwd32_layout(dev, true, B, H, N, M, D), st);
+    if (rc) return rc;
+    // 3. the blend
+    rc = launch(blend_backward_kernel, dim3(H), dim3(kThreads), 0, st, dQb, Zs, gate, dQd, dQf, dgate, B, H, M, D);
+    if (rc) return rc;
+    // 4. the synthesis encoder's backward with dZ = dQd (dL = 0), the seeds
+    //    shared over the batch
+    return backward32(dev, false, (const float*)Qs, 0, (const float*)Ks, (const float*)Vs, Zs, Ls, nullptr, dQd,
+                      nullptr, dQs, (float*)dKs, (float*)dVs, alias, nullptr, B, H, N, M, D, s, wsc + w.region,
+                      bwd32_layout(dev, false, B, H, N, M, D), st);
+  }
+  if (dtype != FLARE_BF16) return FLARE_ERR_UNSUPPORTED;
   if (row_lds(D, M) > dev.lds_max || decode_lds(FLARE_BF16, D, M) > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
   const PpBwdLayout w = pp_bwd_layout(dev, B, H, N, M, D);
   if (ws_bytes < w.total || !ws) return FLARE_ERR_WORKSPACE;

@@ -25,7 +25,8 @@
 //                     and the latents stay in LDS for a head, every wave takes
 //                     32 tokens per step, S = Q K^T and Y^T += Z^T P run on
 //                     MFMA with one lane per token column.
-// backward.h holds the reverse-mode kernels and their entry points.
+// backward.h holds the reverse-mode kernels and their entry points, backward32.h
+// the float32 ones.
 // Scores are kept in log2 units: the queries are pre-multiplied by
 // s*log2(e) so every exponential is a single v_exp_f32.  The bf16 loops use
 // no shift at all (weights exp2(score), checked for range afterwards, with an
@@ -1924,7 +1925,11 @@ size_t flare_workspace_size(int op, int B, int H, int N, int M, int D, int dtype
   if (query_dev(dev) != FLARE_OK) return 0;
   if (op == FLARE_OP_BACKWARD || op == FLARE_OP_ENCODE_BACKWARD || op == FLARE_OP_PP_BACKWARD ||
       op == FLARE_OP_PP_BACKWARD_NORM) {
-    if (dtype != FLARE_BF16) return 0;
+    if (dtype == FLARE_F32) {
+      if (op == FLARE_OP_PP_BACKWARD_NORM) return 0;
+      if (op == FLARE_OP_PP_BACKWARD) return pp_bwd32_layout(dev, B, H, N, M, D).total;
+      return bwd32_layout(dev, op == FLARE_OP_BACKWARD, B, H, N, M, D).total;
+    }
     if (op == FLARE_OP_PP_BACKWARD) return pp_bwd_layout(dev, B, H, N, M, D).total;
     if (op == FLARE_OP_PP_BACKWARD_NORM) return pp_bwd_norm_layout(dev, B, H, N, M, D).total;
     return bwd_layout(dev, op == FLARE_OP_BACKWARD, B, H, N, M, D).total;

@@ -394,7 +394,7 @@ def flare_backward(Q, K, V, Z, L, dY, scale: float = 0.0, dQ=None, dK=None, dV=N
     """Backward of the FLARE pair (flare_backward in include/flare.h): given
     the forward's Z [B,H,M,D] and L [B,H,M] (float32) and the output
     cotangent dY, returns (dQ, dK, dV, dZ); dQ is float32 in Q's layout,
-    dK and dV bf16; dZ only when passed in."""
+    dK and dV in K's dtype (bf16 or float32); dZ only when passed in."""
     B, H, N, M, D, qb = _dims(Q, K)
     dt = _dtype_code(K)
     if Q.dtype != K.dtype or V.dtype != K.dtype or dY.dtype != K.dtype or V.shape != K.shape or dY.shape != K.shape:

@@ -102,7 +102,8 @@ def bwd(lib, dt=1, D=16, M=8, Q=FAKE, Z=FAKE, L=FAKE, dY=FAKE, dQ=FAKE, dK=FAKE,
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dt=0), 2), (dict(D=24), 2), (dict(M=300), 2),              # float32, head size, latent count
+    (dict(dt=3), 2), (dict(D=24), 2), (dict(M=300), 2),              # unknown dtype, head size, latent count
+    (dict(dt=0, Q=None), 1), (dict(dt=0, dQ=MISALIGNED), 1),         # float32: the same argument checks
     (dict(Q=None), 1), (dict(Z=None), 1), (dict(L=None), 1), (dict(dY=None), 1), (dict(dQ=None), 1),
     (dict(dK=None), 1), (dict(dQ=MISALIGNED), 1), (dict(dZo=MISALIGNED), 1),
 ])
@@ -116,9 +117,11 @@ def test_encode_backward_rejects_bad_arguments(lib):
               None) == 1   # dZ is required
     assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 1, 0.0, FAKE,
               1 << 30, None) == 1
-    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 0, 0.0, FAKE, 1 << 30,
-              None) == 2
-    assert lib.flare_workspace_size(4, 1, 1, 8, 8, 16, 0) == 0   # the backward is bf16 only
+    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 3, 0.0, FAKE, 1 << 30,
+              None) == 2   # unknown dtype
+    assert eb(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1, 1, 8, 8, 16, 0, 0.0, FAKE, 1 << 30,
+              None) == 1   # float32: dZ is required too
+    assert lib.flare_workspace_size(7, 1, 1, 8, 8, 16, 0) == 0   # the backward through the norms is bf16 only
 
 
 def ppb(lib, dt=1, D=16, Vs=FAKE, dVs=FAKE, Q=FAKE, dgate=FAKE, dQo=None):
@@ -127,7 +130,7 @@ def ppb(lib, dt=1, D=16, Vs=FAKE, dVs=FAKE, Q=FAKE, dgate=FAKE, dQo=None):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dt=0), 2), (dict(D=20), 2), (dict(Q=None), 1), (dict(dgate=None), 1),
+    (dict(dt=3), 2), (dict(D=20), 2), (dict(Q=None), 1), (dict(dgate=None), 1), (dict(dt=0, Q=None), 1),
     (dict(Vs=ctypes.c_void_p(2 << 20), dVs=None), 1),   # separate synthesis values need their cotangent
     (dict(dQo=MISALIGNED), 1),
 ])
