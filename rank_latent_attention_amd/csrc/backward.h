@@ -803,7 +803,8 @@ int launch_col_k(const ColArgs& a, hipStream_t st) {
 
 template <typename QT, int D, bool DEC>
 int launch_col_d(const ColArgs& a, int NW, int WN, hipStream_t st) {
-  if (NW == 8) return launch_col_k<QT, D, 8, 1, DEC>(a, st);
+  if (NW == 8 && WN == 1) return launch_col_k<QT, D, 8, 1, DEC>(a, st);
+  if (NW != 4) return FLARE_ERR_UNSUPPORTED;  // no kernel for this split plan
   if (WN == 4) return launch_col_k<QT, D, 4, 4, DEC>(a, st);
   if (WN == 2) return launch_col_k<QT, D, 4, 2, DEC>(a, st);
   return launch_col_k<QT, D, 4, 1, DEC>(a, st);

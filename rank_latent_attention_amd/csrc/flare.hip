@@ -61,7 +61,8 @@ constexpr int kTile = 128;         // tokens per float32 encode LDS tile (4 bloc
 // workgroup of NW waves: 32 per wave up to 128, so two tiles of K and V stay
 // within 64 KB and four waves per SIMD still fit.
 template <int NW> constexpr int dma_rows() { return 128 < 32 * NW ? 128 : 32 * NW; }
-constexpr int kDecGroup = 128;     // tokens per decode step of a workgroup (32 per wave)
+constexpr int kDecWaves = 16;      // waves per decode workgroup: one workgroup per compute unit
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTheta = 8.0f;     // lazy-rescale threshold, log2 units
@@ -1309,15 +1310,23 @@ template <typename T, int D> struct DecLds {
 // the dot product of the token's output cotangent with its output.
 // MBT > 0 fixes the number of latent blocks at compile time (a.MB == MBT), so
 // the latent loop unrolls completely; 0 reads it from the arguments.
+//
+// One workgroup of kDecWaves waves per compute unit (four per SIMD) shares a
+// head's staged queries and latents.  Its waves take the piece's 32-token
+// blocks from a counter in LDS as they finish the previous one, so all of them
+// run to the end of the piece together: with several workgroups per compute
+// unit the oldest ones are issued first, finish early and leave the last to
+// run alone at one wave per SIMD.
 template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
+__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
   using L = DecLds<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int MB = MBT > 0 ? MBT : a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
   T* zt = qs + (size_t)Mp * L::QST;
-  __shared__ float zred[kThreads / 64], qred[kThreads / 64];
+  __shared__ float zred[kDecWaves], qred[kDecWaves];
+  __shared__ int next_blk;  // the next unclaimed 32-token block of the piece
   const int zst = (int)L::zst(MB);
   // the wave index is uniform: kept in a scalar register, block guards derived
   // from it become scalar branches
@@ -1347,8 +1356,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     float qerr2 = 0.f;  // largest squared rounding error of a staged query row
     {
       constexpr int QE = 16 / sizeof(QT);          // elements per 16-byte chunk
-      constexpr int QJ = 256 * D / QE / kThreads;  // chunks per thread at M = 256
-      constexpr int ZJ = 256 * D / 4 / kThreads;
+      constexpr int QJ = (256 * D / QE + kDecThreads - 1) / kDecThreads;  // chunks per thread at M = 256
+      constexpr int ZJ = (256 * D / 4 + kDecThreads - 1) / kDecThreads;
       const int nq = M * D / QE, nz = M * D / 4;   // chunks of real rows
       const int pq = Mp * D / QE, pz = Mp * D / 4; // chunks including the zero rows
       // chunk offsets from an index opaque to the compiler, so they are
@@ -1358,17 +1367,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       uint4 qv[QJ], zv[ZJ];
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
-        const int c = tid + j * kThreads;
+        const int c = tid + j * kDecThreads;
         qv[j] = reinterpret_cast<const uint4*>(Qh)[c < nq ? c : 0];
       }
 #pragma unroll
       for (int j = 0; j < ZJ; ++j) {
-        const int c = tid + j * kThreads;
+        const int c = tid + j * kDecThreads;
         zv[j] = reinterpret_cast<const uint4*>(Zh)[c < nz ? c : 0];
       }
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
-        const int c = tid + j * kThreads;
+        const int c = tid + j * kDecThreads;
         float ce2 = 0.f;  // squared rounding error of these QE staged values
         if (c < pq) {
           const int m = c * QE / D, d0 = c * QE % D;
@@ -1400,7 +1409,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       }
 #pragma unroll
       for (int j = 0; j < ZJ; ++j) {
-        const int c = tid + j * kThreads;
+        const int c = tid + j * kDecThreads;
         if (c < pz) {
           const int m = c * 4 / D, d0 = c * 4 % D;
           const float* src = reinterpret_cast<const float*>(&zv[j]);
@@ -1418,9 +1427,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     zmax = wave_max(zmax);
     qerr2 = wave_max(qerr2);
     if (lane == 0) { zred[wave] = zmax; qred[wave] = qerr2; }
+    // wave w starts with block w; the counter hands out the rest
+    if (threadIdx.x == 0) next_blk = kDecWaves;
     __syncthreads();
-    zmax = fmaxf(fmaxf(zred[0], zred[1]), fmaxf(zred[2], zred[3]));
-    qerr2 = fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3]));
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) { zmax = fmaxf(zmax, zred[w]); qerr2 = fmaxf(qerr2, qred[w]); }
     const float zlim = 1.329228e36f / fmaxf(zmax * 1.01f, 1.f);  // 2^120 / max|z|
     // a token block keeps the fast loop's result only if every score it
     // forms is within kScoreErr of the exact one: |k_n|^2 <= klim2
@@ -1428,11 +1439,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
-    // wave w takes tokens t0 + [0, 32) for t0 = n_lo + 32 w, + kDecGroup, ...;
-    // the next block's key rows are fetched while the current one is decoded.
-    // Lanes past the piece read its last row instead: their outputs are not
-    // stored and their scores only reach their own column.
-    int t0 = n_lo + 32 * wave;
+    // Block b holds tokens n_lo + 32 b + [0, 32); the wave claims its next
+    // block when it starts one and fetches that block's key rows while the
+    // current one is decoded.  Lanes past the piece read its last row instead:
+    // their outputs are not stored and their scores only reach their own
+    // column.
+    const int nblk = (n_hi - n_lo + 31) / 32;
+    int b = wave;
+    int t0 = n_lo + 32 * b;
     QKOp<T, D> kop;
     load_op<D>(kop, Kh + (size_t)(t0 + li < n_hi ? t0 + li : n_hi - 1) * D, g);
     // Settle these keys before the loop: inside it the compiler would place
@@ -1440,11 +1454,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
     for (int st = 0; st < (int)(sizeof(kop.v) / sizeof(kop.v[0])); ++st) asm volatile("" : "+v"(kop.v[st]));
     const f32x16 zero16 = {};
-    for (; t0 < n_hi; t0 += kDecGroup) {
+    while (b < nblk) {
       if constexpr (NK) norm_op<D>(kop, a.eps);
+      int bn = 0;
+      if (lane == 0) bn = atomicAdd(&next_blk, 1);
+      bn = __builtin_amdgcn_readfirstlane(bn);
       QKOp<T, D> knext;
       {
-        const int tn = t0 + kDecGroup + li;
+        const int tn = n_lo + 32 * bn + li;
         load_op<D>(knext, Kh + (size_t)(tn < n_hi ? tn : n_hi - 1) * D, g);
       }
       f32x16 acc;
@@ -1587,6 +1604,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         }
       }
       kop = knext;
+      b = bn;
+      t0 = n_lo + 32 * b;
     }
     x = hb + n_hi;
   }
@@ -1646,7 +1665,7 @@ struct EncPlan {
 // Resident waves per compute unit the encode grid is sized for, and the
 // decode's workgroups per compute unit.
 constexpr int kEncWavesPerCu = 16;
-constexpr int kDecWgPerCu = 4;
+constexpr int kDecWgPerCu = 1;
 
 // bf16: one 32-latent block per wave, max(4, blocks) waves per workgroup.
 // f32: up to two latent blocks per wave, 4 waves per workgroup.
@@ -1698,7 +1717,8 @@ int launch_encode_dma(const EncArgs& a, hipStream_t st) {
 
 template <typename QT, int D, bool NK>
 int launch_encode_bf16_dk(const EncArgs& a, int NW, int WN, hipStream_t st) {
-  if (NW == 8) return launch_encode_dma<QT, D, 8, 1, NK>(a, st);
+  if (NW == 8 && WN == 1) return launch_encode_dma<QT, D, 8, 1, NK>(a, st);
+  if (NW != 4) return FLARE_ERR_UNSUPPORTED;  // no kernel for this split plan
   if (WN == 4) return launch_encode_dma<QT, D, 4, 4, NK>(a, st);
   if (WN == 2) return launch_encode_dma<QT, D, 4, 2, NK>(a, st);
   return launch_encode_dma<QT, D, 4, 1, NK>(a, st);
@@ -1773,7 +1793,7 @@ int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  return launch(decode_kernel<T, QT, D, TAIL, NK, ST, MBT>, dim3(a.nwg), dim3(kThreads), lds, st, a);
+  return launch(decode_kernel<T, QT, D, TAIL, NK, ST, MBT>, dim3(a.nwg), dim3(kDecThreads), lds, st, a);
 }
 
 // bf16 decode without a latent tail: 2, 4 or 8 latent blocks (M = 64, 128,

@@ -320,7 +320,8 @@ int launch_proj_k(const ProjArgs& pa, hipStream_t st) {
 
 template <typename QT, bool NK>
 int launch_proj_w(const ProjArgs& pa, int NW, int WN, hipStream_t st) {
-  if (NW == 8) return launch_proj_k<QT, 8, 1, NK>(pa, st);
+  if (NW == 8 && WN == 1) return launch_proj_k<QT, 8, 1, NK>(pa, st);
+  if (NW != 4) return FLARE_ERR_UNSUPPORTED;  // no kernel for this split plan
   if (WN == 4) return launch_proj_k<QT, 4, 4, NK>(pa, st);
   if (WN == 2) return launch_proj_k<QT, 4, 2, NK>(pa, st);
   return launch_proj_k<QT, 4, 1, NK>(pa, st);
