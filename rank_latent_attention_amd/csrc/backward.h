@@ -604,6 +604,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_fast_kernel(RowArgs a) {
   using RL = RowLds<D>;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float wred[2][NW];
+  __shared__ int next_blk;  // the next unclaimed 32-token block of the piece
   const int MB = a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   const int tst = RL::tst(MB);
   bf16* qs = reinterpret_cast<bf16*>(smem);
@@ -675,11 +676,20 @@ __global__ void __launch_bounds__(NW * 64) bwd_row_fast_kernel(RowArgs a) {
         }
       }
     }
+    // wave w starts with block w; the waves claim the rest as they finish one,
+    // so all of them run to the end of the piece (as in the decode)
+    if (threadIdx.x == 0) next_blk = NW;
     __syncthreads();
 
     const bf16* Kh = a.K + (size_t)bh * N * D;
     const bf16x8 sel = record_select(g, false);
-    for (int t0 = n_lo + 32 * wave; t0 < n_hi; t0 += 32 * NW) {
+    const int nblk = (n_hi - n_lo + 31) / 32;
+    int b = wave;
+    while (b < nblk) {
+      const int t0 = n_lo + 32 * b;
+      int bn = 0;
+      if (lane == 0) bn = atomicAdd(&next_blk, 1);
+      b = __builtin_amdgcn_readfirstlane(bn);  // the next block, claimed before this one's work
       // lanes past the piece recompute its last token and store the same values there
       const int n = t0 + li < n_hi ? t0 + li : n_hi - 1;
       QKOp<bf16, D> kop, yop, vop;
