@@ -651,6 +651,7 @@ struct EncArgs {
   const void* V;      // [B,H,N,D], type T (may equal K)
   float* part_acc;    // [nbh][pmax][M][D]
   float2* part_al;    // [nbh][pmax][M]   (shift in log2 units, sum)
+  float* part_km;     // [nbh][pmax] largest squared key norm of each split's keys, or null (bf16)
   long long total;    // nbh * N
   int q_batched, v_alias, H, N, M, G, nwg, pmax, bh0;
   float qscale;       // s * log2(e)
@@ -1077,6 +1078,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) kmax2 = fmaxf(kmax2, kred[w]);
+    if (a.part_km && threadIdx.x < WN)  // the same for each of the piece's WN splits
+      a.part_km[(size_t)bhl * a.pmax + slot - ng + threadIdx.x] = kmax2;
     // unshifted partial (see fast_ok), renormalised to a power-of-two shift
     // so that the merge never adds sums beyond the float range; or the exact
     // recomputation when the rounded queries could move a score too far.
@@ -1134,6 +1137,8 @@ struct MergeArgs {
   const void* Qf;     // [H,M,D] of type QT, blend mode only
   const float* gate;  // [H]
   float* Qout;        // [B,H,M,D], blend mode only
+  const float* part_km;  // the encode's per-split key-norm maxima, or null
+  float* kmax;           // [B H] per head: their maximum (global head index), or null
   long long total;
   int N, M, D, H, WN, nwg, pmax, bh0, nbh;
   int norm_qf;        // blend with N_0(Qf) instead of Qf
@@ -1190,10 +1195,17 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
   const int bhl = (int)(pair / (unsigned)a.M);
   const int bh = a.bh0 + bhl;
   MergeState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (a.N == 0 && a.kmax && m == 0 && lane == 0) a.kmax[bh] = 0.f;
   if (a.N > 0) {
     const long long hb = (long long)bhl * a.N;
     const int cnt = (piece_of(hb + a.N - 1, a.total, a.nwg) - piece_of(hb, a.total, a.nwg) + 1) * a.WN;
     const size_t base = (size_t)bhl * a.pmax;
+    if (a.kmax && m == 0) {  // the head's largest key norm, for the decode (every lane active)
+      float km = 0.f;
+      for (int p = lane; p < cnt; p += 64) km = fmaxf(km, a.part_km[base + p]);
+      km = wave_max(km);
+      if (lane == 0) a.kmax[bh] = km;
+    }
     // slots past cnt load nothing and count as empty
     for (int p0 = pg; p0 < cnt; p0 += kMergeBatch * PGW) {
       float2 v[kMergeBatch];
@@ -1268,6 +1280,7 @@ struct DecArgs {
   float qscale;
   const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
   float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
+  const float* kmax;  // [B H] largest squared key norm of each head (from its encode), or null
   // statistics mode (the kernel's ST flag, bf16): instead of Y, per token
   // one record of 8 bf16 (see split3_record): the negated log2 of the
   // weight sum over the latents and the negated dY . Y, each as three parts
@@ -1434,8 +1447,11 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     for (int w = 0; w < kDecWaves; ++w) { zmax = fmaxf(zmax, zred[w]); qerr2 = fmaxf(qerr2, qred[w]); }
     const float zlim = 1.329228e36f / fmaxf(zmax * 1.01f, 1.f);  // 2^120 / max|z|
     // a token block keeps the fast loop's result only if every score it
-    // forms is within kScoreErr of the exact one: |k_n|^2 <= klim2
+    // forms is within kScoreErr of the exact one: |k_n|^2 <= klim2.  When the
+    // head's encode found no key beyond that (with 1% for the rounding of
+    // keys normalised there and here), no block needs the check.
     const float klim2 = qerr2 > 0.f ? kScoreErr2 / qerr2 : INFINITY;
+    const bool kcheck = !(a.kmax && a.kmax[bh] * 1.01f <= klim2);
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
@@ -1516,7 +1532,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
         // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim;
         // the staged queries' rounding moves no score of a key with
         // |k|^2 <= klim2 by more than kScoreErr
-        const bool redo = !fast_ok(den) || den > zlim || row_norm2<D>(kop) > klim2;
+        const bool redo = !fast_ok(den) || den > zlim || (kcheck && row_norm2<D>(kop) > klim2);
         if (__builtin_amdgcn_ballot_w64(redo) != 0) {
           // careful redo of this token block: exact scores (the queries read
           // again and split into bf16 hi + lo) and the exact maximum of
@@ -1753,10 +1769,10 @@ int launch_encode_f32(const EncArgs& a, hipStream_t st) {
 // qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
 int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0, int H, int N,
                   int M, int D, int dtype, float qscale, float* part_acc, float2* part_al, const EncPlan& p,
-                  const Norms& nm, hipStream_t st) {
+                  const Norms& nm, hipStream_t st, float* part_km = nullptr) {
   EncArgs a;
   a.Q = Q; a.K = K; a.V = V;
-  a.part_acc = part_acc; a.part_al = part_al;
+  a.part_acc = part_acc; a.part_al = part_al; a.part_km = part_km;
   a.total = p.total;
   a.q_batched = q_batched; a.v_alias = (K == V); a.H = H; a.N = N; a.M = M;
   a.G = p.G; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0;
@@ -1774,9 +1790,11 @@ int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const 
 
 int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H, int N,
                  int M, int D, float* Z, float* L, const void* Qf, int qftype, const float* gate, float* Qout,
-                 int norm_qf, const float* zmul, float eps, hipStream_t st) {
+                 int norm_qf, const float* zmul, float eps, hipStream_t st, const float* part_km = nullptr,
+                 float* kmax = nullptr) {
   MergeArgs a;
   a.part_acc = part_acc; a.part_al = part_al;
+  a.part_km = part_km; a.kmax = part_km ? kmax : nullptr;
   a.Z = Z; a.L = L; a.Qf = Qf; a.gate = gate; a.Qout = Qout;
   a.norm_qf = norm_qf; a.zmul = zmul; a.eps = eps;
   a.total = p.total;
@@ -1833,9 +1851,10 @@ size_t decode_lds(int dtype, int D, int M) {
 // nm.norm_k: N_0 of the key rows; nm.qmul1: channel scale of the queries.
 int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const float* Z, void* Y,
                   int bh0, int nbh, int H, int N, int M, int D, int dtype, float qscale, const Norms& nm,
-                  hipStream_t st) {
+                  hipStream_t st, const float* kmax = nullptr) {
   if (N == 0) return FLARE_OK;
-  DecArgs a;
+  DecArgs a{};
+  a.kmax = kmax;
   a.Q = Q; a.K = K; a.Z = Z; a.Y = Y;
   a.total = (long long)nbh * N;
   a.q_batched = q_batched; a.H = H; a.N = N; a.M = M; a.MB = (int)cdiv(M, 32); a.bh0 = bh0;
@@ -1862,6 +1881,8 @@ float pick_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf
 // call needs internally.
 struct WsLayout {
   size_t part_acc = 0, part_al = 0, z = 0, l = 0, q = 0, k = 0, total = 0;
+  size_t km = 0, kh = 0;  // per-split and per-head key-norm maxima (bf16 forwards with a decode)
+  bool kmax = false;
 };
 
 WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, int dtype, bool need_z, bool need_q) {
@@ -1876,6 +1897,11 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
     w.part_acc = 0;
     w.part_al = acc;
     off = acc + al;
+    if (dtype == FLARE_BF16 && op != FLARE_OP_ENCODE) {  // the encode's key norms, for the decode
+      w.kmax = true;
+      w.km = off; off += align256((size_t)BH * p.pmax * sizeof(float));
+      w.kh = off; off += align256((size_t)BH * sizeof(float));
+    }
   }
   if (need_z) { w.z = off; off += align256((size_t)BH * M * D * sizeof(float)); w.l = off; off += align256((size_t)BH * M * sizeof(float)); }
   if (need_q) { w.q = off; off += align256((size_t)BH * M * D * sizeof(float)); }
@@ -2012,14 +2038,17 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
   float* pacc = (float*)(ws + w.part_acc);
   float2* pal = (float2*)(ws + w.part_al);
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
+  float* km = w.kmax ? (float*)(ws + w.km) : nullptr;
+  float* kh = w.kmax ? (float*)(ws + w.kh) : nullptr;
   int rc;
   if (N > 0) {
-    rc = launch_encode(Q, qtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st);
+    rc = launch_encode(Q, qtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st, km);
     if (rc) return rc;
   }
-  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st,
+                    km, kh);
   if (rc) return rc;
-  return launch_decode(dev, Q, qtype, q_batched, K, Z, Y, 0, BH, H, N, M, D, dtype, qs, nm, st);
+  return launch_decode(dev, Q, qtype, q_batched, K, Z, Y, 0, BH, H, N, M, D, dtype, qs, nm, st, kh);
 }
 
 // flare_forward with the workspace at ws (ws_bytes long), or, when ws_bytes
@@ -2130,17 +2159,20 @@ static int routing_proj(const Dev& dev, const void* X, const void* WK, const voi
   float* pacc = (float*)(ws + w.part_acc);
   float2* pal = (float2*)(ws + w.part_al);
   const EncPlan p = plan_encode(dev, BH, N, M, FLARE_BF16);
+  float* km = w.kmax ? (float*)(ws + w.km) : nullptr;
+  float* kh = w.kmax ? (float*)(ws + w.kh) : nullptr;
   int rc;
   if (N > 0) {
-    rc = launch_encode_proj(X, WK, WV, Kbuf, Q, qtype, q_batched, H, N, M, qs, pacc, pal, p, nm, st);
+    rc = launch_encode_proj(X, WK, WV, Kbuf, Q, qtype, q_batched, H, N, M, qs, pacc, pal, p, nm, st, km);
     if (rc) return rc;
   }
-  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st);
+  rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st,
+                    km, kh);
   if (rc) return rc;
   // the keys in Kbuf are already normalised: the decode only moves their scale onto the queries
   Norms dn;
   dn.qmul1 = nm.qmul1;
-  return launch_decode(dev, Q, qtype, q_batched, Kbuf, Z, Y, 0, BH, H, N, M, D, FLARE_BF16, qs, dn, st);
+  return launch_decode(dev, Q, qtype, q_batched, Kbuf, Z, Y, 0, BH, H, N, M, D, FLARE_BF16, qs, dn, st, kh);
 }
 
 static int check_proj(int B, int H, int N, int M, int D, int C, int dtype) {

@@ -246,6 +246,8 @@ encode_proj_kernel(ProjArgs pa) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) { kmax2 = fmaxf(kmax2, kred[w]); kerr2 = fmaxf(kerr2, ered[w]); }
+    if (a.part_km && threadIdx.x < WN)  // the norms of the stored keys, for the decode
+      a.part_km[(size_t)bhl * a.pmax + slot - ng + threadIdx.x] = kmax2;
     // The fast scores q~ . k~ use rounded queries and rounded projected keys:
     // |q~ . k~ - q . k| <= |q~ - q| |k| + |q| |k~ - k| + |q~ - q| |k~ - k|.
     // Normalised keys are the keys by definition (rounded like stored inputs).
@@ -332,11 +334,11 @@ int launch_proj_w(const ProjArgs& pa, int NW, int WN, hipStream_t st) {
 // projected keys are N_0-normalised in LDS, and written so when Kout is set).
 int launch_encode_proj(const void* X, const void* WK, const void* WV, bf16* Kout, const void* Q, int qtype,
                        int q_batched, int H, int N, int M, float qscale, float* part_acc, float2* part_al,
-                       const EncPlan& p, const Norms& nm, hipStream_t st) {
+                       const EncPlan& p, const Norms& nm, hipStream_t st, float* part_km = nullptr) {
   ProjArgs pa;
   EncArgs& a = pa.e;
   a.Q = Q; a.K = nullptr; a.V = nullptr;
-  a.part_acc = part_acc; a.part_al = part_al;
+  a.part_acc = part_acc; a.part_al = part_al; a.part_km = part_km;
   a.total = p.total;
   a.q_batched = q_batched; a.v_alias = WK == WV; a.H = H; a.N = N; a.M = M;
   a.G = p.G; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = 0;

@@ -347,6 +347,34 @@ def test_key_shift_leaves_latents(flare, orc, dtype):
     check("oracle Z of shifted keys vs Z", Zs, Zr, 1e-12)
 
 
+def test_head_key_bound_matches_per_block_checks(flare, orc):
+    """flare_forward hands the decode each head's largest key norm from the
+    encode, and the decode skips its per-block key-norm check for heads
+    where that bound already rules out a score error beyond the limit.  One
+    head here has a few keys 60 times longer than the others (its blocks with
+    them take the exact recomputation), the others none.  The forward's Y must
+    equal, bit for bit, the standalone decode's (which checks every block)
+    on the forward's own Z, and match the oracle."""
+    import torch
+    from rank_latent_attention_amd.inputs import make_gaussian
+    w = make_gaussian(1, 3, 5000, 64, 32, "bf16", seed=41)
+    rng = np.random.default_rng(42)
+    big = rng.choice(5000, size=5, replace=False)
+    K = w.K.astype(np.float32).copy()
+    K[0, 1, big] *= 60.0
+    w.K = dev(K, "bf16").float().cpu().numpy()  # both sides take the bf16-rounded keys
+    Q, Kd, V = dev(w.Q, "bf16"), dev(w.K, "bf16"), dev(w.V, "bf16")
+    Z = torch.empty((1, 3, 64, 32), dtype=torch.float32, device=Kd.device)
+    L = torch.empty((1, 3, 64), dtype=torch.float32, device=Kd.device)
+    Y, _, _ = flare.flare_forward(Q, Kd, V, Z=Z, L=L)
+    Yd = flare.flare_decode(Q, Kd, Z)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yd), "forward and standalone decode differ"
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    check("Y", host(Y), Yr, TOL["bf16"])
+    check("Z", host(Z), Zr, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_query_shift_leaves_decode(flare, orc, dtype):
     """Q -> Q + 1 c^T adds k_n . c to every decode score of token n, which the
