@@ -17,16 +17,22 @@
 //                     workgroup of 8 waves; 128-token K / V tiles arrive by
 //                     LDS DMA one tile ahead, each wave owns 32 latents, and
 //                     S^T = K Q^T and Z^T += V^T P^T run on MFMA.  A split
-//                     emits (shift, sum, accumulator).
+//                     emits (shift, sum, accumulator) and its keys' largest
+//                     squared norm.
 //   encode_kernel  -- the same for float32 inputs, register-staged tiles.
 //   merge_kernel   -- log-sum-exp merge of the splits in a fixed order
 //                     (Sec. 3.3, App. B.3); optionally the FLARE++ blend.
-//   decode_kernel  -- per-token softmax over the latents: the scaled queries
-//                     and the latents stay in LDS for a head, every wave takes
-//                     32 tokens per step, S = Q K^T and Y^T += Z^T P run on
-//                     MFMA with one lane per token column.
-// backward.h holds the reverse-mode kernels and their entry points, backward32.h
-// the float32 ones.
+//   decode_kernel  -- per-token softmax over the latents: one 16-wave
+//                     workgroup per compute unit keeps a head's scaled
+//                     queries and latents in LDS, its waves claim 32-token
+//                     blocks from an LDS counter, and S = Q K^T and
+//                     Y^T += Z^T P run on MFMA with one lane per token column.
+// proj.h holds the encode from the block input (K = X W_K, V = X W_V formed
+// per tile), backward.h the reverse-mode kernels and their entry points,
+// backward32.h the float32 ones.
+// The bf16 paths bound the score error that the rounding of the pre-scaled
+// queries can cause, per unit of work, and recompute exactly (queries split
+// into bf16 hi + lo) where the bound exceeds kScoreErr.
 // Scores are kept in log2 units: the queries are pre-multiplied by
 // s*log2(e) so every exponential is a single v_exp_f32.  The bf16 loops use
 // no shift at all (weights exp2(score), checked for range afterwards, with an
