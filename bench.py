@@ -210,10 +210,17 @@ def time_configs(names: str, with_oracle: bool = False) -> None:
         torch.cuda.synchronize()
         t = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))
         med = t[n // 2]
+        # algorithmic HBM bytes of the forward: the encode reads K and V, the
+        # decode reads K and writes Y (FLARE++ also reads the synthesis keys,
+        # and their values when separate); queries and latents are negligible
+        tok = B * H * N * D * K.element_size()
+        hbm = 4 * tok + ((1 if w.shared_vs else 2) * tok if w.pp else 0)
         rec = {"workload": w.name, "B": B, "H": H, "N": N, "M": M, "D": D, "dtype": w.dtype,
                "flare_pp": bool(w.pp), "us_median": round(med, 1), "us_min": round(t[0], 1),
                "us_max": round(t[-1], 1), "tokens_per_s": B * N / (med * 1e-6),
-               "tflops": round(flops / (med * 1e-6) / 1e12, 1)}
+               "tflops": round(flops / (med * 1e-6) / 1e12, 1),
+               "mfma_frac": round(flops / (med * 1e-6) / 1e12 / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else 157.3), 4),
+               "algorithmic_bytes": hbm, "hbm_frac": round(hbm / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         # Working sets under the 256 MB last-level cache stay resident between
         # back-to-back calls; the cold variant writes a 512 MB buffer before
         # every timed call so the inputs come from HBM.
@@ -228,6 +235,7 @@ def time_configs(names: str, with_oracle: bool = False) -> None:
             torch.cuda.synchronize()
             tc = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))
             rec["us_median_cold"] = round(tc[n // 2], 1)
+            rec["hbm_frac_cold"] = round(hbm / (tc[n // 2] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
             del flush
         if with_oracle and w.N * w.B * w.H * w.M <= (1 << 30):  # the million-token runs stay with the bench line
             rec.update(oracle_times(w))
