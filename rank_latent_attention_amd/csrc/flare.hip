@@ -518,10 +518,10 @@ template <int D> __device__ inline int tile_off(int n, int d) { return chunk_pos
 // Issue the DMA of rows [t0, t0 + dma_rows<NW>()) of a [*, D] bf16 matrix into a
 // swizzled tile.  Rows at or beyond n_hi repeat row n_hi - 1 (they are masked
 // out of the softmax by the caller), so no read leaves the matrix.
-template <int D, int NW>
+template <int D, int NW, int ROWS = dma_rows<NW>()>
 __device__ inline void dma_tile(bf16* tile, const bf16* src, int t0, int n_hi, int wave, int lane) {
   constexpr int CPR = D / 8;
-  constexpr int INSTR = dma_rows<NW>() * CPR / 64;  // 64 chunks (1 KB) per wave instruction
+  constexpr int INSTR = ROWS * CPR / 64;  // 64 chunks (1 KB) per wave instruction
 #pragma unroll
   for (int i = wave; i < INSTR; i += NW) {
     const int P = i * 64 + lane;
@@ -541,9 +541,10 @@ __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memor
 // 16-byte chunk per pass; the D / 8 chunks of a row sit in consecutive lanes
 // and add their partial sums with xor shuffles.  Rows past the piece repeat a
 // valid row, so every row holds finite values.
-template <int D, int NW> __device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
+template <int D, int NW, int ROWS = dma_rows<NW>()>
+__device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
   constexpr int CPR = D / 8;
-  constexpr int CH = dma_rows<NW>() * CPR;
+  constexpr int CH = ROWS * CPR;
 #pragma unroll
   for (int P0 = 0; P0 < CH; P0 += NW * 64) {
     const int P = P0 + wave * 64 + lane;
@@ -570,12 +571,12 @@ template <int D, int NW> __device__ inline void norm_tile(bf16* tile, int wave, 
 // piece repeat its last row, so they add no key from outside it.
 // With dst given, the tile's rows below nvalid are also copied to dst (row
 // n at dst + n D, 16-byte chunks, coalesced).
-template <int D, int NW>
+template <int D, int NW, int ROWS = dma_rows<NW>()>
 __device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float m, bf16* dst = nullptr,
                                      int nvalid = 0) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   constexpr int CPR = D / 8;
-  constexpr int CH = dma_rows<NW>() * CPR;  // a multiple of 64
+  constexpr int CH = ROWS * CPR;  // a multiple of 64
   for (int P0 = wave * 64; P0 < CH; P0 += NW * 64) {
     const int P = P0 + lane;
     const bf16x8 v = reinterpret_cast<const bf16x8*>(tile)[chunk_pos<D>(P / CPR, P % CPR)];
@@ -904,14 +905,15 @@ __device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned
   }
 }
 
-// The dma_rows<NW>()-token tile at t0 for one wave: token blocks ng, ng + WN,
-// ... (the per-wave offset ng * 64 * D is already folded into ka / va, and t0
-// here is the wave's first row).
-template <int D, int NW, int WN, int BO>
+// The ROWS-token tile at t0 for one wave: token blocks ng, ng + WN, ... (the
+// per-wave offset ng * 64 * D is already folded into ka / va, and t0 here is
+// the wave's first row).
+template <int D, int NW, int WN, int BO, int ROWS = dma_rows<NW>()>
 __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
                                    int lane, const QKOp<bf16, D>& qop, RowSum<D>& lsum, f32x16& acc) {
   if (t0 >= n_hi) return;
-  constexpr int NBLK = dma_rows<NW>() / 32 / WN;
+  constexpr int NBLK = ROWS / 32 / WN;
+  static_assert(NBLK >= 1, "a tile holds at least one token block per wave");
   encode_chain<D, WN, BO, 0, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, enc_scores<D, 0, BO>(ka, qop));
 }
 
@@ -971,13 +973,18 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
 // owns latent block w % G (32 latents) and token blocks w / G + k WN of every
 // ROWS-token tile.  Tiles are double-buffered in two distinct LDS arrays: the
 // DMA of the next tile is in flight while the current one is consumed.
-template <typename QT, int D, int NW, int WN, bool NK>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
-  constexpr int ROWS = dma_rows<NW>();
+// Piece `piece` of a.nwg (the workgroup's); tiles: 4 ROWS D bf16 of LDS
+// ([buffer][K, V]), kred: NW floats of LDS (per-wave largest squared key norm
+// of a piece).  With LP the workgroup's piece is one whole head and its split
+// partials go to LDS, lacc [WN][M][D] and lal [WN][M] (split = token lane),
+// and a.part_km, when set, receives the head's largest squared key norm at
+// the head's index.
+template <typename QT, int D, int NW, int WN, bool NK, int ROWS = dma_rows<NW>(), bool LP = false>
+__device__ __attribute__((always_inline)) inline void encode_dma_body(const EncArgs& a, int piece, bf16* tiles,
+                                                                      float* kred, float* lacc = nullptr,
+                                                                      float2* lal = nullptr) {
   constexpr int TE = ROWS * D;  // elements per tile
   constexpr int G = NW / WN;
-  __shared__ __align__(16) bf16 tiles[4 * TE];  // [buffer][K, V][TE]
-  __shared__ float kred[NW];                     // per-wave largest squared key norm of a piece
   bf16* const k0 = tiles;
   bf16* const v0 = tiles + TE;
   bf16* const k1 = tiles + 2 * TE;
@@ -1003,8 +1010,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     for (int k = 0; k < 4; ++k) va[k] = bv + to.vq[k];
   }
 
-  long long x = piece_start(blockIdx.x, a.total, a.nwg);
-  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  long long x = piece_start(piece, a.total, a.nwg);
+  const long long xe = piece_start(piece + 1, a.total, a.nwg);
   while (x < xe) {
     const int bhl = (int)(x / N);
     const long long hb = (long long)bhl * N;
@@ -1012,7 +1019,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const int n_hi = (int)((xe < hb + N ? xe : hb + N) - hb);
     const int bh = a.bh0 + bhl;
     const int h = bh % a.H;
-    const int slot = (blockIdx.x - piece_of(hb, a.total, a.nwg)) * WN + ng;
+    const int slot = (piece - piece_of(hb, a.total, a.nwg)) * WN + ng;
 
     // this lane's latent query row (rows past M repeat row M - 1 and are zeroed)
     auto qrow = [&]() {
@@ -1036,43 +1043,43 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + (size_t)bh * N * D;
     const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + (size_t)bh * N * D;
     __syncthreads();  // the previous piece is done with the tiles
-    dma_tile<D, NW>(k0, Kh, n_lo, n_hi, wave, lane);
-    if (!alias) dma_tile<D, NW>(v0, Vh, n_lo, n_hi, wave, lane);
+    dma_tile<D, NW, ROWS>(k0, Kh, n_lo, n_hi, wave, lane);
+    if (!alias) dma_tile<D, NW, ROWS>(v0, Vh, n_lo, n_hi, wave, lane);
     wait_dma();
     __syncthreads();
     if constexpr (NK) {  // key rows N_0 in place (and the values with them when they alias)
-      norm_tile<D, NW>(k0, wave, lane, a.eps);
+      norm_tile<D, NW, ROWS>(k0, wave, lane, a.eps);
       __syncthreads();
     }
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * ROWS) {
       // tile t0 from buffer 0 while tile t0 + ROWS streams into buffer 1
       const int tn = t0 + ROWS;
-      kmax2 = tile_key_max<D, NW>(k0, wave, lane, kmax2);
+      kmax2 = tile_key_max<D, NW, ROWS>(k0, wave, lane, kmax2);
       if (tn < n_hi) {
-        dma_tile<D, NW>(k1, Kh, tn, n_hi, wave, lane);
-        if (!alias) dma_tile<D, NW>(v1, Vh, tn, n_hi, wave, lane);
+        dma_tile<D, NW, ROWS>(k1, Kh, tn, n_hi, wave, lane);
+        if (!alias) dma_tile<D, NW, ROWS>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 0>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      encode_tile<D, NW, WN, 0, ROWS>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
       if constexpr (NK) {
-        norm_tile<D, NW>(k1, wave, lane, a.eps);
+        norm_tile<D, NW, ROWS>(k1, wave, lane, a.eps);
         __syncthreads();
       }
       // tile tn from buffer 1 while tn + ROWS streams into buffer 0
       const int tn2 = tn + ROWS;
-      kmax2 = tile_key_max<D, NW>(k1, wave, lane, kmax2);
+      kmax2 = tile_key_max<D, NW, ROWS>(k1, wave, lane, kmax2);
       if (tn2 < n_hi) {
-        dma_tile<D, NW>(k0, Kh, tn2, n_hi, wave, lane);
-        if (!alias) dma_tile<D, NW>(v0, Vh, tn2, n_hi, wave, lane);
+        dma_tile<D, NW, ROWS>(k0, Kh, tn2, n_hi, wave, lane);
+        if (!alias) dma_tile<D, NW, ROWS>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 2 * TE * 2>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      encode_tile<D, NW, WN, 2 * TE * 2, ROWS>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       wait_dma();
       __syncthreads();
       if constexpr (NK) {
         if (tn2 < n_hi) {
-          norm_tile<D, NW>(k0, wave, lane, a.eps);
+          norm_tile<D, NW, ROWS>(k0, wave, lane, a.eps);
           __syncthreads();
         }
       }
@@ -1084,8 +1091,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) kmax2 = fmaxf(kmax2, kred[w]);
-    if (a.part_km && threadIdx.x < WN)  // the same for each of the piece's WN splits
-      a.part_km[(size_t)bhl * a.pmax + slot - ng + threadIdx.x] = kmax2;
+    if constexpr (LP) {
+      if (a.part_km && threadIdx.x == 0) a.part_km[bh] = kmax2;
+    } else {
+      if (a.part_km && threadIdx.x < WN)  // the same for each of the piece's WN splits
+        a.part_km[(size_t)bhl * a.pmax + slot - ng + threadIdx.x] = kmax2;
+    }
     // unshifted partial (see fast_ok), renormalised to a power-of-two shift
     // so that the merge never adds sums beyond the float range; or the exact
     // recomputation when the rounded queries could move a score too far.
@@ -1113,8 +1124,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
       shift = (float)e;
     }
     if (m2 < M) {
-      const size_t p = (size_t)bhl * a.pmax + slot;
-      float* dst = a.part_acc + (p * M + m2) * D;
+      const size_t p = LP ? (size_t)slot : (size_t)bhl * a.pmax + slot;
+      float* dst = (LP ? lacc : a.part_acc) + (p * M + m2) * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (8 * c + 4 * g2 < D) {
@@ -1122,10 +1133,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
           *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g2) = v;
         }
       }
-      if (g2 == 0) a.part_al[p * M + m2] = make_float2(shift, ltot);
+      if (g2 == 0) (LP ? lal : a.part_al)[p * M + m2] = make_float2(shift, ltot);
     }
     x = hb + n_hi;
   }
+}
+
+template <typename QT, int D, int NW, int WN, bool NK>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
+  __shared__ __align__(16) bf16 tiles[4 * dma_rows<NW>() * D];
+  __shared__ float kred[NW];
+  encode_dma_body<QT, D, NW, WN, NK>(a, blockIdx.x, tiles, kred);
 }
 
 // ----------------------------------------------------------------------------
@@ -1336,16 +1354,17 @@ template <typename T, int D> struct DecLds {
 // run to the end of the piece together: with several workgroups per compute
 // unit the oldest ones are issued first, finish early and leave the last to
 // run alone at one wave per SIMD.
+// Piece `piece` of a.nwg (the workgroup's); smem: DecLds<T, D>::bytes(MB) of LDS, zred and
+// qred: kDecWaves floats of LDS each, next_blk: one int of LDS (the next
+// unclaimed 32-token block of the piece).
 template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
-__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
+__device__ __attribute__((always_inline)) inline void decode_body(const DecArgs& a, int piece, unsigned char* smem,
+                                                                  float* zred, float* qred, int& next_blk) {
   static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
   using L = DecLds<T, D>;
-  extern __shared__ __align__(16) unsigned char smem[];
   const int MB = MBT > 0 ? MBT : a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
   T* zt = qs + (size_t)Mp * L::QST;
-  __shared__ float zred[kDecWaves], qred[kDecWaves];
-  __shared__ int next_blk;  // the next unclaimed 32-token block of the piece
   const int zst = (int)L::zst(MB);
   // the wave index is uniform: kept in a scalar register, block guards derived
   // from it become scalar branches
@@ -1354,8 +1373,8 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
   constexpr bool mask_tail = TAIL;
   __builtin_assume(MB >= 1);
 
-  long long x = piece_start(blockIdx.x, a.total, a.nwg);
-  const long long xe = piece_start(blockIdx.x + 1, a.total, a.nwg);
+  long long x = piece_start(piece, a.total, a.nwg);
+  const long long xe = piece_start(piece + 1, a.total, a.nwg);
   while (x < xe) {
     const int bhl = (int)(x / N);
     const long long hb = (long long)bhl * N;
@@ -1633,6 +1652,116 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
   }
 }
 
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
+__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float zred[kDecWaves], qred[kDecWaves];
+  __shared__ int next_blk;
+  decode_body<T, QT, D, TAIL, NK, ST, MBT>(a, blockIdx.x, smem, zred, qred, next_blk);
+}
+
+// ----------------------------------------------------------------------------
+// FLARE++ forward with one workgroup per head
+// ----------------------------------------------------------------------------
+// With many heads of a few thousand tokens, the five launches of the FLARE++
+// forward (synthesis encode, blended merge, routing encode, merge, decode)
+// spend much of their time filling and draining the chip between steps.  Here
+// one workgroup of kHeadWaves waves takes a whole head through the five steps,
+// with workgroup barriers in place of the kernel boundaries: the head is one
+// piece of WN splits (one per token lane of waves), whose partials stay in
+// LDS and are merged there by the whole workgroup; the blended queries and
+// the latents pass through their buffers to the next step.  The encodes and
+// the decode run the device code of their own kernels.
+constexpr int kHeadWaves = 16;
+static_assert(kHeadWaves == kDecWaves, "the decode step runs with the decode's wave count");
+
+struct HeadArgs {
+  EncArgs se, re;      // synthesis encode (bf16 seeds), routing encode (float32 blended queries)
+  DecArgs d;           // decode
+  const bf16* Qf;      // [H,M,D] fixed queries of the blend
+  const float* gate;   // [H]
+  float* Qout;         // [B,H,M,D] blended queries (the routing queries)
+  float* Z;            // [B,H,M,D]
+  float* L;            // [B,H,M]
+  int H;
+};
+
+// Token lanes (splits) of the encode steps for MB latent blocks, the tile rows
+// that give each of them one 32-token block per tile, and the dynamic LDS:
+// the encode's tiles (later the decode's staged queries and latents), then
+// the split partials [WN][M][D] and their (shift, sum) [WN][M].
+template <int MB> constexpr int head_wn() { return kHeadWaves / MB; }
+template <int MB> constexpr int head_rows() { return 32 * head_wn<MB>() > 128 ? 32 * head_wn<MB>() : 128; }
+template <int MB> constexpr size_t head_tile_bytes() { return (size_t)4 * head_rows<MB>() * 32 * sizeof(bf16); }
+template <int MB> constexpr size_t head_lds() {
+  return head_tile_bytes<MB>() + (size_t)head_wn<MB>() * 32 * MB * (32 * sizeof(float) + sizeof(float2));
+}
+
+// The merge of one head's split partials from LDS (lacc [WN][M][D], lal
+// [WN][M]) for latent m, features 4 c .. 4 c + 3: the splits are folded in
+// ascending order as in merge_kernel.  Returns Z's four features and sets L.
+template <int WN, int D>
+__device__ inline f32x4 merge_lds(const float* lacc, const float2* lal, int M, int m, int c, float& lse) {
+  MergeState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int p = 0; p < WN; ++p) {
+    const float2 al = lal[p * M + m];
+    st = merge_fold(st, al.x, al.y, reinterpret_cast<const f32x4*>(lacc + ((size_t)p * M + m) * D)[c]);
+  }
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  lse = -INFINITY;
+  if (st.A > -INFINITY) {
+    z = st.num / st.den;
+    lse = kLn2 * (st.A + __builtin_amdgcn_logf(st.den));
+  }
+  return z;
+}
+
+// D = 32, MB latent blocks (M = 32 MB), bf16 keys and values; one head per
+// workgroup (blockIdx.x = head); dynamic LDS of head_lds<MB>() bytes.  Thread
+// t merges latent t / 8, features 4 (t % 8) .. + 3.
+template <int MB>
+__global__ void __launch_bounds__(kHeadWaves * 64) pp_head_kernel(HeadArgs a) {
+  constexpr int D = 32, M = 32 * MB, WN = head_wn<MB>(), ROWS = head_rows<MB>();
+  static_assert(M * D / 4 <= kHeadWaves * 64, "one latent chunk per thread");
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float red[2 * kHeadWaves];
+  __shared__ int next_blk;
+  bf16* const tiles = reinterpret_cast<bf16*>(smem);
+  float* const lacc = reinterpret_cast<float*>(smem + head_tile_bytes<MB>());
+  float2* const lal = reinterpret_cast<float2*>(lacc + WN * M * D);
+  const int bh = blockIdx.x, h = bh % a.H;
+  const int m = threadIdx.x / (D / 4), c = threadIdx.x % (D / 4);
+  const bool mine = m < M;
+  const size_t o = ((size_t)bh * M + m) * D + 4 * c;
+
+  encode_dma_body<bf16, D, kHeadWaves, WN, false, ROWS, true>(a.se, bh, tiles, red, lacc, lal);
+  float qf[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mine) {
+    const bf16* q = a.Qf + ((size_t)h * M + m) * D + 4 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = (float)q[i];
+  }
+  const float g = a.gate[h];
+  __syncthreads();  // the synthesis partials are in LDS
+  if (mine) {
+    float lse;
+    const f32x4 z = merge_lds<WN, D>(lacc, lal, M, m, c, lse);
+    *reinterpret_cast<f32x4*>(a.Qout + o) = f32x4{qf[0] + g * z[0], qf[1] + g * z[1], qf[2] + g * z[2], qf[3] + g * z[3]};
+  }
+  __syncthreads();  // the blended queries are written, the partials read
+  encode_dma_body<float, D, kHeadWaves, WN, false, ROWS, true>(a.re, bh, tiles, red, lacc, lal);
+  __syncthreads();
+  if (mine) {
+    float lse;
+    const f32x4 z = merge_lds<WN, D>(lacc, lal, M, m, c, lse);
+    *reinterpret_cast<f32x4*>(a.Z + o) = z;
+    if (c == 0) a.L[(size_t)bh * M + m] = lse;
+  }
+  __syncthreads();  // Z is written
+  decode_body<bf16, float, D, false, false, false, MB>(a.d, bh, smem, red, red + kHeadWaves, next_blk);
+}
+
 // ----------------------------------------------------------------------------
 // Host side: planning, validation, launches
 // ----------------------------------------------------------------------------
@@ -1772,10 +1901,9 @@ int launch_encode_f32(const EncArgs& a, hipStream_t st) {
   return launch(encode_kernel<float, float, D, MBW>, dim3(a.nwg), dim3(kThreads), lds, st, a);
 }
 
-// qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
-int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0, int H, int N,
-                  int M, int D, int dtype, float qscale, float* part_acc, float2* part_al, const EncPlan& p,
-                  const Norms& nm, hipStream_t st, float* part_km = nullptr) {
+EncArgs encode_args(const void* Q, int q_batched, const void* K, const void* V, int bh0, int H, int N, int M,
+                    float qscale, float* part_acc, float2* part_al, const EncPlan& p, const Norms& nm,
+                    float* part_km) {
   EncArgs a;
   a.Q = Q; a.K = K; a.V = V;
   a.part_acc = part_acc; a.part_al = part_al; a.part_km = part_km;
@@ -1784,6 +1912,14 @@ int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const 
   a.G = p.G; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0;
   a.qscale = qscale;
   a.norm_q = nm.norm_q; a.qmul0 = nm.qmul0; a.qmul1 = nm.qmul1; a.eps = nm.eps;
+  return a;
+}
+
+// qtype: element type of Q (FLARE_F32 or FLARE_BF16); dtype: of K and V.
+int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const void* V, int bh0, int H, int N,
+                  int M, int D, int dtype, float qscale, float* part_acc, float2* part_al, const EncPlan& p,
+                  const Norms& nm, hipStream_t st, float* part_km = nullptr) {
+  const EncArgs a = encode_args(Q, q_batched, K, V, bh0, H, N, M, qscale, part_acc, part_al, p, nm, part_km);
   if (dtype == FLARE_BF16) {
     if (qtype == FLARE_BF16) return launch_encode_bf16<bf16>(a, D, p.NW, p.WN, nm.norm_k, st);
     return launch_encode_bf16<float>(a, D, p.NW, p.WN, nm.norm_k, st);
@@ -1794,10 +1930,9 @@ int launch_encode(const void* Q, int qtype, int q_batched, const void* K, const 
   return p.MBW == 2 ? launch_encode_f32<32, 2>(a, st) : launch_encode_f32<32, 1>(a, st);
 }
 
-int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H, int N,
-                 int M, int D, float* Z, float* L, const void* Qf, int qftype, const float* gate, float* Qout,
-                 int norm_qf, const float* zmul, float eps, hipStream_t st, const float* part_km = nullptr,
-                 float* kmax = nullptr) {
+MergeArgs merge_args(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H,
+                     int N, int M, int D, float* Z, float* L, const void* Qf, const float* gate, float* Qout,
+                     int norm_qf, const float* zmul, float eps, const float* part_km, float* kmax) {
   MergeArgs a;
   a.part_acc = part_acc; a.part_al = part_al;
   a.part_km = part_km; a.kmax = part_km ? kmax : nullptr;
@@ -1805,6 +1940,15 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   a.norm_qf = norm_qf; a.zmul = zmul; a.eps = eps;
   a.total = p.total;
   a.N = N; a.M = M; a.D = D; a.H = H; a.WN = p.WN; a.nwg = p.nwg; a.pmax = p.pmax; a.bh0 = bh0; a.nbh = nbh;
+  return a;
+}
+
+int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al, int bh0, int nbh, int H, int N,
+                 int M, int D, float* Z, float* L, const void* Qf, int qftype, const float* gate, float* Qout,
+                 int norm_qf, const float* zmul, float eps, hipStream_t st, const float* part_km = nullptr,
+                 float* kmax = nullptr) {
+  const MergeArgs a = merge_args(p, part_acc, part_al, bh0, nbh, H, N, M, D, Z, L, Qf, gate, Qout, norm_qf, zmul,
+                                 eps, part_km, kmax);
   const dim3 grid((unsigned)cdiv((long long)nbh * M, kThreads / 64));
   if (qftype == FLARE_BF16) return launch(merge_kernel<bf16>, grid, dim3(kThreads), 0, st, a);
   return launch(merge_kernel<float>, grid, dim3(kThreads), 0, st, a);
@@ -1917,6 +2061,58 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
   }
   w.total = off;
   return w;
+}
+
+// The one-workgroup-per-head FLARE++ forward (pp_head_kernel) serves bf16,
+// D = 32 and M = 64 or 128 without normalisations, when the heads alone
+// occupy at least half of the compute units and each is short: there the
+// split of a head across workgroups gains less than the four kernel
+// boundaries cost.  (Two workgroups per head, both encoding all of its tokens
+// and each decoding half, were no faster at a quarter to half of the compute
+// units: the doubled key and value reads slowed both encodes by what the
+// halved decode saved.)
+constexpr int kHeadMaxN = 8192;
+
+bool pp_head_applies(const Dev& dev, int BH, int N, int M, int D, int dtype, int norm_flags, const WsLayout& w) {
+  if (dtype != FLARE_BF16 || D != 32 || norm_flags || (M != 64 && M != 128)) return false;
+  if (N < 1 || N > kHeadMaxN || 2 * (long long)BH < dev.cus || !w.kmax) return false;
+  return (M == 64 ? head_lds<2>() : head_lds<4>()) + 1024 <= dev.lds_max;
+}
+
+template <int MB>
+int launch_head(const HeadArgs& a, int BH, hipStream_t st) {
+  static_assert(head_tile_bytes<MB>() >= (size_t)(MB * 32 * (32 + 8) + 32 * (MB * 32 + 4)) * sizeof(bf16),
+                "the decode's staging fits in the encode's tiles");
+  const size_t lds = head_lds<MB>();
+  if (lds > 65536 && hipFuncSetAttribute((const void*)pp_head_kernel<MB>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return FLARE_ERR_HIP;
+  return launch(pp_head_kernel<MB>, dim3(BH), dim3(kHeadWaves * 64), lds, st, a);
+}
+
+// FLARE++ forward of B H heads of N tokens (pp_head_applies holds): Qb, Z, L
+// and Y as the launch sequence writes them; kh: [B H] floats of workspace
+// (the heads' largest squared routing-key norms).
+int launch_pp_head(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate, const void* K,
+                   const void* V, void* Y, float* Qb, float* Z, float* L, int B, int H, int N, int M, float qs,
+                   float* kh, hipStream_t st) {
+  const int BH = B * H;
+  EncPlan p{};
+  p.G = M / 32;
+  p.WN = kHeadWaves / p.G;
+  p.nwg = BH;  // piece i is head i
+  p.total = (long long)BH * N;
+  p.pmax = p.WN;
+  HeadArgs a;
+  a.se = encode_args(Qs, 0, Ks, Vs, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, nullptr);
+  a.re = encode_args(Qb, 1, K, V, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, kh);
+  a.d = DecArgs{};
+  a.d.Q = Qb; a.d.K = K; a.d.Z = Z; a.d.Y = Y; a.d.kmax = kh;
+  a.d.total = p.total;
+  a.d.q_batched = 1; a.d.H = H; a.d.N = N; a.d.M = M; a.d.MB = M / 32; a.d.nwg = BH; a.d.bh0 = 0;
+  a.d.qscale = qs;
+  a.Qf = (const bf16*)Qf; a.gate = gate; a.Qout = Qb; a.Z = Z; a.L = L; a.H = H;
+  return M == 64 ? launch_head<2>(a, BH, st) : launch_head<4>(a, BH, st);
 }
 
 }  // namespace
@@ -2141,8 +2337,10 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
   rt.norm_k = norm_flags & FLARE_NORM_K;
   rt.qmul1 = rt.norm_k ? alpha_k : nullptr;
   rt.eps = eps;
-  // Synthesis encode over all heads, merged straight into the blended queries.
+  if (pp_head_applies(dev, BH, N, M, D, dtype, norm_flags, w))  // many short heads: one workgroup each
+    return launch_pp_head(Qs, Ks, Vs, Qf, gate, K, V, Y, Qb, Z, L, B, H, N, M, qs, (float*)(wsc + w.kh), st);
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
+  // Synthesis encode over all heads, merged straight into the blended queries.
   float* pacc = (float*)(wsc + w.part_acc);
   float2* pal = (float2*)(wsc + w.part_al);
   if (N > 0) {

@@ -55,11 +55,14 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     low 16 bits of the float32 pattern are rounded away (RNE on the 16th bit).
     Inputs must be finite.
     """
-    f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
+    f = np.array(x, dtype=np.float32, order="C", copy=True)
+    u = f.view(np.uint32)
     lsb = (u >> 16) & 1
-    u = ((u + 0x7FFF + lsb) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32)
+    # finite patterns are at most 0xFF7FFFFF: adding 0x8000 stays below 2^32
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return f
 
 
 def to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:

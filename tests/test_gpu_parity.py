@@ -202,6 +202,59 @@ def test_pp_shapes_and_unshared_values(flare, orc, dtype):
         check("Y", Y, Yr, TOL[dtype])
 
 
+def _head_batch(H, fill):
+    """A batch size for the FLARE++ forward that runs each head in its own
+    workgroup (D = 32, M = 64 or 128, bf16, up to 8192 tokens per head) once
+    B H reaches half of the compute units: "half" gives B H = half of them,
+    "more" one step of H past that, and "quarter" a quarter of them (the
+    launch sequence, for comparison)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if fill == "quarter":
+        return -(-cus // (4 * H))
+    if fill == "half":
+        return -(-cus // (2 * H))
+    return -(-cus // (2 * H)) + 1
+
+
+@pytest.mark.parametrize("N,M,H,share,mult,fill", [
+    (1, 64, 4, True, 1.0, "half"),        # one token per head
+    (100, 64, 4, False, 1.0, "more"),     # less than one tile, unshared synthesis values
+    (1000, 128, 2, True, 1.0, "half"),
+    (4097, 128, 4, False, 1.0, "more"),   # one token past 16 tiles
+    (8192, 64, 8, True, 1.0, "half"),     # the longest heads it takes
+    (3000, 64, 4, False, 1.0, "quarter"), # below half of the compute units: the launch sequence
+    (3000, 64, 4, True, 8.0, "half"),     # keys x8: exact-score redo in both encodes and the decode
+    (2500, 64, 4, False, 8.0, "more"),
+])
+def test_pp_one_workgroup_per_head(flare, orc, N, M, H, share, mult, fill):
+    from rank_latent_attention_amd.inputs import make_gaussian_pp, to_dtype
+    B = _head_batch(H, fill)
+    w = make_gaussian_pp(B, H, N, M, 32, dtype="bf16", seed=31 + N, share_vs=share)
+    if mult != 1.0:
+        w.Ks = to_dtype(w.Ks.astype(np.float64) * mult, "bf16")
+        w.Vs = w.Ks if share else w.Vs
+        w.K = to_dtype(w.K.astype(np.float64) * mult, "bf16")
+    say(f"[pp per head] B{B} H{H} N{N} M{M} D32 bf16 shared={share} keys x{mult:g} ({fill})")
+    Y, Qo, Z, L = run_pp(flare, w)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Z)) and np.all(np.isfinite(L))
+    tol = TOL["bf16"]
+    Yr, Qr, Zr, Lr = orc.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+    check("Q", Qo, Qr, tol)
+    if mult == 1.0:
+        check("Z", Z, Zr, tol)
+        check_lse("L", L, Lr, tol)
+        check("Y", Y, Yr, tol)
+    # The routing half against the oracle at the queries this call formed:
+    # with scores of a hundred or more, the synthesis's bf16 rounding of the
+    # queries (rel. about 1e-3) alone moves L by more than its bar.
+    say("  routing from the formed queries:")
+    Yq, Zq, Lq = orc.flare_forward(Qo, w.K, w.V)
+    check("Z", Z, Zq, tol)
+    check_lse("L", L, Lq, tol)
+    check("Y", Y, Yq, tol)
+
+
 def test_encode_and_decode_entry_points(flare, orc):
     import torch
     from rank_latent_attention_amd.inputs import make_gaussian
