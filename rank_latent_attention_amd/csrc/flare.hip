@@ -1074,7 +1074,16 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
         dma_tile<D, NW, ROWS>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW, ROWS>(v0, Vh, tn2, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 2 * TE * 2, ROWS>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      if constexpr (2 * TE * 2 < 32768) {
+        encode_tile<D, NW, WN, 2 * TE * 2, ROWS>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      } else {  // buffer 1 beyond the reads' 16-bit offsets: its addresses in registers
+        unsigned kb[D / 16], vb[4];
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) kb[st] = ka[st] + 2 * TE * 2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vb[k] = va[k] + 2 * TE * 2;
+        encode_tile<D, NW, WN, 0, ROWS>(kb, vb, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      }
       wait_dma();
       __syncthreads();
       if constexpr (NK) {
@@ -1687,14 +1696,19 @@ struct HeadArgs {
 };
 
 // Token lanes (splits) of the encode steps for MB latent blocks, the tile rows
-// that give each of them one 32-token block per tile, and the dynamic LDS:
-// the encode's tiles (later the decode's staged queries and latents), then
-// the split partials [WN][M][D] and their (shift, sum) [WN][M].
+// that give each of them two 32-token blocks per tile (the scores of the
+// second go to the matrix core before the first one's weights are formed),
+// and the dynamic LDS: the encode's tiles; once an encode has consumed them,
+// its split partials [WN][M][D] and their (shift, sum) [WN][M]; in the decode
+// its staged queries and latents.
 template <int MB> constexpr int head_wn() { return kHeadWaves / MB; }
-template <int MB> constexpr int head_rows() { return 32 * head_wn<MB>() > 128 ? 32 * head_wn<MB>() : 128; }
+template <int MB> constexpr int head_rows() { return 64 * head_wn<MB>(); }
 template <int MB> constexpr size_t head_tile_bytes() { return (size_t)4 * head_rows<MB>() * 32 * sizeof(bf16); }
+template <int MB> constexpr size_t head_part_bytes() {
+  return (size_t)head_wn<MB>() * 32 * MB * (32 * sizeof(float) + sizeof(float2));
+}
 template <int MB> constexpr size_t head_lds() {
-  return head_tile_bytes<MB>() + (size_t)head_wn<MB>() * 32 * MB * (32 * sizeof(float) + sizeof(float2));
+  return head_tile_bytes<MB>() > head_part_bytes<MB>() ? head_tile_bytes<MB>() : head_part_bytes<MB>();
 }
 
 // The merge of one head's split partials from LDS (lacc [WN][M][D], lal
@@ -1728,7 +1742,7 @@ __global__ void __launch_bounds__(kHeadWaves * 64) pp_head_kernel(HeadArgs a) {
   __shared__ float red[2 * kHeadWaves];
   __shared__ int next_blk;
   bf16* const tiles = reinterpret_cast<bf16*>(smem);
-  float* const lacc = reinterpret_cast<float*>(smem + head_tile_bytes<MB>());
+  float* const lacc = reinterpret_cast<float*>(smem);  // the tiles' space: written once the tiles are consumed
   float2* const lal = reinterpret_cast<float2*>(lacc + WN * M * D);
   const int bh = blockIdx.x, h = bh % a.H;
   const int m = threadIdx.x / (D / 4), c = threadIdx.x % (D / 4);
