@@ -27,6 +27,9 @@
 //                     queries and latents in LDS, its waves claim 32-token
 //                     blocks from an LDS counter, and S = Q K^T and
 //                     Y^T += Z^T P run on MFMA with one lane per token column.
+//   pp_head_kernel -- the whole FLARE++ forward of one head in one 16-wave
+//                     workgroup (many short heads): the encode and decode
+//                     code above with the split merges done in LDS.
 // proj.h holds the encode from the block input (K = X W_K, V = X W_V formed
 // per tile), backward.h the reverse-mode kernels and their entry points,
 // backward32.h the float32 ones.
