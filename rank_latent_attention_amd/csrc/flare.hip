@@ -27,9 +27,9 @@
 //                     queries and latents in LDS, its waves claim 32-token
 //                     blocks from an LDS counter, and S = Q K^T and
 //                     Y^T += Z^T P run on MFMA with one lane per token column.
-//   pp_head_kernel -- the whole FLARE++ forward of one head in one 16-wave
-//                     workgroup (many short heads): the encode and decode
-//                     code above with the split merges done in LDS.
+//   head_kernel    -- the whole FLARE or FLARE++ forward of one head in one
+//                     16-wave workgroup (many short heads): the encode and
+//                     decode code above with the split merges done in LDS.
 // proj.h holds the encode from the block input (K = X W_K, V = X W_V formed
 // per tile), backward.h the reverse-mode kernels and their entry points,
 // backward32.h the float32 ones.
@@ -51,6 +51,7 @@
 
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "flare.h"
@@ -1673,13 +1674,14 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 }
 
 // ----------------------------------------------------------------------------
-// FLARE++ forward with one workgroup per head
+// FLARE and FLARE++ forward with one workgroup per head
 // ----------------------------------------------------------------------------
-// With many heads of a few thousand tokens, the five launches of the FLARE++
-// forward (synthesis encode, blended merge, routing encode, merge, decode)
-// spend much of their time filling and draining the chip between steps.  Here
-// one workgroup of kHeadWaves waves takes a whole head through the five steps,
-// with workgroup barriers in place of the kernel boundaries: the head is one
+// With many heads of a few thousand tokens, the launches of the forward
+// (FLARE++: synthesis encode, blended merge, routing encode, merge, decode;
+// FLARE: the last three) spend much of their time filling and draining the
+// chip between steps.  Here one workgroup of kHeadWaves waves takes a whole
+// head through the steps, with workgroup barriers in place of the kernel
+// boundaries: the head is one
 // piece of WN splits (one per token lane of waves), whose partials stay in
 // LDS and are merged there by the whole workgroup; the blended queries and
 // the latents pass through their buffers to the next step.  The encodes and
@@ -1688,9 +1690,9 @@ constexpr int kHeadWaves = 16;
 static_assert(kHeadWaves == kDecWaves, "the decode step runs with the decode's wave count");
 
 struct HeadArgs {
-  EncArgs se, re;      // synthesis encode (bf16 seeds), routing encode (float32 blended queries)
+  EncArgs se, re;      // synthesis encode (bf16 seeds, FLARE++), routing encode
   DecArgs d;           // decode
-  const bf16* Qf;      // [H,M,D] fixed queries of the blend
+  const bf16* Qf;      // [H,M,D] fixed queries of the blend (FLARE++)
   const float* gate;   // [H]
   float* Qout;         // [B,H,M,D] blended queries (the routing queries)
   float* Z;            // [B,H,M,D]
@@ -1736,9 +1738,12 @@ __device__ inline f32x4 merge_lds(const float* lacc, const float2* lal, int M, i
 
 // D = 32, MB latent blocks (M = 32 MB), bf16 keys and values; one head per
 // workgroup (blockIdx.x = head); dynamic LDS of head_lds<MB>() bytes.  Thread
-// t merges latent t / 8, features 4 (t % 8) .. + 3.
-template <int MB>
-__global__ void __launch_bounds__(kHeadWaves * 64) pp_head_kernel(HeadArgs a) {
+// t merges latent t / 8, features 4 (t % 8) .. + 3.  PP: the FLARE++ forward,
+// whose routing queries are the float32 blended ones it writes to a.Qout;
+// else the FLARE forward with the bf16 queries of a.re.
+template <int MB, bool PP>
+__global__ void __launch_bounds__(kHeadWaves * 64) head_kernel(HeadArgs a) {
+  using RQ = typename std::conditional<PP, float, bf16>::type;  // routing query element type
   constexpr int D = 32, M = 32 * MB, WN = head_wn<MB>(), ROWS = head_rows<MB>();
   static_assert(M * D / 4 <= kHeadWaves * 64, "one latent chunk per thread");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1752,22 +1757,25 @@ __global__ void __launch_bounds__(kHeadWaves * 64) pp_head_kernel(HeadArgs a) {
   const bool mine = m < M;
   const size_t o = ((size_t)bh * M + m) * D + 4 * c;
 
-  encode_dma_body<bf16, D, kHeadWaves, WN, false, ROWS, true>(a.se, bh, tiles, red, lacc, lal);
-  float qf[4] = {0.f, 0.f, 0.f, 0.f};
-  if (mine) {
-    const bf16* q = a.Qf + ((size_t)h * M + m) * D + 4 * c;
+  if constexpr (PP) {
+    encode_dma_body<bf16, D, kHeadWaves, WN, false, ROWS, true>(a.se, bh, tiles, red, lacc, lal);
+    float qf[4] = {0.f, 0.f, 0.f, 0.f};
+    if (mine) {
+      const bf16* q = a.Qf + ((size_t)h * M + m) * D + 4 * c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = (float)q[i];
+      for (int i = 0; i < 4; ++i) qf[i] = (float)q[i];
+    }
+    const float g = a.gate[h];
+    __syncthreads();  // the synthesis partials are in LDS
+    if (mine) {
+      float lse;
+      const f32x4 z = merge_lds<WN, D>(lacc, lal, M, m, c, lse);
+      *reinterpret_cast<f32x4*>(a.Qout + o) =
+          f32x4{qf[0] + g * z[0], qf[1] + g * z[1], qf[2] + g * z[2], qf[3] + g * z[3]};
+    }
+    __syncthreads();  // the blended queries are written, the partials read
   }
-  const float g = a.gate[h];
-  __syncthreads();  // the synthesis partials are in LDS
-  if (mine) {
-    float lse;
-    const f32x4 z = merge_lds<WN, D>(lacc, lal, M, m, c, lse);
-    *reinterpret_cast<f32x4*>(a.Qout + o) = f32x4{qf[0] + g * z[0], qf[1] + g * z[1], qf[2] + g * z[2], qf[3] + g * z[3]};
-  }
-  __syncthreads();  // the blended queries are written, the partials read
-  encode_dma_body<float, D, kHeadWaves, WN, false, ROWS, true>(a.re, bh, tiles, red, lacc, lal);
+  encode_dma_body<RQ, D, kHeadWaves, WN, false, ROWS, true>(a.re, bh, tiles, red, lacc, lal);
   __syncthreads();
   if (mine) {
     float lse;
@@ -1776,7 +1784,7 @@ __global__ void __launch_bounds__(kHeadWaves * 64) pp_head_kernel(HeadArgs a) {
     if (c == 0) a.L[(size_t)bh * M + m] = lse;
   }
   __syncthreads();  // Z is written
-  decode_body<bf16, float, D, false, false, false, MB>(a.d, bh, smem, red, red + kHeadWaves, next_blk);
+  decode_body<bf16, RQ, D, false, false, false, MB>(a.d, bh, smem, red, red + kHeadWaves, next_blk);
 }
 
 // ----------------------------------------------------------------------------
@@ -2080,56 +2088,79 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
   return w;
 }
 
-// The one-workgroup-per-head FLARE++ forward (pp_head_kernel) serves bf16,
-// D = 32 and M = 64 or 128 without normalisations, when the heads alone
-// occupy at least half of the compute units and each is short: there the
-// split of a head across workgroups gains less than the four kernel
-// boundaries cost.  (Two workgroups per head, both encoding all of its tokens
-// and each decoding half, were no faster at a quarter to half of the compute
-// units: the doubled key and value reads slowed both encodes by what the
-// halved decode saved.)
+// The one-workgroup-per-head forward (head_kernel) serves bf16, D = 32 and
+// M = 64 or 128 without normalisations, when the heads alone occupy at least
+// half of the compute units and each is short: there the split of a head
+// across workgroups gains less than the kernel boundaries cost.  Up to
+// kHeadMaxN tokens for FLARE++ (five launches saved), and for FLARE (three)
+// half of that unless the heads fill every compute unit.  (For
+// FLARE++, two workgroups per head, both encoding all of its tokens and each
+// decoding half, were no faster at a quarter to half of the compute units:
+// the doubled key and value reads slowed both encodes by what the halved
+// decode saved.)
 constexpr int kHeadMaxN = 8192;
 
-bool pp_head_applies(const Dev& dev, int BH, int N, int M, int D, int dtype, int norm_flags, const WsLayout& w) {
-  if (dtype != FLARE_BF16 || D != 32 || norm_flags || (M != 64 && M != 128)) return false;
-  if (N < 1 || N > kHeadMaxN || 2 * (long long)BH < dev.cus || !w.kmax) return false;
+bool head_applies(const Dev& dev, bool pp, int BH, int N, int M, int D, int dtype, const WsLayout& w) {
+  if (dtype != FLARE_BF16 || D != 32 || (M != 64 && M != 128)) return false;
+  const int nmax = pp || BH >= dev.cus ? kHeadMaxN : kHeadMaxN / 2;
+  if (N < 1 || N > nmax || 2 * (long long)BH < dev.cus || !w.kmax) return false;
   return (M == 64 ? head_lds<2>() : head_lds<4>()) + 1024 <= dev.lds_max;
 }
 
-template <int MB>
+template <int MB, bool PP>
 int launch_head(const HeadArgs& a, int BH, hipStream_t st) {
   static_assert(head_tile_bytes<MB>() >= (size_t)(MB * 32 * (32 + 8) + 32 * (MB * 32 + 4)) * sizeof(bf16),
                 "the decode's staging fits in the encode's tiles");
   const size_t lds = head_lds<MB>();
-  if (lds > 65536 && hipFuncSetAttribute((const void*)pp_head_kernel<MB>,
+  if (lds > 65536 && hipFuncSetAttribute((const void*)head_kernel<MB, PP>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return FLARE_ERR_HIP;
-  return launch(pp_head_kernel<MB>, dim3(BH), dim3(kHeadWaves * 64), lds, st, a);
+  return launch(head_kernel<MB, PP>, dim3(BH), dim3(kHeadWaves * 64), lds, st, a);
 }
 
-// FLARE++ forward of B H heads of N tokens (pp_head_applies holds): Qb, Z, L
-// and Y as the launch sequence writes them; kh: [B H] floats of workspace
-// (the heads' largest squared routing-key norms).
-int launch_pp_head(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate, const void* K,
-                   const void* V, void* Y, float* Qb, float* Z, float* L, int B, int H, int N, int M, float qs,
-                   float* kh, hipStream_t st) {
+// The plan of one piece per head (its WN splits the token lanes), and the
+// routing encode and decode arguments: queries Q (bf16 with q_batched, or the
+// float32 blended ones), kh: [B H] floats of workspace for the heads' largest
+// squared routing-key norms.
+HeadArgs head_args(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z, float* L, int B,
+                   int H, int N, int M, float qs, float* kh, EncPlan& p) {
   const int BH = B * H;
-  EncPlan p{};
+  p = EncPlan{};
   p.G = M / 32;
   p.WN = kHeadWaves / p.G;
   p.nwg = BH;  // piece i is head i
   p.total = (long long)BH * N;
   p.pmax = p.WN;
-  HeadArgs a;
-  a.se = encode_args(Qs, 0, Ks, Vs, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, nullptr);
-  a.re = encode_args(Qb, 1, K, V, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, kh);
+  HeadArgs a{};
+  a.re = encode_args(Q, q_batched, K, V, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, kh);
   a.d = DecArgs{};
-  a.d.Q = Qb; a.d.K = K; a.d.Z = Z; a.d.Y = Y; a.d.kmax = kh;
+  a.d.Q = Q; a.d.K = K; a.d.Z = Z; a.d.Y = Y; a.d.kmax = kh;
   a.d.total = p.total;
-  a.d.q_batched = 1; a.d.H = H; a.d.N = N; a.d.M = M; a.d.MB = M / 32; a.d.nwg = BH; a.d.bh0 = 0;
+  a.d.q_batched = q_batched; a.d.H = H; a.d.N = N; a.d.M = M; a.d.MB = M / 32; a.d.nwg = BH; a.d.bh0 = 0;
   a.d.qscale = qs;
-  a.Qf = (const bf16*)Qf; a.gate = gate; a.Qout = Qb; a.Z = Z; a.L = L; a.H = H;
-  return M == 64 ? launch_head<2>(a, BH, st) : launch_head<4>(a, BH, st);
+  a.Z = Z; a.L = L; a.H = H;
+  return a;
+}
+
+// FLARE forward of B H heads of N tokens with bf16 queries (head_applies
+// holds): Z, L and Y as the launch sequence writes them.
+int launch_flare_head(const void* Q, int q_batched, const void* K, const void* V, void* Y, float* Z, float* L, int B,
+                      int H, int N, int M, float qs, float* kh, hipStream_t st) {
+  EncPlan p;
+  const HeadArgs a = head_args(Q, q_batched, K, V, Y, Z, L, B, H, N, M, qs, kh, p);
+  return M == 64 ? launch_head<2, false>(a, B * H, st) : launch_head<4, false>(a, B * H, st);
+}
+
+// FLARE++ forward (head_applies holds, no normalisations): Qb, Z, L and Y as
+// the launch sequence writes them.
+int launch_pp_head(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate, const void* K,
+                   const void* V, void* Y, float* Qb, float* Z, float* L, int B, int H, int N, int M, float qs,
+                   float* kh, hipStream_t st) {
+  EncPlan p;
+  HeadArgs a = head_args(Qb, 1, K, V, Y, Z, L, B, H, N, M, qs, kh, p);
+  a.se = encode_args(Qs, 0, Ks, Vs, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, nullptr);
+  a.Qf = (const bf16*)Qf; a.gate = gate; a.Qout = Qb;
+  return M == 64 ? launch_head<2, true>(a, B * H, st) : launch_head<4, true>(a, B * H, st);
 }
 
 }  // namespace
@@ -2259,6 +2290,9 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   float* km = w.kmax ? (float*)(ws + w.km) : nullptr;
   float* kh = w.kmax ? (float*)(ws + w.kh) : nullptr;
+  const bool no_norms = !nm.norm_q && !nm.qmul0 && !nm.qmul1 && !nm.norm_k;
+  if (qtype == FLARE_BF16 && no_norms && head_applies(dev, false, BH, N, M, D, dtype, w))  // many short heads
+    return launch_flare_head(Q, q_batched, K, V, Y, Z, L, B, H, N, M, qs, kh, st);
   int rc;
   if (N > 0) {
     rc = launch_encode(Q, qtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st, km);
@@ -2354,7 +2388,7 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
   rt.norm_k = norm_flags & FLARE_NORM_K;
   rt.qmul1 = rt.norm_k ? alpha_k : nullptr;
   rt.eps = eps;
-  if (pp_head_applies(dev, BH, N, M, D, dtype, norm_flags, w))  // many short heads: one workgroup each
+  if (!norm_flags && head_applies(dev, true, BH, N, M, D, dtype, w))  // many short heads: one workgroup each
     return launch_pp_head(Qs, Ks, Vs, Qf, gate, K, V, Y, Qb, Z, L, B, H, N, M, qs, (float*)(wsc + w.kh), st);
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   // Synthesis encode over all heads, merged straight into the blended queries.

@@ -203,15 +203,17 @@ def test_pp_shapes_and_unshared_values(flare, orc, dtype):
 
 
 def _head_batch(H, fill):
-    """A batch size for the FLARE++ forward that runs each head in its own
-    workgroup (D = 32, M = 64 or 128, bf16, up to 8192 tokens per head) once
-    B H reaches half of the compute units: "half" gives B H = half of them,
-    "more" one step of H past that, and "quarter" a quarter of them (the
+    """A batch size for the forwards that run each head in its own workgroup
+    (D = 32, M = 64 or 128, bf16, short heads) once B H reaches half of the
+    compute units: "half" gives B H = half of them, "more" one step of H
+    past that, "all" every compute unit, and "quarter" a quarter of them (the
     launch sequence, for comparison)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if fill == "quarter":
         return -(-cus // (4 * H))
+    if fill == "all":
+        return -(-cus // H)
     if fill == "half":
         return -(-cus // (2 * H))
     return -(-cus // (2 * H)) + 1
@@ -253,6 +255,51 @@ def test_pp_one_workgroup_per_head(flare, orc, N, M, H, share, mult, fill):
     check("Z", Z, Zq, tol)
     check_lse("L", L, Lq, tol)
     check("Y", Y, Yq, tol)
+
+
+@pytest.mark.parametrize("N,M,H,batched,mult,fill", [
+    (1, 64, 4, False, 1.0, "half"),       # one token per head
+    (100, 128, 4, True, 1.0, "more"),     # less than one tile, per-batch queries
+    (4097, 64, 2, False, 1.0, "half"),    # one token past 8 tiles
+    (4096, 128, 8, True, 1.0, "half"),    # the longest heads it takes below every compute unit
+    (8192, 64, 4, False, 1.0, "all"),     # the longest heads it takes
+    (3000, 64, 4, False, 1.0, "quarter"), # below half of the compute units: the launch sequence
+    (3000, 64, 4, False, 8.0, "more"),    # queries x8: exact-score redo in the encode and the decode
+])
+def test_forward_one_workgroup_per_head(flare, orc, N, M, H, batched, mult, fill):
+    """The FLARE forward runs each head in its own workgroup under the same
+    conditions as FLARE++ (bf16, D = 32, M = 64 or 128, up to 8192 tokens,
+    B H at least half the compute units).  Against the oracle, and against
+    the standalone decode (which checks every block's key norms) on the
+    forward's own Z: bit for bit where no block needs the exact-score redo.
+    With the redo the two differ in rounding, because a redone 32-token block
+    is one of the decode's pieces' blocks, and the per-head decode cuts the
+    tokens into blocks from each head's start."""
+    import torch
+    from rank_latent_attention_amd.inputs import make_gaussian, to_dtype
+    B = _head_batch(H, fill)
+    w = make_gaussian(B, H, N, M, 32, "bf16", seed=57 + N)
+    if batched:
+        rng = np.random.default_rng(58 + N)
+        w.Q = to_dtype(rng.standard_normal((B, H, M, 32)) / math.sqrt(32), "bf16")
+    if mult != 1.0:
+        w.Q = to_dtype(w.Q.astype(np.float64) * mult, "bf16")
+    say(f"[forward per head] B{B} H{H} N{N} M{M} D32 bf16 batched={batched} queries x{mult:g} ({fill})")
+    Q, K, V = dev(w.Q, "bf16"), dev(w.K, "bf16"), dev(w.V, "bf16")
+    Z = torch.empty((B, H, M, 32), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    Y, _, _ = flare.flare_forward(Q, K, V, Z=Z, L=L)
+    Yd = flare.flare_decode(Q, K, Z)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    if mult == 1.0:
+        assert torch.equal(Y, Yd), "forward and standalone decode differ"
+    else:
+        check("Y against the standalone decode", host(Y), host(Yd), tol)
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    check("Z", host(Z), Zr, tol)
+    check_lse("L", host(L), Lr, tol)
+    check("Y", host(Y), Yr, tol)
 
 
 def test_encode_and_decode_entry_points(flare, orc):
