@@ -1367,9 +1367,9 @@ template <typename T, int D> struct DecLds {
 // run to the end of the piece together: with several workgroups per compute
 // unit the oldest ones are issued first, finish early and leave the last to
 // run alone at one wave per SIMD.
-// Piece `piece` of a.nwg (the workgroup's); smem: DecLds<T, D>::bytes(MB) of LDS, zred and
-// qred: kDecWaves floats of LDS each, next_blk: one int of LDS (the next
-// unclaimed 32-token block of the piece).
+// Piece `piece` of a.nwg (the workgroup's); smem: DecLds<T, D>::bytes(MB)
+// of LDS, zred and qred: kDecWaves floats of LDS each, next_blk: one int of
+// LDS (the next unclaimed 32-token block of the piece).
 template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs& a, int piece, unsigned char* smem,
                                                                   float* zred, float* qred, int& next_blk) {
@@ -1681,11 +1681,11 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 // FLARE: the last three) spend much of their time filling and draining the
 // chip between steps.  Here one workgroup of kHeadWaves waves takes a whole
 // head through the steps, with workgroup barriers in place of the kernel
-// boundaries: the head is one
-// piece of WN splits (one per token lane of waves), whose partials stay in
-// LDS and are merged there by the whole workgroup; the blended queries and
-// the latents pass through their buffers to the next step.  The encodes and
-// the decode run the device code of their own kernels.
+// boundaries: the head is one piece of WN splits (one per token lane of
+// waves), whose partials stay in LDS and are merged there by the whole
+// workgroup; the blended queries and the latents pass through their buffers
+// to the next step.  The encodes and the decode run the device code of their
+// own kernels.
 constexpr int kHeadWaves = 16;
 static_assert(kHeadWaves == kDecWaves, "the decode step runs with the decode's wave count");
 
