@@ -40,7 +40,9 @@ def _run(flare, w, noalloc):
 
 def test_noalloc_matches_forward_twice_second_smaller(flare):
     from rank_latent_attention_amd.inputs import make_gaussian
-    for shape, dtype in [((2, 4, 40000, 256, 32), "bf16"), ((1, 3, 5000, 64, 16), "bf16"), ((1, 2, 3000, 48, 16), "f32")]:
+    # the second shape has enough short heads for one workgroup per head
+    for shape, dtype in [((2, 4, 40000, 256, 32), "bf16"), ((32, 4, 2000, 64, 32), "bf16"), ((1, 3, 5000, 64, 16), "bf16"),
+                         ((1, 2, 3000, 48, 16), "f32")]:
         w = make_gaussian(*shape, dtype=dtype, seed=sum(shape))
         print(f"[noalloc] {shape} {dtype}", flush=True)
         ref = _run(flare, w, noalloc=False)
