@@ -1318,12 +1318,57 @@ struct DecArgs {
   const float* qmul;  // [H, D] channel scale of the queries (the keys' N_a scale), or null
   float eps;          // key rows are N_0-normalised when the kernel's NK flag is set
   const float* kmax;  // [B H] largest squared key norm of each head (from its encode), or null
+  // With the kernel's MRG flag, Z is not read: the staging merges the head's
+  // split partials itself (the encode's plan: total etotal, enwg pieces, eWN
+  // splits per piece, pmax slots per head), takes the head's key-norm maximum
+  // from part_km (or null), and the workgroup holding the head's first token
+  // writes Z and L to Zout and Lout (or null).
+  const float* part_acc;  // [nbh][pmax][M][D]
+  const float2* part_al;  // [nbh][pmax][M]
+  const float* part_km;   // [nbh][pmax]
+  float* Zout;            // [B,H,M,D]
+  float* Lout;            // [B,H,M]
+  long long etotal;
+  int enwg, eWN, pmax;
   // statistics mode (the kernel's ST flag, bf16): instead of Y, per token
   // one record of 8 bf16 (see split3_record): the negated log2 of the
   // weight sum over the latents and the negated dY . Y, each as three parts
   const void* dY;     // [B,H,N,D], type T
   uint4* srec;        // [B,H,N]
 };
+
+// Z (features d0 .. d0 + 3 of latent m) and L of one head from its cnt
+// split partials at slots pbase .. pbase + cnt - 1, folded in ascending order
+// by the merge's rule; each batch of kMergeBatch splits is loaded before any
+// of it is folded.
+__device__ inline f32x4 merge_splits(const float* part_acc, const float2* part_al, size_t pbase, int cnt, int M, int D,
+                                     int m, int d0, float& lse) {
+  MergeState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int p0 = 0; p0 < cnt; p0 += kMergeBatch) {
+    float2 v[kMergeBatch];
+    f32x4 u[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int p = p0 + j;
+      v[j] = make_float2(-INFINITY, 0.f);  // slots past cnt count as empty
+      u[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p < cnt) {
+        const size_t i = (pbase + p) * M + m;
+        v[j] = part_al[i];
+        u[j] = *reinterpret_cast<const f32x4*>(part_acc + i * D + d0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) st = merge_fold(st, v[j].x, v[j].y, u[j]);
+  }
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  lse = -INFINITY;
+  if (st.A > -INFINITY) {
+    z = st.num / st.den;
+    lse = kLn2 * (st.A + __builtin_amdgcn_logf(st.den));
+  }
+  return z;
+}
 
 // Record of two float32 values x, y as 8 bf16: x = x0 + x1 + x2 and
 // y = y0 + y1 + y2 (each part the bf16 rounding of what the previous parts
@@ -1359,7 +1404,8 @@ template <typename T, int D> struct DecLds {
 // token's softmax over the latents (log2 units, the queries' scaling) and
 // the dot product of the token's output cotangent with its output.
 // MBT > 0 fixes the number of latent blocks at compile time (a.MB == MBT), so
-// the latent loop unrolls completely; 0 reads it from the arguments.
+// the latent loop unrolls completely; 0 reads it from the arguments.  MRG:
+// the staging merges the encode's split partials (see DecArgs).
 //
 // One workgroup of kDecWaves waves per compute unit (four per SIMD) shares a
 // head's staged queries and latents.  Its waves take the piece's 32-token
@@ -1370,7 +1416,7 @@ template <typename T, int D> struct DecLds {
 // Piece `piece` of a.nwg (the workgroup's); smem: DecLds<T, D>::bytes(MB)
 // of LDS, zred and qred: kDecWaves floats of LDS each, next_blk: one int of
 // LDS (the next unclaimed 32-token block of the piece).
-template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0, bool MRG = false>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs& a, int piece, unsigned char* smem,
                                                                   float* zred, float* qred, int& next_blk) {
   static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
@@ -1403,6 +1449,14 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
     __syncthreads();
     const QT* Qh = reinterpret_cast<const QT*>(a.Q) + (size_t)(a.q_batched ? bh : h) * M * D;
     const float* Zh = a.Z + (size_t)bh * M * D;
+    // MRG: the head's split slots, and whether this workgroup writes Z and L
+    int cnt = 0;
+    size_t pbase = 0;
+    if constexpr (MRG) {
+      cnt = (piece_of(hb + N - 1, a.etotal, a.enwg) - piece_of(hb, a.etotal, a.enwg) + 1) * a.eWN;
+      pbase = (size_t)bhl * a.pmax;
+    }
+    const bool writer = MRG && n_lo == 0;
     float zmax = 0.f;
     float qerr2 = 0.f;  // largest squared rounding error of a staged query row
     {
@@ -1421,10 +1475,12 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
         const int c = tid + j * kDecThreads;
         qv[j] = reinterpret_cast<const uint4*>(Qh)[c < nq ? c : 0];
       }
+      if constexpr (!MRG) {
 #pragma unroll
-      for (int j = 0; j < ZJ; ++j) {
-        const int c = tid + j * kDecThreads;
-        zv[j] = reinterpret_cast<const uint4*>(Zh)[c < nz ? c : 0];
+        for (int j = 0; j < ZJ; ++j) {
+          const int c = tid + j * kDecThreads;
+          zv[j] = reinterpret_cast<const uint4*>(Zh)[c < nz ? c : 0];
+        }
       }
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
@@ -1463,12 +1519,23 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
         const int c = tid + j * kDecThreads;
         if (c < pz) {
           const int m = c * 4 / D, d0 = c * 4 % D;
-          const float* src = reinterpret_cast<const float*>(&zv[j]);
+          f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+          if (c < nz) {
+            if constexpr (MRG) {
+              float lse;
+              z4 = merge_splits(a.part_acc, a.part_al, pbase, cnt, M, D, m, d0, lse);
+              if (writer) {
+                *reinterpret_cast<f32x4*>(a.Zout + ((size_t)bh * M + m) * D + d0) = z4;
+                if (a.Lout && d0 == 0) a.Lout[(size_t)bh * M + m] = lse;
+              }
+            } else {
+              z4 = *reinterpret_cast<const f32x4*>(&zv[j]);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float z = c < nz ? src[i] : 0.f;
-            zt[(d0 + i) * zst + m] = from_f<T>(z);
-            zmax = fmaxf(zmax, fabsf(z));
+            zt[(d0 + i) * zst + m] = from_f<T>(z4[i]);
+            zmax = fmaxf(zmax, fabsf(z4[i]));
           }
         }
       }
@@ -1489,7 +1556,17 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
     // head's encode found no key beyond that (with 1% for the rounding of
     // keys normalised there and here), no block needs the check.
     const float klim2 = qerr2 > 0.f ? kScoreErr2 / qerr2 : INFINITY;
-    const bool kcheck = !(a.kmax && a.kmax[bh] * 1.01f <= klim2);
+    float khead = INFINITY;  // the head's largest squared key norm, if known
+    if constexpr (MRG) {
+      if (a.part_km) {
+        khead = 0.f;
+        for (int p = lane; p < cnt; p += 64) khead = fmaxf(khead, a.part_km[pbase + p]);
+        khead = wave_max(khead);
+      }
+    } else {
+      if (a.kmax) khead = a.kmax[bh];
+    }
+    const bool kcheck = !(khead * 1.01f <= klim2);
 
     const T* Kh = reinterpret_cast<const T*>(a.K) + (size_t)bh * N * D;
     T* Yh = reinterpret_cast<T*>(a.Y) + (size_t)bh * N * D;
@@ -1665,12 +1742,12 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
   }
 }
 
-template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0, bool MRG = false>
 __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float zred[kDecWaves], qred[kDecWaves];
   __shared__ int next_blk;
-  decode_body<T, QT, D, TAIL, NK, ST, MBT>(a, blockIdx.x, smem, zred, qred, next_blk);
+  decode_body<T, QT, D, TAIL, NK, ST, MBT, MRG>(a, blockIdx.x, smem, zred, qred, next_blk);
 }
 
 // ----------------------------------------------------------------------------
@@ -1979,14 +2056,14 @@ int launch_merge(const EncPlan& p, const float* part_acc, const float2* part_al,
   return launch(merge_kernel<float>, grid, dim3(kThreads), 0, st, a);
 }
 
-template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0>
+template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, int MBT = 0, bool MRG = false>
 int launch_decode_k(const DecArgs& a, size_t lds, hipStream_t st) {
-  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK, ST, MBT>;
+  const void* fn = (const void*)decode_kernel<T, QT, D, TAIL, NK, ST, MBT, MRG>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return FLARE_ERR_HIP;
   }
-  return launch(decode_kernel<T, QT, D, TAIL, NK, ST, MBT>, dim3(a.nwg), dim3(kDecThreads), lds, st, a);
+  return launch(decode_kernel<T, QT, D, TAIL, NK, ST, MBT, MRG>, dim3(a.nwg), dim3(kDecThreads), lds, st, a);
 }
 
 // bf16 decode without a latent tail: 2, 4 or 8 latent blocks (M = 64, 128,
@@ -2023,10 +2100,33 @@ size_t decode_lds(int dtype, int D, int M) {
   return D == 16 ? DecLds<float, 16>::bytes(MB) : DecLds<float, 32>::bytes(MB);
 }
 
+// The encode's split partials for a decode that merges them in its staging
+// (the kernel's MRG flag), with Z and L written by the first workgroup of
+// each head.
+struct DecMerge {
+  const EncPlan* p = nullptr;
+  const float* part_acc = nullptr;
+  const float2* part_al = nullptr;
+  const float* part_km = nullptr;
+  float* Z = nullptr;
+  float* L = nullptr;
+};
+
+// Whether the decode merges the splits itself: bf16 at M = 256 without key
+// norms, with at least 16384 (head, latent) pairs and at most 16 splits per
+// head.  The merge kernel takes one wave per pair, so its time grows with
+// the pairs; the decode's staging instead folds a head's splits in about two
+// memory round trips per workgroup.  (With few pairs or many splits the
+// separate merge was measured faster: at the PDE-mesh and M = 64 point-cloud
+// workloads, and at the million-token one.)
+bool decode_merges(const EncPlan& p, int BH, int N, int M, int dtype, const Norms& nm) {
+  return dtype == FLARE_BF16 && M == 256 && !nm.norm_k && N > 0 && (long long)BH * M >= 16384 && p.pmax <= 16;
+}
+
 // nm.norm_k: N_0 of the key rows; nm.qmul1: channel scale of the queries.
 int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const void* K, const float* Z, void* Y,
                   int bh0, int nbh, int H, int N, int M, int D, int dtype, float qscale, const Norms& nm,
-                  hipStream_t st, const float* kmax = nullptr) {
+                  hipStream_t st, const float* kmax = nullptr, const DecMerge* mg = nullptr) {
   if (N == 0) return FLARE_OK;
   DecArgs a{};
   a.kmax = kmax;
@@ -2041,6 +2141,17 @@ int launch_decode(const Dev& dev, const void* Q, int qtype, int q_batched, const
   a.nwg = (int)(want < maxw ? want : maxw);
   const size_t lds = decode_lds(dtype, D, M);
   if (lds > dev.lds_max) return FLARE_ERR_UNSUPPORTED;
+  if (mg) {  // decode_merges holds: bf16, M = 256 (8 whole latent blocks), no key norms
+    a.part_acc = mg->part_acc; a.part_al = mg->part_al; a.part_km = mg->part_km;
+    a.Zout = mg->Z; a.Lout = mg->L;
+    a.etotal = mg->p->total; a.enwg = mg->p->nwg; a.eWN = mg->p->WN; a.pmax = mg->p->pmax;
+    if (dtype != FLARE_BF16 || a.MB != 8 || nk) return FLARE_ERR_UNSUPPORTED;
+    if (qtype == FLARE_BF16)
+      return D == 16 ? launch_decode_k<bf16, bf16, 16, false, false, false, 8, true>(a, lds, st)
+                     : launch_decode_k<bf16, bf16, 32, false, false, false, 8, true>(a, lds, st);
+    return D == 16 ? launch_decode_k<bf16, float, 16, false, false, false, 8, true>(a, lds, st)
+                   : launch_decode_k<bf16, float, 32, false, false, false, 8, true>(a, lds, st);
+  }
   if (dtype == FLARE_BF16) {
     if (qtype == FLARE_BF16)
       return D == 16 ? launch_decode_t<bf16, bf16, 16>(a, lds, nk, st) : launch_decode_t<bf16, bf16, 32>(a, lds, nk, st);
@@ -2297,6 +2408,11 @@ static int routing(const Dev& dev, const void* Q, int qtype, int q_batched, cons
   if (N > 0) {
     rc = launch_encode(Q, qtype, q_batched, K, V, 0, H, N, M, D, dtype, qs, pacc, pal, p, nm, st, km);
     if (rc) return rc;
+  }
+  if (decode_merges(p, BH, N, M, dtype, nm)) {  // the decode merges the splits as it stages Z
+    DecMerge mg;
+    mg.p = &p; mg.part_acc = pacc; mg.part_al = pal; mg.part_km = km; mg.Z = Z; mg.L = L;
+    return launch_decode(dev, Q, qtype, q_batched, K, Z, Y, 0, BH, H, N, M, D, dtype, qs, nm, st, nullptr, &mg);
   }
   rc = launch_merge(p, pacc, pal, 0, BH, H, N, M, D, Z, L, nullptr, FLARE_F32, nullptr, nullptr, 0, nullptr, 0.f, st,
                     km, kh);

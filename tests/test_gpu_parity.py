@@ -302,6 +302,43 @@ def test_forward_one_workgroup_per_head(flare, orc, N, M, H, batched, mult, fill
     check("Y", host(Y), Yr, tol)
 
 
+@pytest.mark.parametrize("D,mult", [(32, 1.0), (16, 1.0), (32, 8.0)])
+def test_decode_merges_the_splits(flare, orc, D, mult):
+    """bf16 at M = 256 with at least 16384 (head, latent) pairs and few
+    splits per head: the decode merges the encode's splits as it stages the
+    latents (no merge launch), and the first workgroup of each head writes Z
+    and L.  Against the oracle; Y bit for bit against the standalone decode
+    on the forward's Z where no block needs the exact-score redo; and the
+    FLARE++ forward, whose routing decode takes float32 queries."""
+    import torch
+    from rank_latent_attention_amd.inputs import make_gaussian, make_gaussian_pp, to_dtype
+    w = make_gaussian(16, 4, 3000, 256, D, "bf16", seed=61 + D)
+    if mult != 1.0:
+        w.Q = to_dtype(w.Q.astype(np.float64) * mult, "bf16")
+    say(f"[decode merges] B16 H4 N3000 M256 D{D} bf16 queries x{mult:g}")
+    Q, K, V = dev(w.Q, "bf16"), dev(w.K, "bf16"), dev(w.V, "bf16")
+    Z = torch.empty((16, 4, 256, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((16, 4, 256), dtype=torch.float32, device=K.device)
+    Y, _, _ = flare.flare_forward(Q, K, V, Z=Z, L=L)
+    Yd = flare.flare_decode(Q, K, Z)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    if mult == 1.0:
+        assert torch.equal(Y, Yd), "forward and standalone decode differ"
+    Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    check("Z", host(Z), Zr, tol)
+    check_lse("L", host(L), Lr, tol)
+    check("Y", host(Y), Yr, tol)
+    if D == 32 and mult == 1.0:
+        wp = make_gaussian_pp(16, 4, 3000, 256, 32, dtype="bf16", seed=63)
+        Yp, Qo, Zp, Lp = run_pp(flare, wp)
+        Ypr, Qpr, Zpr, Lpr = orc.flare_pp_forward(wp.Qs, wp.Ks, wp.Vs, wp.Qf, wp.gate, wp.K, wp.V)
+        check("FLARE++ Q", Qo, Qpr, tol)
+        check("FLARE++ Z", Zp, Zpr, tol)
+        check_lse("FLARE++ L", Lp, Lpr, tol)
+        check("FLARE++ Y", Yp, Ypr, tol)
+
+
 def test_encode_and_decode_entry_points(flare, orc):
     import torch
     from rank_latent_attention_amd.inputs import make_gaussian
