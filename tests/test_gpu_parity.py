@@ -401,10 +401,21 @@ def test_token_permutation_equivariance(flare, dtype):
 
 
 def test_bitwise_reproducible(flare):
-    from rank_latent_attention_amd.inputs import make_gaussian
-    w = make_gaussian(2, 4, 50000, 128, 32, "bf16", seed=12)
-    a = run_flare(flare, w)
-    b = run_flare(flare, w)
+    """Repeated calls give identical bits: the split launch sequence, the
+    one-workgroup-per-head forwards (FLARE and FLARE++) and the decode that
+    merges the splits itself."""
+    from rank_latent_attention_amd.inputs import make_gaussian, make_gaussian_pp
+    B = _head_batch(4, "half")
+    for w in (make_gaussian(2, 4, 50000, 128, 32, "bf16", seed=12), make_gaussian(B, 4, 2000, 64, 32, "bf16", seed=13),
+              make_gaussian(16, 4, 3000, 256, 16, "bf16", seed=14)):
+        say(f"[reproducible] B{w.B} H{w.H} N{w.N} M{w.M} D{w.D}")
+        a = run_flare(flare, w)
+        b = run_flare(flare, w)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    wp = make_gaussian_pp(B, 4, 2000, 64, 32, dtype="bf16", seed=16)
+    a = run_pp(flare, wp)
+    b = run_pp(flare, wp)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
@@ -532,12 +543,19 @@ def test_query_shift_leaves_decode(flare, orc, dtype):
 
 
 def test_explicit_scale(flare, orc):
-    from rank_latent_attention_amd.inputs import make_gaussian
+    from rank_latent_attention_amd.inputs import make_gaussian, make_gaussian_pp
     w = make_gaussian(1, 2, 900, 32, 16, "f32", seed=15)
     Y, Z, L = run_flare(flare, w, scale=0.37)
     Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V, scale=0.37)
     check("Z", Z, Zr, 1e-5)
     check("Y", Y, Yr, 1e-5)
+    # the one-workgroup-per-head FLARE++ forward with the same override
+    wp = make_gaussian_pp(_head_batch(4, "half"), 4, 700, 64, 32, dtype="bf16", seed=17)
+    Y, Qo, Z, L = run_pp(flare, wp, scale=0.37)
+    Yr, Qr, Zr, Lr = orc.flare_pp_forward(wp.Qs, wp.Ks, wp.Vs, wp.Qf, wp.gate, wp.K, wp.V, scale=0.37)
+    check("Q", Qo, Qr, TOL["bf16"])
+    check("Z", Z, Zr, TOL["bf16"])
+    check("Y", Y, Yr, TOL["bf16"])
 
 
 def test_empty_token_axis(flare):
