@@ -30,6 +30,9 @@
 //   head_kernel    -- the whole FLARE or FLARE++ forward of one head in one
 //                     16-wave workgroup (many short heads): the encode and
 //                     decode code above with the split merges done in LDS.
+//   latent_kernel  -- the FLARE++ encodes of one (head, latent block) per
+//                     workgroup over all of the head's tokens, before the
+//                     decode launch.
 // proj.h holds the encode from the block input (K = X W_K, V = X W_V formed
 // per tile), backward.h the reverse-mode kernels and their entry points,
 // backward32.h the float32 ones.
@@ -665,6 +668,7 @@ struct EncArgs {
   float* part_km;     // [nbh][pmax] largest squared key norm of each split's keys, or null (bf16)
   long long total;    // nbh * N
   int q_batched, v_alias, H, N, M, G, nwg, pmax, bh0;
+  int m0 = 0;         // first latent of the workgroup's G latent blocks (bf16 encode)
   float qscale;       // s * log2(e)
   // query rows: N_0 when norm_q, then channel scales qmul0 / qmul1 ([H, D] or
   // null); keys N_0 per row when the kernel's NK flag is set (bf16 only)
@@ -979,8 +983,9 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
 // DMA of the next tile is in flight while the current one is consumed.
 // Piece `piece` of a.nwg (the workgroup's); tiles: 4 ROWS D bf16 of LDS
 // ([buffer][K, V]), kred: NW floats of LDS (per-wave largest squared key norm
-// of a piece).  With LP the workgroup's piece is one whole head and its split
-// partials go to LDS, lacc [WN][M][D] and lal [WN][M] (split = token lane),
+// of a piece).  The waves' latents start at a.m0.  With LP the workgroup's
+// piece is one whole head and its split partials go to LDS, lacc
+// [WN][32 G][D] and lal [WN][32 G] (split = token lane, latents from a.m0),
 // and a.part_km, when set, receives the head's largest squared key norm at
 // the head's index.
 template <typename QT, int D, int NW, int WN, bool NK, int ROWS = dma_rows<NW>(), bool LP = false>
@@ -1027,12 +1032,12 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
 
     // this lane's latent query row (rows past M repeat row M - 1 and are zeroed)
     auto qrow = [&]() {
-      const int m = mg * 32 + li;
+      const int m = a.m0 + mg * 32 + li;
       return reinterpret_cast<const QT*>(a.Q) + ((size_t)(a.q_batched ? bh : h) * M + (m < M ? m : M - 1)) * D;
     };
     const float* qm0 = a.qmul0 ? a.qmul0 + (size_t)h * D : nullptr;
     const float* qm1 = a.qmul1 ? a.qmul1 + (size_t)h * D : nullptr;
-    const int m = mg * 32 + li;
+    const int m = a.m0 + mg * 32 + li;
     QKOp<bf16, D> qop;
     // the wave's largest query rounding error (uniform: a scalar register)
     const float qerr2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
@@ -1117,7 +1122,7 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
     // that none is held in a register across the tile loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane2 = tid & 63, li2 = lane2 & 31, g2 = lane2 >> 5, m2 = mg * 32 + li2;
+    const int lane2 = tid & 63, li2 = lane2 & 31, g2 = lane2 >> 5, ml2 = mg * 32 + li2, m2 = a.m0 + ml2;
     float ltot = wsum.total(li2, acc), shift = 0.f;
     const bool inexact = qerr2 * kmax2 > kScoreErr2;
     if (inexact || fast_failed(ltot, n_lo + 32 * ng < n_hi, acc)) {
@@ -1137,8 +1142,10 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
       shift = (float)e;
     }
     if (m2 < M) {
+      // LP: [WN][32 G][D] over the workgroup's latents; else [pmax][M][D] per head
       const size_t p = LP ? (size_t)slot : (size_t)bhl * a.pmax + slot;
-      float* dst = (LP ? lacc : a.part_acc) + (p * M + m2) * D;
+      const size_t row = LP ? p * (32 * G) + ml2 : p * M + m2;
+      float* dst = (LP ? lacc : a.part_acc) + row * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (8 * c + 4 * g2 < D) {
@@ -1146,7 +1153,7 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
           *reinterpret_cast<f32x4*>(dst + 8 * c + 4 * g2) = v;
         }
       }
-      if (g2 == 0) (LP ? lal : a.part_al)[p * M + m2] = make_float2(shift, ltot);
+      if (g2 == 0) (LP ? lal : a.part_al)[row] = make_float2(shift, ltot);
     }
     x = hb + n_hi;
   }
@@ -1774,7 +1781,7 @@ struct HeadArgs {
   float* Qout;         // [B,H,M,D] blended queries (the routing queries)
   float* Z;            // [B,H,M,D]
   float* L;            // [B,H,M]
-  int H;
+  int H, nbh;          // heads per batch entry, B H
 };
 
 // Token lanes (splits) of the encode steps for MB latent blocks, the tile rows
@@ -1862,6 +1869,71 @@ __global__ void __launch_bounds__(kHeadWaves * 64) head_kernel(HeadArgs a) {
   }
   __syncthreads();  // Z is written
   decode_body<bf16, RQ, D, false, false, false, MB>(a.d, bh, smem, red, red + kHeadWaves, next_blk);
+}
+
+// ----------------------------------------------------------------------------
+// FLARE++ encodes with one workgroup per (head, latent block)
+// ----------------------------------------------------------------------------
+// The encode of a latent needs only that latent's query, so a head's latent
+// blocks can be encoded apart, each over all of the head's tokens: then no
+// split partials leave the workgroup and no merge launch follows, and a head
+// of M = 32 MB latents spreads over MB compute units.  One workgroup runs the
+// synthesis encode, the blend and the routing encode of one latent block
+// (the routing encode of a latent needs only its own blended query); the
+// decode, which needs all of a head's latents, follows as its own launch.  A
+// workgroup of kHeadWaves waves takes the block's 32 latents with all waves
+// as token lanes.
+constexpr int kLatRows = 32 * kHeadWaves;  // tokens per tile: one 32-token block per wave
+constexpr size_t kLatTileBytes = (size_t)4 * kLatRows * 32 * sizeof(bf16);
+constexpr size_t kLatPartBytes = (size_t)kHeadWaves * 32 * (32 * sizeof(float) + sizeof(float2));
+constexpr size_t kLatLds = kLatTileBytes > kLatPartBytes ? kLatTileBytes : kLatPartBytes;
+
+// D = 32, bf16 keys and values; workgroup w takes head w % nbh and latent
+// block w / nbh (latents 32 (w / nbh) .. + 31), so the workgroups of a head
+// are nbh apart; dynamic LDS of kLatLds bytes.  Thread t < 256 merges latent
+// t / 8 of the block, features 4 (t % 8) .. + 3.  Writes the blended queries
+// a.Qout, Z and L of its latents, and the head's largest squared routing-key
+// norm to the routing encode's part_km (block 0).
+__global__ void __launch_bounds__(kHeadWaves * 64) latent_kernel(HeadArgs a) {
+  constexpr int D = 32, WN = kHeadWaves, NC = 32 * D / 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float red[kHeadWaves];
+  bf16* const tiles = reinterpret_cast<bf16*>(smem);
+  float* const lacc = reinterpret_cast<float*>(smem);  // the tiles' space: written once the tiles are consumed
+  float2* const lal = reinterpret_cast<float2*>(lacc + WN * 32 * D);
+  const int mb = (int)blockIdx.x / a.nbh, bh = (int)blockIdx.x - mb * a.nbh, h = bh % a.H, M = a.re.M;
+  const int ml = threadIdx.x / (D / 4), c = threadIdx.x % (D / 4), m = 32 * mb + ml;
+  const bool mine = threadIdx.x < NC && m < M;
+  const size_t o = ((size_t)bh * M + m) * D + 4 * c;
+
+  EncArgs se = a.se;
+  se.m0 = 32 * mb;
+  encode_dma_body<bf16, D, kHeadWaves, WN, false, kLatRows, true>(se, bh, tiles, red, lacc, lal);
+  float qf[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mine) {
+    const bf16* q = a.Qf + ((size_t)h * M + m) * D + 4 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = (float)q[i];
+  }
+  const float g = a.gate[h];
+  __syncthreads();  // the synthesis partials are in LDS
+  if (mine) {
+    float lse;
+    const f32x4 z = merge_lds<WN, D>(lacc, lal, 32, ml, c, lse);
+    *reinterpret_cast<f32x4*>(a.Qout + o) = f32x4{qf[0] + g * z[0], qf[1] + g * z[1], qf[2] + g * z[2], qf[3] + g * z[3]};
+  }
+  __syncthreads();  // the block's blended queries are written, the partials read
+  EncArgs re = a.re;
+  re.m0 = 32 * mb;
+  if (mb != 0) re.part_km = nullptr;  // the head's key-norm maximum: written once
+  encode_dma_body<float, D, kHeadWaves, WN, false, kLatRows, true>(re, bh, tiles, red, lacc, lal);
+  __syncthreads();
+  if (mine) {
+    float lse;
+    const f32x4 z = merge_lds<WN, D>(lacc, lal, 32, ml, c, lse);
+    *reinterpret_cast<f32x4*>(a.Z + o) = z;
+    if (c == 0) a.L[(size_t)bh * M + m] = lse;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -2216,6 +2288,23 @@ WsLayout ws_layout(const Dev& dev, int op, int B, int H, int N, int M, int D, in
 // decode saved.)
 constexpr int kHeadMaxN = 8192;
 
+// The FLARE++ encodes by (head, latent block) with a separate decode
+// (latent_kernel) serve the inputs of head_kernel (bf16, D = 32, no
+// normalisations) for M a multiple of 32 and 2048 to kHeadMaxN tokens per
+// head, when the B H M / 32 workgroups fill more than half of the compute
+// units and at most all of them.  Each head's keys and values are then read
+// by M / 32 workgroups, so the encodes gain less than the spread suggests:
+// at the long-sequence workload 58.5-58.9 against 61.8-62.4 us for
+// head_kernel.  For FLARE, with one encode, it was no faster than head_kernel
+// or the launch sequence, and for shorter heads the second launch costs more
+// than the spread gains.
+bool latent_applies(const Dev& dev, int BH, int N, int M, int D, int dtype, const WsLayout& w) {
+  if (dtype != FLARE_BF16 || D != 32 || (M & 31) || N < 2048 || N > kHeadMaxN || !w.kmax) return false;
+  const long long wgs = (long long)BH * (M / 32);
+  if (2 * wgs <= dev.cus || wgs > dev.cus) return false;
+  return kLatLds + 1024 <= dev.lds_max && decode_lds(dtype, D, M) <= dev.lds_max;
+}
+
 bool head_applies(const Dev& dev, bool pp, int BH, int N, int M, int D, int dtype, const WsLayout& w) {
   if (dtype != FLARE_BF16 || D != 32 || (M != 64 && M != 128)) return false;
   const int nmax = pp || BH >= dev.cus ? kHeadMaxN : kHeadMaxN / 2;
@@ -2256,6 +2345,31 @@ HeadArgs head_args(const void* Q, int q_batched, const void* K, const void* V, v
   a.d.qscale = qs;
   a.Z = Z; a.L = L; a.H = H;
   return a;
+}
+
+// The FLARE++ encodes by (head, latent block) followed by the decode: Qb, Z,
+// L and Y as the launch sequence writes them; kh: [B H] floats of workspace.
+int launch_latent(const Dev& dev, const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
+                  const void* K, const void* V, void* Y, float* Qb, float* Z, float* L, int B, int H, int N, int M,
+                  float qs, float* kh, hipStream_t st) {
+  const int BH = B * H, D = 32;
+  EncPlan p{};
+  p.G = 1;
+  p.WN = kHeadWaves;
+  p.nwg = BH;  // piece i is head i
+  p.total = (long long)BH * N;
+  p.pmax = p.WN;
+  HeadArgs a{};
+  a.se = encode_args(Qs, 0, Ks, Vs, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, nullptr);
+  a.re = encode_args(Qb, 1, K, V, 0, H, N, M, qs, nullptr, nullptr, p, Norms{}, kh);
+  a.Qf = (const bf16*)Qf; a.gate = gate; a.Qout = Qb;
+  a.Z = Z; a.L = L; a.H = H; a.nbh = BH;
+  if (kLatLds > 65536 && hipFuncSetAttribute((const void*)latent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kLatLds) != hipSuccess)
+    return FLARE_ERR_HIP;
+  const int rc = launch(latent_kernel, dim3(BH * (M / 32)), dim3(kHeadWaves * 64), kLatLds, st, a);
+  if (rc) return rc;
+  return launch_decode(dev, Qb, FLARE_F32, 1, K, Z, Y, 0, BH, H, N, M, D, FLARE_BF16, qs, Norms{}, st, kh);
 }
 
 // FLARE forward of B H heads of N tokens with bf16 queries (head_applies
@@ -2509,8 +2623,12 @@ int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const 
   rt.norm_k = norm_flags & FLARE_NORM_K;
   rt.qmul1 = rt.norm_k ? alpha_k : nullptr;
   rt.eps = eps;
-  if (!norm_flags && head_applies(dev, true, BH, N, M, D, dtype, w))  // many short heads: one workgroup each
-    return launch_pp_head(Qs, Ks, Vs, Qf, gate, K, V, Y, Qb, Z, L, B, H, N, M, qs, (float*)(wsc + w.kh), st);
+  if (!norm_flags) {  // many short heads: one workgroup per latent block, or per head
+    if (latent_applies(dev, BH, N, M, D, dtype, w))
+      return launch_latent(dev, Qs, Ks, Vs, Qf, gate, K, V, Y, Qb, Z, L, B, H, N, M, qs, (float*)(wsc + w.kh), st);
+    if (head_applies(dev, true, BH, N, M, D, dtype, w))
+      return launch_pp_head(Qs, Ks, Vs, Qf, gate, K, V, Y, Qb, Z, L, B, H, N, M, qs, (float*)(wsc + w.kh), st);
+  }
   const EncPlan p = plan_encode(dev, BH, N, M, dtype);
   // Synthesis encode over all heads, merged straight into the blended queries.
   float* pacc = (float*)(wsc + w.part_acc);

@@ -339,6 +339,41 @@ def test_decode_merges_the_splits(flare, orc, D, mult):
         check("FLARE++ Y", Yp, Ypr, tol)
 
 
+@pytest.mark.parametrize("B,H,N,M,share,mult", [
+    (16, 4, 4096, 128, True, 1.0),
+    (8, 3, 2048, 256, False, 1.0),   # the shortest heads it takes, unshared synthesis values
+    (16, 5, 3001, 96, True, 1.0),    # three latent blocks (the decode's generic latent loop)
+    (16, 4, 3000, 128, True, 8.0),   # keys x8: exact-score redo in both encodes and the decode
+])
+def test_latent_blocks_per_workgroup(flare, orc, B, H, N, M, share, mult):
+    """FLARE++, bf16, D = 32, heads of 2048 to 8192 tokens whose latent
+    blocks B H M / 32 fill more than half of the compute units and at most
+    all of them (on MI355X): every (head, latent block) runs its synthesis
+    encode, blend and routing encode in its own workgroup over all of the
+    head's tokens, then the decode runs as its own launch."""
+    from rank_latent_attention_amd.inputs import make_gaussian_pp, to_dtype
+    say(f"[latent blocks] B{B} H{H} N{N} M{M} D32 bf16 shared={share} keys x{mult:g}")
+    tol = TOL["bf16"]
+    w = make_gaussian_pp(B, H, N, M, 32, dtype="bf16", seed=71 + N, share_vs=share)
+    if mult != 1.0:
+        w.Ks = to_dtype(w.Ks.astype(np.float64) * mult, "bf16")
+        w.Vs = w.Ks if share else w.Vs
+        w.K = to_dtype(w.K.astype(np.float64) * mult, "bf16")
+    Y, Qo, Z, L = run_pp(flare, w)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Z)) and np.all(np.isfinite(L))
+    Yr, Qr, Zr, Lr = orc.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+    check("Q", Qo, Qr, tol)
+    if mult == 1.0:
+        check("Z", Z, Zr, tol)
+        check_lse("L", L, Lr, tol)
+        check("Y", Y, Yr, tol)
+    say("  routing from the formed queries:")
+    Yq, Zq, Lq = orc.flare_forward(Qo, w.K, w.V)
+    check("Z", Z, Zq, tol)
+    check_lse("L", L, Lq, tol)
+    check("Y", Y, Yq, tol)
+
+
 def test_encode_and_decode_entry_points(flare, orc):
     import torch
     from rank_latent_attention_amd.inputs import make_gaussian
