@@ -207,7 +207,9 @@ def _head_batch(H, fill):
     (D = 32, M = 64 or 128, bf16, short heads) once B H reaches half of the
     compute units: "half" gives B H = half of them, "more" one step of H
     past that, "all" every compute unit, and "quarter" a quarter of them (the
-    launch sequence, for comparison)."""
+    launch sequence, for comparison).  FLARE++ heads of 2048 tokens or more
+    at "half" with M = 64 take one workgroup per (head, latent block)
+    instead."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if fill == "quarter":
