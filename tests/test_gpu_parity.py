@@ -645,3 +645,59 @@ def test_random_shapes(flare, orc, shape, dtype):
     check("Z", Z, Zr, tol)
     check_lse("L", L, Lr, tol)
     check("Y", Y, Yr, tol)
+
+
+def _random_short_heads(seed, count):
+    """Seeded shapes (B, H, N, M, FLARE++) for the many-short-heads forwards,
+    drawn in turn from four regimes of a 256-unit chip: latent blocks per
+    workgroup (FLARE++, B H M / 32 between half and all of the units, 2048 to
+    8192 tokens), one workgroup per head (M of 64 or 128, B H of half the
+    units or more), the decode that merges the splits (FLARE, M = 256, many
+    heads), and shapes just outside these (M not a power of two, heads longer
+    than the per-head bound).  B H N M stays under 8e7 so that the oracle
+    ends in seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        H = int(rng.choice([2, 4, 8]))
+        regime = i % 4
+        if regime == 0:
+            MB = int(rng.integers(2, 9))
+            lo, hi = 128 // MB + 1, 256 // MB
+            BH = int(rng.integers(lo, hi + 1))
+            N, M, pp = int(rng.integers(2048, 8193)), 32 * MB, True
+        elif regime == 1:
+            M, pp = int(rng.choice([64, 128])), bool(rng.integers(0, 2))
+            BH = int(rng.integers(128, 321))
+            N = int(rng.integers(1, (8192 if pp or BH >= 256 else 4096) + 1))
+        elif regime == 2:
+            BH, M, pp = int(rng.integers(64, 161)), 256, False
+            N = int(rng.integers(1, 8193))
+        else:
+            M, pp = int(rng.choice([96, 160, 192])), bool(rng.integers(0, 2))
+            BH = int(rng.integers(32, 257))
+            N = int(rng.integers(4097, 9001))
+        N = max(1, min(N, 80_000_000 // (BH * M)))
+        out.append((max(1, BH // H), H, N, M, pp))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_short_heads(77, 8),
+                         ids=lambda s: "B{}H{}N{}M{}{}".format(*s[:4], "pp" if s[4] else ""))
+def test_random_short_head_shapes(flare, orc, shape):
+    from rank_latent_attention_amd.inputs import make_gaussian, make_gaussian_pp
+    B, H, N, M, pp = shape
+    say(f"[short heads] B{B} H{H} N{N} M{M} D32 bf16 {'FLARE++' if pp else 'FLARE'}")
+    tol = TOL["bf16"]
+    if pp:
+        w = make_gaussian_pp(B, H, N, M, 32, dtype="bf16", seed=N + M, share_vs=bool(N % 2))
+        Y, Qo, Z, L = run_pp(flare, w)
+        Yr, Qr, Zr, Lr = orc.flare_pp_forward(w.Qs, w.Ks, w.Vs, w.Qf, w.gate, w.K, w.V)
+        check("Q", Qo, Qr, tol)
+    else:
+        w = make_gaussian(B, H, N, M, 32, "bf16", seed=N + M)
+        Y, Z, L = run_flare(flare, w)
+        Yr, Zr, Lr = orc.flare_forward(w.Q, w.K, w.V)
+    check("Z", Z, Zr, tol)
+    check_lse("L", L, Lr, tol)
+    check("Y", Y, Yr, tol)
