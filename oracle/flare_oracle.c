@@ -113,8 +113,10 @@ int oracle_encode(const double* Q, int q_batched, const double* K, const double*
  * [B,H,count,D]. */
 int oracle_decode_rows(const double* Q, int q_batched, const double* K, const double* Z, int B, int H,
                        int N, int M, int D, double scale, const long* idx, long count, double* Y) {
-    if (B <= 0 || H <= 0 || N <= 0 || M <= 0 || D <= 0 || count < 0) return 1;
+    if (B <= 0 || H <= 0 || N < 0 || M <= 0 || D <= 0 || count < 0) return 1;
     if (!idx && count != N) return 1;
+    if (count == 0) return 0; /* no token rows (also every N = 0 call) */
+    if (N == 0) return 1;     /* indices into an empty token axis */
     const double s = pick_scale(scale, D);
     const long rows = (long)B * H * count;
     int bad = 0;

@@ -28,9 +28,11 @@ __all__ = ["build", "lib", "threads", "encode", "decode", "flare_forward", "pp_q
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into oracle/liboracle.so."""
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math) into oracle/liboracle.so
+    (without force, only when the library is missing or older than its source)."""
     global _lib
-    if force or not os.path.exists(_LIB_PATH):
+    stale = not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
                "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]

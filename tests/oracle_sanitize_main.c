@@ -52,7 +52,11 @@ static int run_shape(int B, int H, int N, int M, int D, int qb) {
     const size_t nz = (size_t)B * H * M * D, nl = (size_t)B * H * M;
     double *Q = buf(nq), *K = buf(nkv), *V = buf(nkv), *Z = buf(nz), *L = buf(nl), *Y = buf(nkv);
     int bad = 0;
-    if (oracle_flare_forward(Q, qb, K, V, B, H, N, M, D, 0.0, Y, Z, L) != (N > 0 ? 0 : 1)) bad = 1;
+    if (oracle_flare_forward(Q, qb, K, V, B, H, N, M, D, 0.0, Y, Z, L) != 0) bad = 1;
+    if (!bad && N == 0) { /* no token rows: empty latents */
+        for (size_t i = 0; i < nz; ++i) bad |= Z[i] != 0.0;
+        for (size_t i = 0; i < nl; ++i) bad |= !(isinf(L[i]) && L[i] < 0);
+    }
     if (oracle_encode(Q, qb, K, V, B, H, N, M, D, 0.0, Z, L) != 0) bad = 1;
     if (!bad && N == 0) {
         for (size_t i = 0; i < nz; ++i) bad |= Z[i] != 0.0;

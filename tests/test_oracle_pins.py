@@ -189,6 +189,19 @@ def test_p7_split_merge_with_empty_shard(orc):
 
 # --- P8: degenerate axes ---
 
+def test_p8_no_tokens(orc):
+    """N = 0: every latent is an empty row (Z = 0, L = -inf, App. B.3) and Y
+    has no rows, for the forward as for the encode alone."""
+    B, H, M, D = 2, 3, 5, 4
+    Q = _rand(34, H, M, D)
+    K = np.zeros((B, H, 0, D))
+    Y, Z, L = orc.flare_forward(Q, K, K)
+    assert Y.shape == (B, H, 0, D)
+    assert np.all(Z == 0.0) and np.all(np.isneginf(L))
+    Ze, Le = orc.encode(Q, K, K)
+    assert np.all(Ze == 0.0) and np.all(np.isneginf(Le))
+
+
 def test_p8_single_latent_and_single_token(orc):
     N, D = 23, 4
     Q1, K, V = _rand(31, 1, D), _rand(32, N, D), _rand(33, N, D)
