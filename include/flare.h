@@ -171,8 +171,11 @@ int flare_pp_forward(const void* Qs, const void* Ks, const void* Vs, const void*
  *   eps         > 0 when any flag is set (the pages do not fix it; 1e-6 is
  *               the value this library's tests use).
  * Normalisation needs dtype FLARE_BF16 (else FLARE_ERR_UNSUPPORTED); a bad
- * flag or eps gives FLARE_ERR_INVALID_ARG.  The normalised keys are rounded
- * to bf16 before the matrix products, like the inputs themselves. */
+ * flag or eps gives FLARE_ERR_INVALID_ARG.  Keys normalised on the fly are
+ * rounded to fp16 for the score products (their elements are at most sqrt(D)
+ * in magnitude), with the queries they meet rounded to fp16 as well; keys
+ * that are also the values (Vs == Ks) are rounded to bf16 instead, as the
+ * value products take them. */
 int flare_pp_forward_norm(const void* Qs, const void* Ks, const void* Vs, const void* Qf, const float* gate,
                           const void* K, const void* V, void* Y, float* Q_out, float* Z_out, float* L_out,
                           int B, int H, int N, int M, int D, int dtype, float scale, int norm_flags,

@@ -65,6 +65,7 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -86,6 +87,10 @@ constexpr float kMinSum = 0x1p-64f;  // smallest weight sum the unshifted bf16 p
 // ----------------------------------------------------------------------------
 template <typename T> __device__ inline float to_f(T x) { return (float)x; }
 template <typename T> __device__ inline T from_f(float x) { return (T)x; }  // RNE for bf16
+// fp16 values carried in bf16 registers and LDS (bit patterns), for score
+// operands of normalised rows (see qk_mma_h)
+__device__ inline bf16 h_bits(float x) { return __builtin_bit_cast(bf16, (_Float16)x); }
+__device__ inline float h_val(bf16 b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -170,7 +175,9 @@ __device__ inline float norm_factor(float sumsq, int D, float eps) { return rsqr
 // lo receives the bf16 rounding of what that rounding left, so hi + lo is
 // the scaled row to about 2^-17 of each element.  Returns the squared
 // Euclidean norm of the rounding error of the whole row, |bf16(v) - v|^2.
-template <int D, typename QT>
+// With H the row is rounded to fp16 instead (bit patterns; no lo), and an
+// element beyond the fp16 range makes that error infinite.
+template <int D, typename QT, bool H = false>
 __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT* row, int g, float scale, bool norm,
                                    float eps, const float* mul0, const float* mul1, float* norm2 = nullptr) {
   float x[D / 2];
@@ -202,8 +209,8 @@ __device__ inline float load_q_row(QKOp<bf16, D>& o, QKOp<bf16, D>* lo, const QT
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const float vs = v[8 * st + s];
-      const bf16 h = (bf16)vs;
-      const float r = vs - (float)h;
+      const bf16 h = H ? h_bits(vs) : (bf16)vs;
+      const float r = vs - (H ? h_val(h) : (float)h);
       o.v[st][s] = h;
       if (lo) lo->v[st][s] = (bf16)r;
       e2 += r * r;
@@ -243,9 +250,16 @@ __device__ inline float wave_max(float x) {
 
 // Squared Euclidean norm of a bf16 QK operand row (half in this lane, half in
 // lane +-32; all 64 lanes must call this).
-template <int D> __device__ inline float row_norm2(const QKOp<bf16, D>& o) {
+template <int D, bool H = false> __device__ inline float row_norm2(const QKOp<bf16, D>& o) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float s = 0.f;
+  if constexpr (H) {  // fp16 elements
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) s += h_val(o.v[st][p]) * h_val(o.v[st][p]);
+    return pair_sum(s);
+  }
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
 #pragma unroll
@@ -257,8 +271,9 @@ template <int D> __device__ inline float row_norm2(const QKOp<bf16, D>& o) {
 }
 
 // N_0 of a bf16 QK operand in registers (a key row, half in this lane and
-// half in lane +-32; all 64 lanes must call this).  Returns the row's factor.
-template <int D> __device__ inline float norm_op(QKOp<bf16, D>& o, float eps) {
+// half in lane +-32; all 64 lanes must call this), rounded to bf16, or with H
+// to fp16 bit patterns.  Returns the row's factor.
+template <int D, bool H = false> __device__ inline float norm_op(QKOp<bf16, D>& o, float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
@@ -271,7 +286,7 @@ template <int D> __device__ inline float norm_op(QKOp<bf16, D>& o, float eps) {
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) o.v[st][s] = (bf16)((float)o.v[st][s] * r);
+    for (int s = 0; s < 8; ++s) o.v[st][s] = H ? h_bits((float)o.v[st][s] * r) : (bf16)((float)o.v[st][s] * r);
   return r;
 }
 
@@ -279,6 +294,23 @@ template <int D> __device__ inline f32x16 qk_mma(const QKOp<bf16, D>& a, const Q
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[st], b.v[st], c, 0, 0, 0);
   return c;
+}
+// Score operands of rows N_0-normalised on the fly: their elements are at
+// most sqrt(D) in magnitude, so they are held as fp16 (bit patterns in the
+// bf16 operand registers), whose 2^-11 rounding is 8 times finer than bf16's;
+// the queries they meet are rounded to fp16 too.  The matrix core takes both
+// formats at the same rate.
+template <int D> __device__ inline f32x16 qk_mma_h(const QKOp<bf16, D>& a, const QKOp<bf16, D>& b, f32x16 c) {
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.v[st]), __builtin_bit_cast(f16x8, b.v[st]),
+                                               c, 0, 0, 0);
+  return c;
+}
+// the bf16 product, or with H the fp16 one
+template <bool H, int D> __device__ inline f32x16 qk_mma_sel(const QKOp<bf16, D>& a, const QKOp<bf16, D>& b, f32x16 c) {
+  if constexpr (H) return qk_mma_h<D>(a, b, c);
+  else return qk_mma<D>(a, b, c);
 }
 template <int D> __device__ inline f32x16 qk_mma(const QKOp<float, D>& a, const QKOp<float, D>& b, f32x16 c) {
 #pragma unroll
@@ -547,8 +579,9 @@ __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memor
 // DMA is complete and visible to the workgroup.  Each thread takes one
 // 16-byte chunk per pass; the D / 8 chunks of a row sit in consecutive lanes
 // and add their partial sums with xor shuffles.  Rows past the piece repeat a
-// valid row, so every row holds finite values.
-template <int D, int NW, int ROWS = dma_rows<NW>()>
+// valid row, so every row holds finite values.  With H the rows are written as
+// fp16 (bit patterns; see qk_mma_h).
+template <int D, int NW, int ROWS = dma_rows<NW>(), bool H = false>
 __device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
   constexpr int CPR = D / 8;
   constexpr int CH = ROWS * CPR;
@@ -565,7 +598,7 @@ __device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
       for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
       const float r = norm_factor(ss, D, eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)v[i] * r);
+      for (int i = 0; i < 8; ++i) v[i] = H ? h_bits((float)v[i] * r) : (bf16)((float)v[i] * r);
       *ptr = v;
     }
   }
@@ -577,8 +610,8 @@ __device__ inline void norm_tile(bf16* tile, int wave, int lane, float eps) {
 // consecutive lanes, add their partial sums by quad permutes.  Rows past the
 // piece repeat its last row, so they add no key from outside it.
 // With dst given, the tile's rows below nvalid are also copied to dst (row
-// n at dst + n D, 16-byte chunks, coalesced).
-template <int D, int NW, int ROWS = dma_rows<NW>()>
+// n at dst + n D, 16-byte chunks, coalesced).  H: the tile holds fp16 rows.
+template <int D, int NW, int ROWS = dma_rows<NW>(), bool H = false>
 __device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float m, bf16* dst = nullptr,
                                      int nvalid = 0) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -589,10 +622,15 @@ __device__ inline float tile_key_max(const bf16* tile, int wave, int lane, float
     const bf16x8 v = reinterpret_cast<const bf16x8*>(tile)[chunk_pos<D>(P / CPR, P % CPR)];
     if (dst && P / CPR < nvalid) *reinterpret_cast<bf16x8*>(dst + (size_t)(P / CPR) * D + (P % CPR) * 8) = v;
     float s = 0.f;
+    if constexpr (H) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const bf16x2 w = {v[2 * p], v[2 * p + 1]};
-      s = __builtin_amdgcn_fdot2_f32_bf16(w, w, s, false);
+      for (int i = 0; i < 8; ++i) s += h_val(v[i]) * h_val(v[i]);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const bf16x2 w = {v[2 * p], v[2 * p + 1]};
+        s = __builtin_amdgcn_fdot2_f32_bf16(w, w, s, false);
+      }
     }
     // lanes 4r .. 4r + 3 (D = 32) or 2r, 2r + 1 (D = 16) hold one row
     s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, false));  // xor 1
@@ -863,7 +901,7 @@ template <int OFF> __device__ inline bf16x8 k_read(unsigned addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
-template <int D, int NB, int BO>
+template <int D, int NB, int BO, bool H = false>
 __device__ inline f32x16 enc_scores(const unsigned (&ka)[D / 16], const QKOp<bf16, D>& qop) {
   constexpr int OFF = BO + NB * 64 * D;
   QKOp<bf16, D> kop;
@@ -871,7 +909,7 @@ __device__ inline f32x16 enc_scores(const unsigned (&ka)[D / 16], const QKOp<bf1
   for (int st = 0; st < D / 16; ++st) kop.v[st] = k_read<OFF>(ka[st]);
   if constexpr (D == 32) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kop.v[0]), "+v"(kop.v[1]));
   else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kop.v[0]));
-  return qk_mma<D>(kop, qop, f32x16{});
+  return qk_mma_sel<H, D>(kop, qop, f32x16{});
 }
 
 // Weights of those scores into the running sum and Z^T += V^T P^T.  row0 is
@@ -901,13 +939,14 @@ __device__ inline void enc_consume(const unsigned (&va)[4], f32x16 sc, int row0,
 // exponentiated, so the MFMAs run under the exponentials.  Blocks past the
 // end of the piece are computed and masked to zero weight (their rows repeat
 // the piece's last row): a branch per block costs more than the rare waste.
-template <int D, int WN, int BO, int J, int NBLK>
+// H: keys and queries are fp16 (see qk_mma_h).
+template <int D, int WN, int BO, int J, int NBLK, bool H = false>
 __device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
                                     int lane, const QKOp<bf16, D>& qop, RowSum<D>& lsum, f32x16& acc, const f32x16& cur) {
   if constexpr (J + 1 < NBLK) {
-    const f32x16 nxt = enc_scores<D, (J + 1) * WN, BO>(ka, qop);
+    const f32x16 nxt = enc_scores<D, (J + 1) * WN, BO, H>(ka, qop);
     enc_consume<D, J * WN, BO>(va, cur, t0 + 32 * J * WN, n_hi, g, lane, lsum, acc);
-    encode_chain<D, WN, BO, J + 1, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, nxt);
+    encode_chain<D, WN, BO, J + 1, NBLK, H>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, nxt);
   } else {
     enc_consume<D, J * WN, BO>(va, cur, t0 + 32 * J * WN, n_hi, g, lane, lsum, acc);
   }
@@ -916,13 +955,13 @@ __device__ inline void encode_chain(const unsigned (&ka)[D / 16], const unsigned
 // The ROWS-token tile at t0 for one wave: token blocks ng, ng + WN, ... (the
 // per-wave offset ng * 64 * D is already folded into ka / va, and t0 here is
 // the wave's first row).
-template <int D, int NW, int WN, int BO, int ROWS = dma_rows<NW>()>
+template <int D, int NW, int WN, int BO, int ROWS = dma_rows<NW>(), bool H = false>
 __device__ inline void encode_tile(const unsigned (&ka)[D / 16], const unsigned (&va)[4], int t0, int n_hi, int g,
                                    int lane, const QKOp<bf16, D>& qop, RowSum<D>& lsum, f32x16& acc) {
   if (t0 >= n_hi) return;
   constexpr int NBLK = ROWS / 32 / WN;
   static_assert(NBLK >= 1, "a tile holds at least one token block per wave");
-  encode_chain<D, WN, BO, 0, NBLK>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, enc_scores<D, 0, BO>(ka, qop));
+  encode_chain<D, WN, BO, 0, NBLK, H>(ka, va, t0, n_hi, g, lane, qop, lsum, acc, enc_scores<D, 0, BO, H>(ka, qop));
 }
 
 // Careful recomputation of one wave's share of a piece (the token blocks
@@ -988,7 +1027,7 @@ __device__ inline float encode_careful(const bf16* Kh, const bf16* Vh, bool alia
 // [WN][32 G][D] and lal [WN][32 G] (split = token lane, latents from a.m0),
 // and a.part_km, when set, receives the head's largest squared key norm at
 // the head's index.
-template <typename QT, int D, int NW, int WN, bool NK, int ROWS = dma_rows<NW>(), bool LP = false>
+template <typename QT, int D, int NW, int WN, bool NK, int ROWS = dma_rows<NW>(), bool LP = false, bool H = false>
 __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncArgs& a, int piece, bf16* tiles,
                                                                       float* kred, float* lacc = nullptr,
                                                                       float2* lal = nullptr) {
@@ -1041,7 +1080,7 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
     QKOp<bf16, D> qop;
     // the wave's largest query rounding error (uniform: a scalar register)
     const float qerr2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
-        wave_max(load_q_row<D>(qop, nullptr, qrow(), g, a.qscale, a.norm_q != 0, a.eps, qm0, qm1)))));
+        wave_max(load_q_row<D, QT, H>(qop, nullptr, qrow(), g, a.qscale, a.norm_q != 0, a.eps, qm0, qm1)))));
     if (m >= M) zero_op<D>(qop);
     f32x16 acc;
 #pragma unroll
@@ -1057,47 +1096,47 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
     wait_dma();
     __syncthreads();
     if constexpr (NK) {  // key rows N_0 in place (and the values with them when they alias)
-      norm_tile<D, NW, ROWS>(k0, wave, lane, a.eps);
+      norm_tile<D, NW, ROWS, H>(k0, wave, lane, a.eps);
       __syncthreads();
     }
     for (int t0 = n_lo; t0 < n_hi; t0 += 2 * ROWS) {
       // tile t0 from buffer 0 while tile t0 + ROWS streams into buffer 1
       const int tn = t0 + ROWS;
-      kmax2 = tile_key_max<D, NW, ROWS>(k0, wave, lane, kmax2);
+      kmax2 = tile_key_max<D, NW, ROWS, H>(k0, wave, lane, kmax2);
       if (tn < n_hi) {
         dma_tile<D, NW, ROWS>(k1, Kh, tn, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW, ROWS>(v1, Vh, tn, n_hi, wave, lane);
       }
-      encode_tile<D, NW, WN, 0, ROWS>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+      encode_tile<D, NW, WN, 0, ROWS, H>(ka, va, t0 + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       wait_dma();
       __syncthreads();
       if (tn >= n_hi) break;
       if constexpr (NK) {
-        norm_tile<D, NW, ROWS>(k1, wave, lane, a.eps);
+        norm_tile<D, NW, ROWS, H>(k1, wave, lane, a.eps);
         __syncthreads();
       }
       // tile tn from buffer 1 while tn + ROWS streams into buffer 0
       const int tn2 = tn + ROWS;
-      kmax2 = tile_key_max<D, NW, ROWS>(k1, wave, lane, kmax2);
+      kmax2 = tile_key_max<D, NW, ROWS, H>(k1, wave, lane, kmax2);
       if (tn2 < n_hi) {
         dma_tile<D, NW, ROWS>(k0, Kh, tn2, n_hi, wave, lane);
         if (!alias) dma_tile<D, NW, ROWS>(v0, Vh, tn2, n_hi, wave, lane);
       }
       if constexpr (2 * TE * 2 < 32768) {
-        encode_tile<D, NW, WN, 2 * TE * 2, ROWS>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+        encode_tile<D, NW, WN, 2 * TE * 2, ROWS, H>(ka, va, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       } else {  // buffer 1 beyond the reads' 16-bit offsets: its addresses in registers
         unsigned kb[D / 16], vb[4];
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) kb[st] = ka[st] + 2 * TE * 2;
 #pragma unroll
         for (int k = 0; k < 4; ++k) vb[k] = va[k] + 2 * TE * 2;
-        encode_tile<D, NW, WN, 0, ROWS>(kb, vb, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
+        encode_tile<D, NW, WN, 0, ROWS, H>(kb, vb, tn + 32 * ng, n_hi, g, lane, qop, wsum, acc);
       }
       wait_dma();
       __syncthreads();
       if constexpr (NK) {
         if (tn2 < n_hi) {
-          norm_tile<D, NW, ROWS>(k0, wave, lane, a.eps);
+          norm_tile<D, NW, ROWS, H>(k0, wave, lane, a.eps);
           __syncthreads();
         }
       }
@@ -1159,11 +1198,11 @@ __device__ __attribute__((always_inline)) inline void encode_dma_body(const EncA
   }
 }
 
-template <typename QT, int D, int NW, int WN, bool NK>
+template <typename QT, int D, int NW, int WN, bool NK, bool H = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) encode_dma_kernel(EncArgs a) {
   __shared__ __align__(16) bf16 tiles[4 * dma_rows<NW>() * D];
   __shared__ float kred[NW];
-  encode_dma_body<QT, D, NW, WN, NK>(a, blockIdx.x, tiles, kred);
+  encode_dma_body<QT, D, NW, WN, NK, dma_rows<NW>(), false, H>(a, blockIdx.x, tiles, kred);
 }
 
 // ----------------------------------------------------------------------------
@@ -1427,6 +1466,10 @@ template <typename T, typename QT, int D, bool TAIL, bool NK, bool ST = false, i
 __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs& a, int piece, unsigned char* smem,
                                                                   float* zred, float* qred, int& next_blk) {
   static_assert(!ST || sizeof(T) == 2, "statistics mode is bf16 only");
+  // key rows N_0 on the fly: fp16 score operands (queries and keys; see
+  // qk_mma_h), except in statistics mode, whose weights the backward forms
+  // again from bf16 keys
+  constexpr bool H = NK && !ST && sizeof(T) == 2;
   using L = DecLds<T, D>;
   const int MB = MBT > 0 ? MBT : a.MB, Mp = 32 * MB, M = a.M, N = a.N;
   T* qs = reinterpret_cast<T*>(smem);
@@ -1511,9 +1554,17 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
 #pragma unroll
           for (int i = 0; i < QE; ++i) {
             const float q = (c < nq ? to_f(src[i]) * a.qscale : 0.f) * qm[i];
-            const T r = from_f<T>(q);
+            T r;
+            float rv;
+            if constexpr (H) {
+              r = h_bits(q);
+              rv = h_val(r);
+            } else {
+              r = from_f<T>(q);
+              rv = to_f(r);
+            }
             qs[m * L::QST + d0 + i] = r;
-            ce2 += (q - to_f(r)) * (q - to_f(r));
+            ce2 += (q - rv) * (q - rv);
           }
         }
         // the D / QE chunks of a row sit in consecutive, aligned lanes
@@ -1593,7 +1644,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
     for (int st = 0; st < (int)(sizeof(kop.v) / sizeof(kop.v[0])); ++st) asm volatile("" : "+v"(kop.v[st]));
     const f32x16 zero16 = {};
     while (b < nblk) {
-      if constexpr (NK) norm_op<D>(kop, a.eps);
+      if constexpr (NK) norm_op<D, H>(kop, a.eps);
       int bn = 0;
       if (lane == 0) bn = atomicAdd(&next_blk, 1);
       bn = __builtin_amdgcn_readfirstlane(bn);
@@ -1620,7 +1671,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
         auto scores = [&](int mb) {
           QKOp<T, D> qop;
           load_op<D>(qop, qrow + mb * 32 * L::QST, g);
-          return qk_mma<D>(qop, kop, zero16);
+          return qk_mma_sel<H, D>(qop, kop, zero16);
         };
         auto consume = [&](f32x16 sc, int mb, const f32x16& from) {
           PVOp<T> zop;
@@ -1654,7 +1705,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
         // |Y accumulator| <= den * max |z| stays below 2^120 when den <= zlim;
         // the staged queries' rounding moves no score of a key with
         // |k|^2 <= klim2 by more than kScoreErr
-        const bool redo = !fast_ok(den) || den > zlim || (kcheck && row_norm2<D>(kop) > klim2);
+        const bool redo = !fast_ok(den) || den > zlim || (kcheck && row_norm2<D, H>(kop) > klim2);
         if (__builtin_amdgcn_ballot_w64(redo) != 0) {
           // careful redo of this token block: exact scores (the queries read
           // again and split into bf16 hi + lo) and the exact maximum of
@@ -1664,6 +1715,11 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
           acc = zero16;
           lsum = 0.f;
           const float* qm = a.qmul ? a.qmul + (size_t)h * D : nullptr;
+          QKOp<T, D> kx = kop;  // bf16 keys
+          if constexpr (H) {  // this lane's key row again, N_0 in bf16
+            load_op<D>(kx, Kh + (size_t)(t0 + li < n_hi ? t0 + li : n_hi - 1) * D, g);
+            norm_op<D>(kx, a.eps);
+          }
           int mc = 0;
           do {
             const int m = mc * 32 + li;
@@ -1673,7 +1729,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecArgs&
             PVOp<T> zop;
             if (li < D) load_pv(zop, zt + li * zst + mc * 32, g);
             else ones_pv(zop, li, D);
-            f32x16 sc = qk_mma<D>(qlo, kop, qk_mma<D>(qhi, kop, negs));
+            f32x16 sc = qk_mma<D>(qlo, kx, qk_mma<D>(qhi, kx, negs));
             if (mask_tail && mc == MB - 1) mask_rows(sc, M - mc * 32, g);
             online_step(sc, negs, started, lsum, acc);
             bf16x8 b0, b1;
@@ -2040,22 +2096,28 @@ int check_common(int B, int H, int N, int M, int D, int dtype, int q_batched) {
   return FLARE_OK;
 }
 
-template <typename QT, int D, int NW, int WN, bool NK>
+template <typename QT, int D, int NW, int WN, bool NK, bool H>
 int launch_encode_dma(const EncArgs& a, hipStream_t st) {
-  return launch(encode_dma_kernel<QT, D, NW, WN, NK>, dim3(a.nwg), dim3(NW * 64), 0, st, a);
+  return launch(encode_dma_kernel<QT, D, NW, WN, NK, H>, dim3(a.nwg), dim3(NW * 64), 0, st, a);
 }
 
-template <typename QT, int D, bool NK>
+template <typename QT, int D, bool NK, bool H = false>
 int launch_encode_bf16_dk(const EncArgs& a, int NW, int WN, hipStream_t st) {
-  if (NW == 8 && WN == 1) return launch_encode_dma<QT, D, 8, 1, NK>(a, st);
+  if (NW == 8 && WN == 1) return launch_encode_dma<QT, D, 8, 1, NK, H>(a, st);
   if (NW != 4) return FLARE_ERR_UNSUPPORTED;  // no kernel for this split plan
-  if (WN == 4) return launch_encode_dma<QT, D, 4, 4, NK>(a, st);
-  if (WN == 2) return launch_encode_dma<QT, D, 4, 2, NK>(a, st);
-  return launch_encode_dma<QT, D, 4, 1, NK>(a, st);
+  if (WN == 4) return launch_encode_dma<QT, D, 4, 4, NK, H>(a, st);
+  if (WN == 2) return launch_encode_dma<QT, D, 4, 2, NK, H>(a, st);
+  return launch_encode_dma<QT, D, 4, 1, NK, H>(a, st);
 }
 
+// With key rows N_0 and separate values the scores take fp16 operands (the
+// normalised keys and the queries; see qk_mma_h).  Values that alias the keys
+// are normalised in the same tile and stay bf16 for the value products.
 template <typename QT>
 int launch_encode_bf16(const EncArgs& a, int D, int NW, int WN, bool nk, hipStream_t st) {
+  if (nk && !a.v_alias)
+    return D == 16 ? launch_encode_bf16_dk<QT, 16, true, true>(a, NW, WN, st)
+                   : launch_encode_bf16_dk<QT, 32, true, true>(a, NW, WN, st);
   if (nk)
     return D == 16 ? launch_encode_bf16_dk<QT, 16, true>(a, NW, WN, st)
                    : launch_encode_bf16_dk<QT, 32, true>(a, NW, WN, st);

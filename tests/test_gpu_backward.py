@@ -69,6 +69,27 @@ SHAPES = [  # B, H, N, M, D, q_batched
 ]
 
 
+def test_backward_single_token(flare, orc):
+    """N = 1: every latent is the one value row and so is every output, for
+    any queries and key (the encode's softmax over one token is 1, and the
+    decode's weights sum to one over equal latents), so dQ = dK = 0 exactly.
+    A relative error against that zero is meaningless: their computed values
+    are rounding noise, bounded against dV (= dY here); dV and dZ match the
+    oracle."""
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian
+    w = make_gaussian(2, 3, 1, 64, 16, "bf16", seed=93)
+    dY = cotangent(94, "dy", w.K.shape)
+    say("[backward] B2 H3 N1 M64 D16")
+    dQ, dK, dV, dZ = gpu_backward(flare, w.Q, w.K, w.V, dY)
+    ref = orc.flare_backward(w.Q, w.K, w.V, dY, return_dZ=True)
+    check("dV", dV, ref[2])
+    check("dZ", dZ, ref[3])
+    big = np.linalg.norm(dV)
+    say(f"  |dQ| {np.linalg.norm(dQ):.2e}, |dK| {np.linalg.norm(dK):.2e}, |dV| {big:.2e}")
+    assert np.all(np.isfinite(dQ)) and np.all(np.isfinite(dK))
+    assert np.linalg.norm(dQ) <= 1e-5 * big and np.linalg.norm(dK) <= 1e-5 * big
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}N{}M{}D{}qb{}".format(*s))
 def test_backward_gaussian(flare, orc, shape):
     from rank_latent_attention_amd.inputs import cotangent, make_gaussian

@@ -76,6 +76,24 @@ SHAPES = [  # B, H, N, M, D, q_batched
 ]
 
 
+def test_backward_f32_single_token(flare, orc):
+    """N = 1: dQ = dK = 0 exactly (see the bf16 test of the same case); their
+    computed values are rounding noise, bounded against dV; dV and dZ match
+    the oracle at the float32 bar."""
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian
+    w = make_gaussian(1, 3, 1, 28, 32, "f32", seed=95)
+    dY = cotangent(96, "dy", w.K.shape, dtype="f32")
+    say("[backward f32] B1 H3 N1 M28 D32")
+    dQ, dK, dV, dZ = gpu_backward(flare, w.Q, w.K, w.V, dY)
+    ref = orc.flare_backward(w.Q, w.K, w.V, dY, return_dZ=True)
+    check("dV", dV, ref[2])
+    check("dZ", dZ, ref[3])
+    big = np.linalg.norm(dV)
+    say(f"  |dQ| {np.linalg.norm(dQ):.2e}, |dK| {np.linalg.norm(dK):.2e}, |dV| {big:.2e}")
+    assert np.all(np.isfinite(dQ)) and np.all(np.isfinite(dK))
+    assert np.linalg.norm(dQ) <= 1e-5 * big and np.linalg.norm(dK) <= 1e-5 * big
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}N{}M{}D{}qb{}".format(*s))
 def test_backward_f32_gaussian(flare, orc, shape):
     from rank_latent_attention_amd.inputs import cotangent, make_gaussian

@@ -108,6 +108,21 @@ def test_norm_flags_one_at_a_time(flare, orc, flags):
     compare(orc, flare, w, flags)
 
 
+@pytest.mark.parametrize("flags", [8, 12])
+@pytest.mark.parametrize("scale", [0.0, 0.3])
+def test_normalised_routing_keys_at_a_sharper_scale(flare, orc, flags, scale):
+    """N_0 routing keys (with and without N_0 on the fixed queries) at the
+    default scale and at 1.2 times it (D = 16): the keys normalised on the fly
+    and the queries they meet are rounded to fp16 for the score products, so
+    the rounding of the normalised keys moves no score by more than 2^-11 of
+    its terms.  With bf16 operands this shape reached rel-L2 1.1e-2 on Y at
+    the sharper scale."""
+    from rank_latent_attention_amd.inputs import make_gaussian_pp_raw
+    w = make_gaussian_pp_raw(2, 7, 13392, 64, 16, "bf16", seed=2130, variant="flarepp")
+    say(f"[norm flags {flags}, scale {scale}]")
+    compare(orc, flare, w, flags, scale=scale)
+
+
 def test_scaled_shared_keys_scale_the_latents(flare, orc):
     # N_a on keys that are also the values (App. A.6 with a learned scale):
     # the scale multiplies both the scores and the merged synthesis latents
