@@ -497,3 +497,33 @@ def test_pp_backward_norm_without_tokens(flare):
     for t in (dQs, dQf, dgate, da_qs, da_k):
         assert torch.all(torch.isfinite(t)) and torch.count_nonzero(t).item() == 0
     assert dKs.numel() == 0 and dK.numel() == 0 and dV.numel() == 0
+
+
+def _random_backward_shapes(seed, count):
+    """Seeded shapes (B, H, N, M, D, q_batched, scale) for the FLARE backward:
+    token counts from 2 to 40,000, any M up to 256, both head sizes, shared
+    and per-batch queries, the default scale or an explicit one up to 1.2
+    times it; B H N M stays under 6e6 so that the oracle ends in seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 9))
+        M = int(rng.choice([int(rng.integers(1, 257)), 64, 128, 256]))
+        D = int(rng.choice([16, 32]))
+        N = int(rng.integers(2, 40001))
+        N = max(2, min(N, 6_000_000 // (B * H * M)))
+        scale = float(rng.choice([0.0, 0.0, 0.11, 0.3]))
+        out.append((B, H, N, M, D, bool(rng.integers(0, 2)), scale))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_backward_shapes(404, 8),
+                         ids=lambda s: "B{}H{}N{}M{}D{}qb{}s{}".format(*s))
+def test_random_backward_shapes(flare, orc, shape):
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian
+    B, H, N, M, D, qb, scale = shape
+    w = make_gaussian(B, H, N, M, D, "bf16", seed=N + M)
+    Q = np.broadcast_to(w.Q, (B,) + w.Q.shape).copy() if qb else w.Q
+    dY = cotangent(N + M + 1, "dy", w.K.shape)
+    say(f"[backward, random] B{B} H{H} N{N} M{M} D{D} q_batched {qb} scale {scale}")
+    compare(orc, flare, Q, w.K, w.V, dY, scale=scale)

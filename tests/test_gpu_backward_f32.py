@@ -242,3 +242,18 @@ def test_pp_backward_f32(flare, orc, shape):
             assert e <= BAR
             continue
         check(n, g, r)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 5221, 93, 32, True, 0.0), (1, 5, 12000, 64, 16, False, 0.3),
+                                   (3, 2, 777, 256, 32, False, 0.11), (1, 1, 2, 7, 16, True, 0.0)],
+                         ids=lambda s: "B{}H{}N{}M{}D{}qb{}s{}".format(*s))
+def test_backward_f32_more_shapes(flare, orc, shape):
+    """Irregular M, an explicit scale 1.2 times the default (D = 16), two
+    tokens, per-batch queries: the float32 bar on every gradient."""
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian
+    B, H, N, M, D, qb, scale = shape
+    w = make_gaussian(B, H, N, M, D, "f32", seed=N + M)
+    Q = np.broadcast_to(w.Q, (B,) + w.Q.shape).copy() if qb else w.Q
+    dY = cotangent(N + M + 1, "dy", w.K.shape, dtype="f32")
+    say(f"[backward f32] B{B} H{H} N{N} M{M} D{D} q_batched {qb} scale {scale}")
+    compare(orc, flare, Q, w.K, w.V, dY, scale=scale)
