@@ -527,3 +527,50 @@ def test_random_backward_shapes(flare, orc, shape):
     dY = cotangent(N + M + 1, "dy", w.K.shape)
     say(f"[backward, random] B{B} H{H} N{N} M{M} D{D} q_batched {qb} scale {scale}")
     compare(orc, flare, Q, w.K, w.V, dY, scale=scale)
+
+
+def _random_pp_backward_shapes(seed, count):
+    """Seeded FLARE++ backward shapes (B, H, N, M, D, shared values)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        M = int(rng.choice([int(rng.integers(1, 257)), 64, 128]))
+        D = int(rng.choice([16, 32]))
+        N = max(2, min(int(rng.integers(2, 30001)), 3_000_000 // (B * H * M)))
+        out.append((B, H, N, M, D, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_pp_backward_shapes(7, 6),
+                         ids=lambda s: "B{}H{}N{}M{}D{}shared{}".format(*s))
+def test_random_pp_backward_shapes(flare, orc, shape):
+    """The FLARE++ backward at seeded shapes.  Every gradient but the gate's
+    meets the bf16 bar as a rel-L2.  The gate's, dg_h = sum over b, m, d of
+    dQ * Qd, is one sum per head of terms of both signs, so its relative error
+    is the error of dQ amplified by cancellation: it is bounded against the
+    sum of the terms' magnitudes instead (computed from the oracle's routing
+    cotangent and synthesis latents)."""
+    from rank_latent_attention_amd.inputs import cotangent, make_gaussian_pp
+    B, H, N, M, D, shared = shape
+    w = make_gaussian_pp(B, H, N, M, D, "bf16", seed=N + M, share_vs=shared)
+    dY = cotangent(N + M + 2, "dy", w.K.shape)
+    say(f"[pp backward, random] B{B} H{H} N{N} M{M} D{D} shared {shared}")
+    got = gpu_pp_backward(flare, w, dY, shared)
+    Vs = w.Ks if shared else w.Vs
+    ref = orc.flare_pp_backward(w.Qs, w.Ks, Vs, w.Qf, w.gate, w.K, w.V, dY, shared_vs=shared)
+    for n, g, r in zip(PP_NAMES, got, ref):
+        if r is None:
+            assert g is None, n
+            continue
+        assert np.all(np.isfinite(g)), n
+        if n != "dgate":
+            check(n, g, r)
+    Qb = orc.pp_queries(w.Qs, w.Ks, Vs, w.Qf, w.gate)
+    Qd = (Qb - np.asarray(w.Qf, np.float64)[None]) / np.asarray(w.gate, np.float64)[None, :, None, None]
+    dQ = orc.flare_backward(Qb, w.K, w.V, dY)[0]
+    mass = np.abs(dQ * Qd).sum(axis=(0, 2, 3))  # per head
+    e = np.abs(np.asarray(got[4], np.float64) - np.asarray(ref[4], np.float64)) / mass
+    say(f"  dgate: error / sum |dQ Qd| up to {e.max():.2e} (bar {TOL['bf16']:g}); "
+        f"conditioning sum |terms| / |sum| up to {np.max(mass / np.abs(ref[4])):.1f}")
+    assert np.all(e <= TOL["bf16"]), e
