@@ -519,9 +519,16 @@ __device__ inline void online_step_s(f32x16& s, float& shift, bool& started, flo
 // so the weights lost to underflow (below 2^-126) are under 2^-62 n of it,
 // far below bf16 resolution for any n < 2^40.  A column sum below kMinSum or
 // a non-finite sum or accumulator sends that wave's work to a careful
-// recomputation with the exact maximum of every block.  The tests work on the exponent bits and on ordered
-// comparisons, so they do not depend on the compiler's NaN assumptions.
-__device__ inline bool nonfinite(float x) { return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u; }
+// recomputation with the exact maximum of every block.  A sum can be NaN
+// here even for finite inputs (an Inf weight times a zero selector in the
+// matrix-core sums), so the test works on the exponent bits of a value the
+// compiler cannot trace back to a float: built without NaN semantics, it
+// would otherwise fold the test into an infinity check.
+__device__ inline bool nonfinite(float x) {
+  unsigned u = __float_as_uint(x);
+  asm volatile("" : "+v"(u));
+  return (u & 0x7f800000u) == 0x7f800000u;
+}
 
 // Column sum usable: finite and not vanishing.
 __device__ inline bool fast_ok(float den) { return !nonfinite(den) && den >= kMinSum; }

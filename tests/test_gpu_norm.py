@@ -188,6 +188,45 @@ def test_norms_on_the_careful_path(flare, orc):
     compare(orc, flare, w, 15, scale=scale)
 
 
+def test_normalised_keys_with_queries_beyond_fp16(flare, orc):
+    # s log2(e) = 2^16: the scaled routing queries (+-2^15, +-3 * 2^15) lie
+    # beyond the fp16 range, so the fp16 score operands of the normalised
+    # keys cannot hold them: their rounding error is infinite and every unit
+    # of work takes the exact recomputation (hi + lo bf16 queries).  Scores
+    # reach 3 * 10^6 (log2), where any relative error of a normalised key
+    # would show, so every normalised row here is a sign row (its N_0 is
+    # exact) and eps = 1e-30 leaves the row factors at exactly one; the
+    # scores are then exact integers on both sides
+    import torch
+    w = _exact_inputs(1, 2, 700, 32, 32, seed=77)
+    for name in ("Qs", "Ks", "K", "Qf"):
+        setattr(w, name, np.sign(getattr(w, name)).astype(np.float32))
+    w.Vs = w.Ks
+    eps = 1e-30
+    scale = 2.0 ** 16 / math.log2(math.e)
+    d = "bf16"
+    Qs, Ks, Qf, K, V = dev(w.Qs, d), dev(w.Ks, d), dev(w.Qf, d), dev(w.K, d), dev(w.V, d)
+    B, H, N, D = K.shape
+    M = Qs.shape[1]
+    Qo = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    Y, _, _, _ = flare.flare_pp_forward_norm(Qs, Ks, Ks, Qf, dev(w.gate, "f32"), K, V, 15, None, None, None, eps=eps,
+                                            scale=scale, Q_out=Qo, Z=Z, L=L)
+    torch.cuda.synchronize()
+    Y, Q, Z, L = host(Y), host(Qo), host(Z), host(L)
+    Yr, Qr, Zr, Lr = orc.flare_pp_forward_normed(w.Qs, w.Ks, w.Ks, w.Qf, w.gate, w.K, w.V, norm_qs=True, norm_ks=True,
+                                                 norm_qf=True, norm_k=True, eps=eps, scale=scale)
+    for n, g, r in (("Y", Y, Yr), ("Q", Q, Qr), ("Z", Z, Zr)):
+        assert np.all(np.isfinite(g)), n
+        check(n, g, r, TOL["bf16"])
+    # L is of order 10^6 here: float32 holds it to about 0.1, so it is
+    # compared to within a few units in its last place, not through e^L
+    dL = np.abs(np.asarray(L, np.float64) - Lr)
+    say(f"  L: largest |L - L_oracle| {dL.max():.3g} at |L| up to {np.abs(Lr).max():.3g}")
+    assert np.all(dL <= 4 * 2.0 ** -23 * np.abs(Lr) + 1e-3)
+
+
 def test_million_token_raw_workload_sampled(flare, orc):
     # the million-point FLARE++ workload before its norms, launched whole and
     # checked on the routing queries, Z and L of two heads and on sampled rows of Y

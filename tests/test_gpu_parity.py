@@ -488,6 +488,40 @@ def test_large_scores_do_not_overflow(flare, orc, dtype, mult):
     check("Y", Y, Yr, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("e", [6, 12])
+def test_extreme_scores_stay_finite(flare, orc, dtype, e):
+    """Scores of order 10^4 and 10^6 in log2 units (s log2(e) = 2^e, sign
+    keys, queries of one or two times a sign row), exact in every product:
+    every unshifted weight overflows, so the fast loops' sums are Inf or NaN
+    (an Inf weight times a zero selector), and every unit of work must take
+    the exact recomputation.  L is of order 10^5 to 10^7 here and float32
+    holds it to a few units in its last place."""
+    rng = np.random.default_rng(11)
+
+    def signs(shape, lo, hi):
+        mag = np.exp2(rng.integers(lo, hi, size=shape[:-1] + (1,)))
+        return ((rng.integers(0, 2, size=shape) * 2 - 1) * mag).astype(np.float32)
+    B, H, N, M, D = 1, 2, 700, 64, 32
+    Q, K = signs((H, M, D), 0, 2), signs((B, H, N, D), -1, 3)
+    V = (np.round(rng.standard_normal((B, H, N, D)) * 4) / 4).astype(np.float32)
+    scale = 2.0 ** e / math.log2(math.e)
+    say(f"[extreme scores] s log2 e = 2^{e}, {dtype}")
+    import torch
+    Qd, Kd, Vd = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=Kd.device)
+    L = torch.empty((B, H, M), dtype=torch.float32, device=Kd.device)
+    Y, _, _ = flare.flare_forward(Qd, Kd, Vd, scale=scale, Z=Z, L=L)
+    torch.cuda.synchronize()
+    Y, Z, L = host(Y), host(Z), host(L)
+    Yr, Zr, Lr = orc.flare_forward(Q, K, V, scale=scale)
+    check("Z", Z, Zr, TOL[dtype])
+    check("Y", Y, Yr, TOL[dtype])
+    dL = np.abs(np.asarray(L, np.float64) - Lr)
+    say(f"  L: largest |L - L_oracle| {dL.max():.3g} at |L| up to {np.abs(Lr).max():.3g}")
+    assert np.all(dL <= 4 * 2.0 ** -23 * np.abs(Lr) + 1e-3)
+
+
 def test_split_sums_beyond_float_range(flare, orc):
     """All keys identical with log2 scores of about 115, over 2^16 tokens cut
     into hundreds of workgroup splits: every split's weight sum is finite
