@@ -227,6 +227,29 @@ def test_normalised_keys_with_queries_beyond_fp16(flare, orc):
     assert np.all(dL <= 4 * 2.0 ** -23 * np.abs(Lr) + 1e-3)
 
 
+@pytest.mark.parametrize("N", [1024, 2048], ids=lambda n: f"N{n}")
+def test_short_heads_at_extreme_scores(flare, orc, N):
+    # 128 heads of M = 64 with no norms take the one-workgroup-per-head
+    # kernel (N 1024) or the per-latent-block kernel (N 2048); s log2(e) = 2^6
+    # makes every unshifted weight overflow, so their encodes and decode must
+    # all take the exact recomputation.  Scores are exact dyadic sums.
+    w = _exact_inputs(32, 4, N, 64, 32, seed=78)
+    scale = 2.0 ** 6 / math.log2(math.e)
+    Y, Q, Z, L = run_norm(flare, w, 0, scale)
+    Yr, Qr, Zr, Lr = oracle_norm(orc, w, 0, scale)
+    for n, g, r in (("Y", Y, Yr), ("Q", Q, Qr), ("Z", Z, Zr)):
+        assert np.all(np.isfinite(g)), n
+        check(n, g, r, TOL["bf16"])
+    # Without norms the routing queries are blends of tied synthesis keys,
+    # not all bf16-exact: where the exact-score bound holds, a unit keeps its
+    # fast scores, each within 2^-5 (log2) of the exact one, and L, set by the
+    # largest scores, inherits up to that (ln 2 / 32 = 0.022), plus float32
+    # rounding of L (of order 10^4 here)
+    dL = np.abs(np.asarray(L, np.float64) - Lr)
+    say(f"  L: largest |L - L_oracle| {dL.max():.3g} at |L| up to {np.abs(Lr).max():.3g}")
+    assert np.all(dL <= math.log(2) / 32 + 8 * 2.0 ** -23 * np.abs(Lr) + 1e-3)
+
+
 def test_million_token_raw_workload_sampled(flare, orc):
     # the million-point FLARE++ workload before its norms, launched whole and
     # checked on the routing queries, Z and L of two heads and on sampled rows of Y
